@@ -1,0 +1,489 @@
+"""CPU oracle for KIVI-style KV-cache quantization and decode attention.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check of the package
+entry point and the CPU-baseline leg of the benchmark may import or run this
+module.  It shares no code with the HIP library and imports nothing from it:
+it is written from the pages' definitions and from the cache layout as the
+library's header states it in prose.
+
+Sources (web pages, cited by title and section):
+  [KIVI-PR]   sonos/tract PR "KIVI-style KV-cache quantization - packed u8
+              storage": "The idea" (keys per channel, values per token),
+              "What's in the PR" (per-token value store = D bytes + 2 f32
+              params per token; per-channel key store = D bytes per token +
+              D x 8 bytes of params; GQA handled; output has Q's shape),
+              squashed commit messages (round-trip error <= scale/2, bits
+              configurable, memory = bits/16 of an f16 cache).
+  [STORE-PR]  sonos/tract PR "quantized KV-cache storage op (int8/int4)":
+              PR description (keys per channel in frozen fixed-size blocks,
+              values per token) and commit message (first SINK_TOKENS kept in
+              f32 in both stores).
+  [GUIDE]     pigeon guide page "KV-cache quantization": "How it works"
+              steps 1-5 (per-channel keys over G-token groups, per-token
+              values, q = round((x - min)/delta), delta = (max - min)/(2^b - 1),
+              full-precision residual window of R tokens quantized once a
+              group fills, softmax(q K^T / sqrt(d)) V over the dequantized
+              cache) and "Source code" (numpy round = half to even, clip).
+
+Readings where the pages are silent (each is listed in the design notes):
+  R1 partition: with n = max(0, T - S) tokens past the sinks, the quantized
+     count is Q = G * floor((n - R) / G) when n >= R, else 0; tokens
+     [S, S+Q) are quantized, [S+Q, T) stay in full precision (between R and
+     R+G-1 of them once n >= R), so the most recent R are always exact.
+  R2 groups start right after the sinks.
+  R3 K and V share the partition.
+  R4 rounding is half to even (numpy.rint).
+  R5 delta = fl32(fl32(max - min) / (2^b - 1)); code = rint(fl32(fl32(x - zp)
+     / delta)), a true IEEE fp32 division.
+  R6 max == min gives delta = 0 and every code 0.
+  R7 the zero point is the fp32 minimum, stored as mn + 0.0f (so -0 -> +0).
+  R8 sink and residual tokens are stored losslessly in the input dtype.
+  R9 GQA: q head hq reads KV head hq // (Hq / Hkv).
+  R10 default softmax scale 1/sqrt(D); the query attends to every cached token.
+  R11 codes are clamped to [0, 2^b - 1].
+
+Every function here is pinned by tests/test_oracle_pins.py against worked
+examples, closed forms, brute force and library routines.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+SUPPORTED_BITS = (2, 4, 8)
+_F32 = np.float32
+
+
+# ----------------------------------------------------------------------------
+# step 0: input dtype -> fp32 (exact for fp16 and bf16)
+# ----------------------------------------------------------------------------
+def to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen stored input values to fp32.  bf16 arrives as uint16 bit
+    patterns and becomes the fp32 with those 16 bits on top."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=_F32)
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float16).astype(_F32)
+    if dtype == "bf16":
+        u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return u.view(_F32)
+    raise ValueError(dtype)
+
+
+def elem_bytes(dtype: str) -> int:
+    return {"f32": 4, "f16": 2, "bf16": 2}[dtype]
+
+
+def storage_np_dtype(dtype: str):
+    return {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+
+
+# ----------------------------------------------------------------------------
+# step 1: which tokens are sinks, quantized, or full-precision residual (R1)
+# ----------------------------------------------------------------------------
+def partition(T: int, S: int, R: int, G: int):
+    """Returns (n_sink, Q, n_resid) for T cached tokens."""
+    n_sink = min(T, S)
+    n = max(0, T - S)
+    Q = G * ((n - R) // G) if n >= R else 0
+    return n_sink, Q, n - Q
+
+
+def ring_slot(t: int, S: int, R: int, G: int) -> int:
+    """Slot of token t (t >= S) in the (R+G)-slot full-precision ring."""
+    return (t - S) % (R + G)
+
+
+# ----------------------------------------------------------------------------
+# steps 2-3: the asymmetric affine quantizer ([GUIDE] How it works, step 3)
+# ----------------------------------------------------------------------------
+def affine_params(mn: np.ndarray, mx: np.ndarray, bits: int):
+    """delta = (max - min) / (2^b - 1) and zero point = min, in fp32 (R5, R7)."""
+    mn = np.asarray(mn, dtype=_F32)
+    mx = np.asarray(mx, dtype=_F32)
+    delta = (mx - mn) / _F32(2 ** bits - 1)
+    zp = mn + _F32(0.0)
+    return delta.astype(_F32), zp.astype(_F32)
+
+
+def affine_codes(x: np.ndarray, delta: np.ndarray, zp: np.ndarray, bits: int) -> np.ndarray:
+    """code = clamp(round_half_even((x - zp) / delta), 0, 2^b - 1); delta == 0
+    gives code 0 (R4, R5, R6, R11)."""
+    x = np.asarray(x, dtype=_F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = (x - zp) / delta
+    r = np.rint(quot)
+    r = np.clip(r, _F32(0), _F32(2 ** bits - 1))
+    r = np.where(delta == 0, _F32(0), r)
+    return r.astype(np.uint8)
+
+
+def quantize_keys_per_channel(K: np.ndarray, G: int, bits: int):
+    """Keys per channel over G-token groups ([GUIDE] step 1; [STORE-PR] frozen
+    fixed-size blocks).  K: [..., n, D] fp32 with n a multiple of G.
+    Returns codes [..., n, D], delta and zp [..., n/G, D]."""
+    *lead, n, D = K.shape
+    assert n % G == 0
+    Kg = K.reshape(*lead, n // G, G, D)
+    mn = Kg.min(axis=-2)
+    mx = Kg.max(axis=-2)
+    delta, zp = affine_params(mn, mx, bits)
+    codes = affine_codes(Kg, delta[..., None, :], zp[..., None, :], bits)
+    return codes.reshape(*lead, n, D), delta, zp
+
+
+def quantize_values_per_token(V: np.ndarray, bits: int):
+    """Values per token ([GUIDE] step 2; [KIVI-PR] per-token value store).
+    V: [..., n, D] fp32.  Returns codes [..., n, D], delta and zp [..., n]."""
+    mn = V.min(axis=-1)
+    mx = V.max(axis=-1)
+    delta, zp = affine_params(mn, mx, bits)
+    codes = affine_codes(V, delta[..., None], zp[..., None], bits)
+    return codes, delta, zp
+
+
+# ----------------------------------------------------------------------------
+# step 4: packed byte layouts (the library header states them in prose)
+# ----------------------------------------------------------------------------
+def pack_key_rows(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Key codes are token-major: row u holds D codes in D*b/8 bytes, channel
+    d at bit offset d*b of the row, low bits first."""
+    *lead, n, D = codes.shape
+    per = 8 // bits
+    c = codes.astype(np.uint8).reshape(*lead, n, D // per, per)
+    out = np.zeros((*lead, n, D // per), dtype=np.uint8)
+    for i in range(per):
+        out |= (c[..., i] << np.uint8(bits * i)).astype(np.uint8)
+    return out
+
+
+def unpack_key_rows(packed: np.ndarray, bits: int, D: int) -> np.ndarray:
+    per = 8 // bits
+    mask = np.uint8(2 ** bits - 1)
+    *lead, n, nb = packed.shape
+    out = np.zeros((*lead, n, nb, per), dtype=np.uint8)
+    for i in range(per):
+        out[..., i] = (packed >> np.uint8(bits * i)) & mask
+    return out.reshape(*lead, n, D)
+
+
+def value_block_tokens(bits: int) -> int:
+    """Tokens per value-code block: 64 at 2 bits, 32 at 4 and 8 bits."""
+    return 64 if bits == 2 else 32
+
+
+def value_unit_codes(bits: int) -> int:
+    """Codes of one channel held in one unit: 16 at 2 bits (32-bit unit),
+    8 at 4 bits (32-bit unit), 8 at 8 bits (64-bit unit)."""
+    return 16 if bits == 2 else 8
+
+
+def value_code_location(u: int, d: int, bits: int, D: int):
+    """(byte offset, bit shift) of value code (token u, channel d) inside one
+    head's value-code array, straight from the layout's definition:
+
+    * tokens are cut into blocks of L tokens (L = 64 at 2 bits, else 32);
+    * inside a block, token offset o splits as o = 32*s + 16*h + 4*g + r with
+      s in [0, L/32), h in {0, 1}, g in [0, 4), r in [0, 4);
+    * one unit holds the codes of one channel for the tokens sharing (g);
+      units are ordered in the block by g, then j = d % 16, then n = d // 16:
+      unit index = (g*16 + j) * (D/16) + n, units of U*b/8 bytes;
+    * inside the unit, the token (s, h, r) is code slot i = r + 4*s + (U/2)*h,
+      slot i at bit offset i*b, low bits first.
+    """
+    L = value_block_tokens(bits)
+    U = value_unit_codes(bits)
+    unit_bytes = U * bits // 8
+    blk, o = divmod(u, L)
+    s, rem = divmod(o, 32)
+    h, rem = divmod(rem, 16)
+    g, r = divmod(rem, 4)
+    j, n = d % 16, d // 16
+    unit = blk * 4 * D + (g * 16 + j) * (D // 16) + n
+    i = r + 4 * s + (U // 2) * h
+    byte = unit * unit_bytes + (i * bits) // 8
+    return byte, (i * bits) % 8
+
+
+def value_codes_bytes(n_tokens_cap: int, bits: int, D: int) -> int:
+    L = value_block_tokens(bits)
+    nblk = -(-n_tokens_cap // L)
+    return nblk * L * D * bits // 8
+
+
+def pack_value_codes_loop(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Slow, literal form of the value layout for small cases.
+    codes: [n, D] -> bytes [value_codes_bytes(n)]."""
+    n, D = codes.shape
+    out = np.zeros(value_codes_bytes(n, bits, D), dtype=np.uint8)
+    for u in range(n):
+        for d in range(D):
+            byte, sh = value_code_location(u, d, bits, D)
+            out[byte] |= np.uint8(int(codes[u, d]) << sh)
+    return out
+
+
+def _value_perm_axes(bits: int):
+    # codes[u, d] viewed as [blk, s, h, g, r, n, j] -> [blk, g, j, n, h, s, r]
+    return (0, 3, 6, 5, 2, 1, 4)
+
+
+def pack_value_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Vectorized value layout.  codes: [..., n, D] -> [..., bytes]; tokens
+    past n (a partial last block) are packed as code 0 and are not part of
+    the cache contents."""
+    *lead, n, D = codes.shape
+    L = value_block_tokens(bits)
+    nblk = -(-n // L)
+    c = np.zeros((*lead, nblk * L, D), dtype=np.uint8)
+    c[..., :n, :] = codes
+    S_ = L // 32
+    c = c.reshape(*lead, nblk, S_, 2, 4, 4, D // 16, 16)
+    nl = len(lead)
+    axes = tuple(range(nl)) + tuple(nl + a for a in _value_perm_axes(bits))
+    c = np.transpose(c, axes)  # [..., blk, g, j, n, h, s, r] -> slot i = r + 4s + (U/2)h
+    U = value_unit_codes(bits)
+    c = c.reshape(*lead, nblk * 4 * D, U)
+    per = 8 // bits
+    c = c.reshape(*lead, nblk * 4 * D, U // per, per)
+    out = np.zeros((*lead, nblk * 4 * D, U // per), dtype=np.uint8)
+    for i in range(per):
+        out |= (c[..., i] << np.uint8(bits * i)).astype(np.uint8)
+    return out.reshape(*lead, nblk * 4 * D * U // per)
+
+
+def unpack_value_codes(packed: np.ndarray, bits: int, D: int, n: int) -> np.ndarray:
+    """Inverse of pack_value_codes: [..., bytes] -> codes [..., n, D]."""
+    *lead, nbytes = packed.shape
+    L = value_block_tokens(bits)
+    U = value_unit_codes(bits)
+    per = 8 // bits
+    nblk = nbytes // (L * D * bits // 8)
+    p = packed.reshape(*lead, nblk * 4 * D, U // per)
+    c = np.zeros((*lead, nblk * 4 * D, U // per, per), dtype=np.uint8)
+    mask = np.uint8(2 ** bits - 1)
+    for i in range(per):
+        c[..., i] = (p >> np.uint8(bits * i)) & mask
+    S_ = L // 32
+    c = c.reshape(*lead, nblk, 4, 16, D // 16, 2, S_, 4)   # [blk, g, j, n, h, s, r]
+    nl = len(lead)
+    inv = np.argsort(_value_perm_axes(bits))
+    axes = tuple(range(nl)) + tuple(nl + int(a) for a in inv)
+    c = np.transpose(c, axes)  # back to [blk, s, h, g, r, n, j]
+    return c.reshape(*lead, nblk * L, D)[..., :n, :]
+
+
+def value_valid_byte_mask(n_valid: int, n_cap: int, bits: int, D: int) -> np.ndarray:
+    """Bytes of a head's value-code array that hold codes of tokens < n_valid."""
+    ones = np.zeros((n_cap, D), dtype=np.uint8)
+    ones[:n_valid] = 2 ** bits - 1
+    return pack_value_codes(ones, bits) != 0
+
+
+# ----------------------------------------------------------------------------
+# the cache state, in the library's buffer layout
+# ----------------------------------------------------------------------------
+class CacheGeometry:
+    """Sizes of every cache buffer for a configuration.  The quantized-token
+    capacity is cap - S rounded up to a multiple of max(64, G)."""
+
+    def __init__(self, B, Hkv, D, bits, G, S, R, capacity, dtype):
+        assert bits in SUPPORTED_BITS
+        self.B, self.Hkv, self.D, self.bits = B, Hkv, D, bits
+        self.G, self.S, self.R, self.capacity, self.dtype = G, S, R, capacity, dtype
+        step = max(64, G)
+        qcap = max(0, capacity - S)
+        self.qcap = -(-qcap // step) * step
+        self.ring = R + G
+        self.k_row_bytes = D * bits // 8
+        self.v_head_bytes = value_codes_bytes(self.qcap, bits, D)
+
+    def empty_state(self):
+        B, H, D = self.B, self.Hkv, self.D
+        sd = storage_np_dtype(self.dtype)
+        return {
+            "k_codes": np.zeros((B, H, self.qcap, self.k_row_bytes), np.uint8),
+            "v_codes": np.zeros((B, H, self.v_head_bytes), np.uint8),
+            "k_scale": np.zeros((B, H, self.qcap // self.G, D), _F32),
+            "k_zero": np.zeros((B, H, self.qcap // self.G, D), _F32),
+            "v_scale": np.zeros((B, H, self.qcap), _F32),
+            "v_zero": np.zeros((B, H, self.qcap), _F32),
+            "k_sink": np.zeros((B, H, self.S, D), sd),
+            "v_sink": np.zeros((B, H, self.S, D), sd),
+            "k_resid": np.zeros((B, H, self.ring, D), sd),
+            "v_resid": np.zeros((B, H, self.ring, D), sd),
+        }
+
+
+def _store_groups(geo: CacheGeometry, st: dict, u0: int, Kq: np.ndarray, Vq: np.ndarray):
+    """Quantize tokens [S+u0, S+u0+n) (fp32 [B, H, n, D], n a multiple of G,
+    u0 a multiple of G) into the state's code and parameter arrays."""
+    n = Kq.shape[2]
+    if n == 0:
+        return
+    b = geo.bits
+    kc, kd, kz = quantize_keys_per_channel(Kq, geo.G, b)
+    vc, vd, vz = quantize_values_per_token(Vq, b)
+    st["k_codes"][:, :, u0:u0 + n] = pack_key_rows(kc, b)
+    st["k_scale"][:, :, u0 // geo.G:(u0 + n) // geo.G] = kd
+    st["k_zero"][:, :, u0 // geo.G:(u0 + n) // geo.G] = kz
+    st["v_scale"][:, :, u0:u0 + n] = vd
+    st["v_zero"][:, :, u0:u0 + n] = vz
+    # value codes: write only the bytes that belong to tokens [u0, u0+n).
+    # Blocks are independent runs of bytes, so work on the covered blocks.
+    L = value_block_tokens(b)
+    blk0, blk1 = u0 // L, -(-(u0 + n) // L)
+    span = (blk1 - blk0) * L
+    part = np.zeros((geo.B, geo.Hkv, span, geo.D), np.uint8)
+    part[:, :, u0 - blk0 * L:u0 - blk0 * L + n] = vc
+    packed = pack_value_codes(part, b)
+    touched = np.zeros((span, geo.D), np.uint8)
+    touched[u0 - blk0 * L:u0 - blk0 * L + n] = 1
+    tmask = pack_value_codes(touched, b) != 0      # bytes holding these tokens
+    # a byte only ever holds tokens of one 32-token step, and a step lies in
+    # one G-group (G is a multiple of 32), so whole bytes move.
+    blk_bytes = L * geo.D * b // 8
+    dst = st["v_codes"][:, :, blk0 * blk_bytes:blk1 * blk_bytes]
+    dst[:, :, tmask] = packed[:, :, tmask]
+
+
+def prefill(geo: CacheGeometry, K: np.ndarray, V: np.ndarray, T: int) -> dict:
+    """Cache state after loading T tokens at once (K, V in storage dtype,
+    [B, H, >=T, D])."""
+    st = geo.empty_state()
+    ns, Q, nr = partition(T, geo.S, geo.R, geo.G)
+    st["k_sink"][:, :, :ns] = K[:, :, :ns]
+    st["v_sink"][:, :, :ns] = V[:, :, :ns]
+    Kf = to_f32(K[:, :, geo.S:geo.S + Q], geo.dtype)
+    Vf = to_f32(V[:, :, geo.S:geo.S + Q], geo.dtype)
+    _store_groups(geo, st, 0, Kf, Vf)
+    for t in range(geo.S + Q, T):
+        sl = ring_slot(t, geo.S, geo.R, geo.G)
+        st["k_resid"][:, :, sl] = K[:, :, t]
+        st["v_resid"][:, :, sl] = V[:, :, t]
+    return st
+
+
+def append(geo: CacheGeometry, st: dict, n_before: int, k_new: np.ndarray,
+           v_new: np.ndarray) -> dict:
+    """Streaming append of token t = n_before ([B, H, D] in storage dtype).
+    The token goes to its sink or ring slot; when the full-precision count
+    reaches R + G the oldest G ring tokens are quantized as the next group
+    and frozen ([STORE-PR] frozen blocks; [GUIDE] step 4)."""
+    t = n_before
+    if t < geo.S:
+        st["k_sink"][:, :, t] = k_new
+        st["v_sink"][:, :, t] = v_new
+    else:
+        sl = ring_slot(t, geo.S, geo.R, geo.G)
+        st["k_resid"][:, :, sl] = k_new
+        st["v_resid"][:, :, sl] = v_new
+    _, q_old, _ = partition(t, geo.S, geo.R, geo.G)
+    _, q_new, _ = partition(t + 1, geo.S, geo.R, geo.G)
+    if q_new > q_old:
+        assert q_new - q_old == geo.G
+        toks = [geo.S + q_old + i for i in range(geo.G)]
+        slots = [ring_slot(x, geo.S, geo.R, geo.G) for x in toks]
+        Kf = to_f32(st["k_resid"][:, :, slots], geo.dtype)
+        Vf = to_f32(st["v_resid"][:, :, slots], geo.dtype)
+        _store_groups(geo, st, q_old, Kf, Vf)
+    return st
+
+
+def valid_masks(geo: CacheGeometry, T: int) -> dict:
+    """Which parts of each buffer hold cache contents after T tokens."""
+    ns, Q, nr = partition(T, geo.S, geo.R, geo.G)
+    ring = np.zeros(geo.ring, bool)
+    for t in range(geo.S + Q, T):
+        ring[ring_slot(t, geo.S, geo.R, geo.G)] = True
+    return {
+        "n_sink": ns, "Q": Q, "ring": ring,
+        "v_bytes": value_valid_byte_mask(Q, geo.qcap, geo.bits, geo.D),
+    }
+
+
+# ----------------------------------------------------------------------------
+# step 5: dequantize in fp64 ([GUIDE] step 5: dequantized group by group)
+# ----------------------------------------------------------------------------
+def dequant_cache(geo: CacheGeometry, st: dict, T: int, heads=None):
+    """K_hat, V_hat in fp64, [B, len(heads), T, D], in token order."""
+    heads = range(geo.Hkv) if heads is None else heads
+    heads = list(heads)
+    ns, Q, nr = partition(T, geo.S, geo.R, geo.G)
+    B, D = geo.B, geo.D
+    Kh = np.zeros((B, len(heads), T, D), np.float64)
+    Vh = np.zeros((B, len(heads), T, D), np.float64)
+    for i, h in enumerate(heads):
+        Kh[:, i, :ns] = to_f32(st["k_sink"][:, h, :ns], geo.dtype)
+        Vh[:, i, :ns] = to_f32(st["v_sink"][:, h, :ns], geo.dtype)
+        if Q:
+            kc = unpack_key_rows(st["k_codes"][:, h, :Q], geo.bits, D).astype(np.float64)
+            kd = np.repeat(st["k_scale"][:, h, :Q // geo.G], geo.G, axis=1).astype(np.float64)
+            kz = np.repeat(st["k_zero"][:, h, :Q // geo.G], geo.G, axis=1).astype(np.float64)
+            Kh[:, i, geo.S:geo.S + Q] = kc * kd + kz
+            vc = unpack_value_codes(st["v_codes"][:, h], geo.bits, D, Q).astype(np.float64)
+            vd = st["v_scale"][:, h, :Q].astype(np.float64)[..., None]
+            vz = st["v_zero"][:, h, :Q].astype(np.float64)[..., None]
+            Vh[:, i, geo.S:geo.S + Q] = vc * vd + vz
+        for t in range(geo.S + Q, T):
+            sl = ring_slot(t, geo.S, geo.R, geo.G)
+            Kh[:, i, t] = to_f32(st["k_resid"][:, h, sl], geo.dtype)
+            Vh[:, i, t] = to_f32(st["v_resid"][:, h, sl], geo.dtype)
+    return Kh, Vh
+
+
+# ----------------------------------------------------------------------------
+# step 6: attention in fp64 ([GUIDE] step 5; [KIVI-PR] GQA handled)
+# ----------------------------------------------------------------------------
+def attention(q: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, scale: float | None = None):
+    """softmax(scale * q K^T) V per (batch, q head), fp64.
+    q [B, Hq, D] (any float), Kh/Vh [B, Hkv, T, D] fp64.  Head hq reads
+    KV head hq // (Hq / Hkv) (R9).  Returns [B, Hq, D] fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = Kh.shape[1]
+    g = Hq // Hkv
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = np.zeros((B, Hq, D), np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            kv = hq // g
+            s = sc * (Kh[b, kv] @ q[b, hq])
+            m = s.max()
+            p = np.exp(s - m)
+            out[b, hq] = (p @ Vh[b, kv]) / p.sum()
+    return out
+
+
+def decode(geo: CacheGeometry, st: dict, T: int, q_stored: np.ndarray,
+           n_q_heads: int, scale: float | None = None, rows=None):
+    """Decode attention of q (storage dtype [B, Hq, D]) over the T cached
+    tokens, through the dequantized cache.  `rows` optionally restricts the
+    computation to a list of (b, hq) pairs (others left as NaN)."""
+    q = to_f32(q_stored, geo.dtype).astype(np.float64)
+    B, Hq, D = q.shape
+    g = Hq // geo.Hkv
+    if rows is None:
+        Kh, Vh = dequant_cache(geo, st, T)
+        return attention(q, Kh, Vh, scale)
+    out = np.full((B, Hq, D), np.nan)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    by_head = {}
+    for (b, hq) in rows:
+        by_head.setdefault(hq // g, []).append((b, hq))
+    for kv, lst in by_head.items():
+        Kh, Vh = dequant_cache(geo, st, T, heads=[kv])
+        for (b, hq) in lst:
+            s = sc * (Kh[b, 0] @ q[b, hq])
+            p = np.exp(s - s.max())
+            out[b, hq] = (p @ Vh[b, 0]) / p.sum()
+    return out
+
+
+def row_rel_error(o: np.ndarray, ref: np.ndarray) -> float:
+    """Max over (b, hq) rows of max_d |o - ref| / max_d |ref| (R12)."""
+    o = np.asarray(o, np.float64).reshape(-1, o.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    num = np.abs(o - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1)
+    return float((num / den).max())

@@ -1,0 +1,449 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a
+hand-derived fixture under tests/golden/, a closed form, brute force in
+exact rational arithmetic, a library routine (torch's scaled-dot-product
+attention, torch's bfloat16 conversion), or an invariant the pages state.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvq_oracle as O
+from kivi_quantized_kv_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------- worked examples
+def test_e1_round_half_even():
+    g = gold("e1_round_half_even.json")
+    x = np.array(g["x"], np.float32)
+    d, z = O.affine_params(x.min(), x.max(), g["bits"])
+    assert float(d) == g["delta"] and float(z) == g["zero"]
+    c = O.affine_codes(x, d, z, g["bits"])
+    assert c.tolist() == g["codes"]
+    err = np.abs(x - (c * d + z)).max()
+    assert err == g["max_abs_roundtrip_error"]
+
+
+def test_e2_packing():
+    for case in gold("e2_packing.json")["cases"]:
+        b = case["bits"]
+        codes = np.array(case["codes"], np.uint8)[None, :]
+        packed = O.pack_key_rows(codes, b)
+        assert packed[0].tolist() == case["bytes"]
+        assert O.unpack_key_rows(packed, b, codes.shape[1])[0].tolist() == case["codes"]
+
+
+def test_e3_degenerate_group():
+    g = gold("e3_degenerate.json")
+    x = np.array(g["x"], np.float32)
+    d, z = O.affine_params(x.min(), x.max(), g["bits"])
+    assert float(d) == 0.0 and float(z) == g["zero"]
+    assert O.affine_codes(x, d, z, g["bits"]).tolist() == g["codes"]
+    # per-channel keys and per-token values both reduce to it
+    K = np.tile(x[:, None], (1, 4))
+    kc, kd, kz = O.quantize_keys_per_channel(K, 4, g["bits"])
+    assert (kc == 0).all() and (kd == 0).all() and (kz == np.float32(1.25)).all()
+
+
+def test_e4_negative_zero_and_fp32_division():
+    g = gold("e4_negative_zero.json")
+    x = np.array(g["x"], np.float32)
+    d, z = O.affine_params(x.min(), x.max(), g["bits"])
+    assert int(np.float32(z).view(np.uint32)) == g["zero_bits"]
+    assert int(np.float32(d).view(np.uint32)) == g["delta_bits"]
+    assert O.affine_codes(x, d, z, g["bits"]).tolist() == g["codes"]
+
+
+# --------------------------------------------------------------- on-grid inputs
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_on_grid_inputs_quantize_exactly(bits, dtype):
+    """x = z + c * 2^-k with codes 0 and 2^b - 1 present: delta = 2^-k
+    exactly, the generating codes come back, dequantization is lossless."""
+    rng = np.random.default_rng(bits * 7 + len(dtype))
+    L = 2 ** bits - 1
+    G, D, n = 32, 16, 96
+    k = 4 if dtype != "f32" else 10
+    step = np.float32(2.0 ** -k)
+    codes = rng.integers(0, L + 1, size=(n, D)).astype(np.uint8)
+    for grp in range(n // G):
+        codes[grp * G, :] = 0
+        codes[grp * G + 1, :] = L
+    z = np.float32(-2.0) + step * rng.integers(0, 8, size=(1, D)).astype(np.float32)
+    x = (z + codes.astype(np.float32) * step).astype(np.float32)
+    stored = synth.cast(x, dtype)
+    assert (O.to_f32(stored, dtype) == x).all()  # exact in the dtype
+    kc, kd, kz = O.quantize_keys_per_channel(O.to_f32(stored, dtype), G, bits)
+    assert (kd == step).all()
+    assert (kc == codes).all()
+    assert (kc * kd.repeat(G, 0) + kz.repeat(G, 0) == x).all()
+    # values per token: grid along D
+    vcodes = rng.integers(0, L + 1, size=(n, D)).astype(np.uint8)
+    vcodes[:, 0] = 0
+    vcodes[:, 1] = L
+    zt = np.float32(0.5) + step * rng.integers(0, 8, size=(n, 1)).astype(np.float32)
+    v = (zt + vcodes.astype(np.float32) * step).astype(np.float32)
+    vc, vd, vz = O.quantize_values_per_token(v, bits)
+    assert (vd == step).all() and (vc == vcodes).all()
+
+
+# --------------------------------------------------------------- brute force
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_codes_are_nearest_grid_points_brute_force(bits):
+    """Each code minimizes |x - (zp + c*delta)| over all 2^b codes in exact
+    rational arithmetic (ties resolved to the even code).  Slack of a few
+    fp32 ulps of the quotient covers the fp32 division (reading R5)."""
+    rng = np.random.default_rng(100 + bits)
+    L = 2 ** bits - 1
+    for trial in range(40):
+        x = rng.standard_normal(4).astype(np.float32) * np.float32(rng.uniform(0.1, 30))
+        d, z = O.affine_params(x.min(), x.max(), bits)
+        c = O.affine_codes(x, d, z, bits)
+        D_, Z_ = Fraction(float(d)), Fraction(float(z))
+        for xi, ci in zip(x, c):
+            X = Fraction(float(xi))
+            errs = [abs(X - Z_ - k * D_) for k in range(L + 1)]
+            best = min(errs)
+            slack = D_ * Fraction(1, 2 ** 20)
+            assert errs[int(ci)] <= best + slack
+            # exact ties go to the even code
+            cands = [k for k in range(L + 1) if errs[k] == best]
+            if len(cands) == 2 and errs[int(ci)] == best:
+                assert int(ci) % 2 == 0
+
+
+def test_e7_subnormal_range_needs_the_clamp():
+    g = gold("e7_subnormal_clamp.json")
+    x = np.array(g["x_over_min_subnormal"], np.float32) * np.float32(2.0 ** -149)
+    d, z = O.affine_params(x.min(), x.max(), g["bits"])
+    assert int(np.float32(d).view(np.uint32)) == g["delta_bits"]
+    assert O.affine_codes(x, d, z, g["bits"]).tolist() == g["codes"]
+
+
+def test_clamp_keeps_codes_in_range():
+    # the top code can overshoot by an ulp without the clamp
+    x = np.array([0.0, 1e-30, 7.0000005, 7.0], np.float32)
+    for bits in (2, 4, 8):
+        d, z = O.affine_params(x.min(), x.max(), bits)
+        c = O.affine_codes(x, d, z, bits)
+        assert c.max() <= 2 ** bits - 1 and c.min() >= 0
+        assert c[np.argmax(x)] == 2 ** bits - 1
+
+
+# --------------------------------------------------------------- invariants
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_roundtrip_error_at_most_half_scale(bits):
+    """[KIVI-PR] commit message: round-trip error <= scale/2."""
+    rng = np.random.default_rng(bits)
+    K = (rng.standard_normal((256, 64)) * rng.uniform(0.5, 20, size=(1, 64))).astype(np.float32)
+    kc, kd, kz = O.quantize_keys_per_channel(K, 32, bits)
+    kd_t = np.repeat(kd, 32, 0).astype(np.float64)
+    kz_t = np.repeat(kz, 32, 0).astype(np.float64)
+    err = np.abs(K - (kc * kd_t + kz_t))
+    u = 2.0 ** -24
+    assert (err <= kd_t / 2 + 4 * u * (np.abs(K) + np.abs(kz_t)) + 1e-30).all()
+    vc, vd, vz = O.quantize_values_per_token(K, bits)
+    err = np.abs(K - (vc * vd[:, None].astype(np.float64) + vz[:, None]))
+    assert (err <= vd[:, None] / 2 + 4 * u * (np.abs(K) + np.abs(vz[:, None])) + 1e-30).all()
+
+
+def test_roundtrip_error_shrinks_with_bits():
+    """[KIVI-PR] commit message: the error shrinks with bits."""
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((256, 64)).astype(np.float32)
+    errs = []
+    for bits in (2, 4, 8):
+        kc, kd, kz = O.quantize_keys_per_channel(K, 32, bits)
+        rec = kc * np.repeat(kd, 32, 0) + np.repeat(kz, 32, 0)
+        errs.append(float(np.abs(K - rec).mean()))
+    assert errs[0] > errs[1] > errs[2]
+
+
+def _deviation(o, ref):
+    """Mean over rows of ||o - ref||_2 / ||ref||_2 (reading R15)."""
+    return float(np.mean(np.linalg.norm(o - ref, axis=-1) / np.linalg.norm(ref, axis=-1)))
+
+
+def _quality_case(seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, D = 256, 64
+    chans = rng.choice(D, size=4, replace=False)
+    K = rng.standard_normal((T, D), dtype=np.float32)
+    K[:, chans] *= np.float32(20)
+    V = rng.standard_normal((T, D), dtype=np.float32)
+    q = rng.standard_normal((8, D), dtype=np.float32)
+    return K, V, q
+
+
+def _attend(q, K, V):
+    return O.attention(q[None], K[None, None].astype(np.float64), V[None, None].astype(np.float64))[0]
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_per_channel_keys_beat_per_token_keys_and_int8_near_lossless(seed):
+    """[KIVI-PR] The idea + Correctness & gates: per-channel K is much closer
+    to full attention than per-token K on outlier channels; int8 is
+    near-lossless; [GUIDE] When it breaks: per-token keys fail on outlier
+    channels."""
+    K, V, q = _quality_case(seed)
+    ref = _attend(q, K, V)
+    dev_c, dev_t = {}, {}
+    for bits in (2, 4, 8):
+        vc, vd, vz = O.quantize_values_per_token(V, bits)
+        Vh = vc * vd[:, None].astype(np.float64) + vz[:, None]
+        kc, kd, kz = O.quantize_keys_per_channel(K, 32, bits)
+        Kc = kc * np.repeat(kd, 32, 0).astype(np.float64) + np.repeat(kz, 32, 0)
+        tc, td, tz = O.quantize_values_per_token(K, bits)    # per-token keys
+        Kt = tc * td[:, None].astype(np.float64) + tz[:, None]
+        dev_c[bits] = _deviation(_attend(q, Kc, Vh), ref)
+        dev_t[bits] = _deviation(_attend(q, Kt, Vh), ref)
+        assert dev_t[bits] / dev_c[bits] >= 1.5, (bits, dev_c, dev_t)
+    assert dev_c[8] <= 0.02
+    assert dev_c[8] < dev_c[4] < dev_c[2]
+
+
+# --------------------------------------------------------------- closed forms
+def test_store_closed_forms_and_mistral_example():
+    g = gold("e5_closed_forms.json")
+    # one block covering every token = the PR's single set of channel params
+    T, D = 4096, 128
+    geo = O.CacheGeometry(1, 1, D, 8, T, 0, 0, T, "f32")
+    st = geo.empty_state()
+    key_bytes = st["k_codes"].nbytes + st["k_scale"].nbytes + st["k_zero"].nbytes
+    val_bytes = st["v_codes"].nbytes + st["v_scale"].nbytes + st["v_zero"].nbytes
+    assert key_bytes == T * D + D * 8
+    assert val_bytes == T * D + T * 8
+    m = g["mistral"]
+    assert 2 * m["n_kv_heads"] * m["head_dim"] * 4 * m["tokens"] == m["f32_bytes"]
+    assert m["n_kv_heads"] * (key_bytes + val_bytes) == m["int8_bytes"]
+    g7 = g["guide_7b"]
+    assert 2 * g7["layers"] * g7["hidden"] * 2 == g7["bytes_per_token"]
+    assert g7["bytes_per_token"] * 4096 == g7["bytes_4096_tokens"]
+
+
+def test_packed_int8_saves_more_than_3x_vs_f32():
+    """[KIVI-PR] Correctness & gates: more than 3x saving at int8."""
+    g = gold("e5_closed_forms.json")["int8_d64"]
+    T, D, G = 1024, 64, 32
+    geo = O.CacheGeometry(1, 1, D, 8, G, 0, 0, T, "f32")
+    st = geo.empty_state()
+    v = st["v_codes"].nbytes + st["v_scale"].nbytes + st["v_zero"].nbytes
+    k = st["k_codes"].nbytes + st["k_scale"].nbytes + st["k_zero"].nbytes
+    assert (T * D * 4) / v == pytest.approx(g["value_ratio_vs_f32"])
+    assert (T * D * 4) / k == pytest.approx(g["key_ratio_vs_f32_G32"])
+    assert (T * D * 4) / v > 3 and (T * D * 4) / k > 3
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_packed_sizes_are_bits_over_8(bits):
+    geo = O.CacheGeometry(2, 3, 128, bits, 64, 4, 128, 4100, "bf16")
+    st = geo.empty_state()
+    assert st["k_codes"].nbytes == 2 * 3 * geo.qcap * 128 * bits // 8
+    assert st["v_codes"].nbytes == st["k_codes"].nbytes
+
+
+# --------------------------------------------------------------- layouts
+def test_value_layout_hand_positions():
+    for c in gold("e6_value_layout.json")["cases"]:
+        assert O.value_code_location(c["u"], c["d"], c["bits"], c["D"]) == (c["byte"], c["shift"])
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_value_layout_is_a_bijection_and_vector_form_matches(bits, D):
+    n = O.value_block_tokens(bits) * 3
+    seen = set()
+    for u in range(n):
+        for d in range(D):
+            loc = O.value_code_location(u, d, bits, D)
+            assert loc not in seen
+            assert loc[0] < O.value_codes_bytes(n, bits, D)
+            seen.add(loc)
+    assert len(seen) * bits == O.value_codes_bytes(n, bits, D) * 8
+    rng = np.random.default_rng(bits + D)
+    c = rng.integers(0, 2 ** bits, size=(n - 7, D)).astype(np.uint8)
+    a = O.pack_value_codes(c, bits)
+    b = O.pack_value_codes_loop(c, bits)
+    assert (a == b).all()
+    assert (O.unpack_value_codes(a, bits, D, n - 7) == c).all()
+
+
+def test_bf16_widening_matches_torch():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(4096) * 10.0 ** rng.integers(-30, 30, 4096)).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    ours = O.to_f32(bits, "bf16")
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert (ours.view(np.uint32) == ref.view(np.uint32)).all()
+
+
+# --------------------------------------------------------------- partition
+def test_partition_matches_worked_counts():
+    # tiny workload: T 256, S 4, R 32, G 32 -> 192 quantized, 60 full precision
+    assert O.partition(256, 4, 32, 32) == (4, 192, 60)
+    # 70B-shaped: T 131072, S 4, R 128, G 64 -> 130880 quantized, 188 fp
+    assert O.partition(131072, 4, 128, 64) == (4, 130880, 188)
+    # Mistral-shaped: T 32768, S 4, R 128, G 32 -> 32608 quantized
+    assert O.partition(32768, 4, 128, 32) == (4, 32608, 156)
+    assert O.partition(3, 4, 32, 32) == (3, 0, 0)
+    assert O.partition(40, 0, 0, 32) == (0, 32, 8)
+
+
+@pytest.mark.parametrize("S,R,G", [(0, 0, 32), (4, 32, 32), (1, 64, 32), (3, 0, 64), (4, 128, 64)])
+def test_partition_keeps_most_recent_R_in_full_precision(S, R, G):
+    prev_q = 0
+    for T in range(0, S + 4 * (R + G) + 5):
+        ns, Q, nr = O.partition(T, S, R, G)
+        n = max(0, T - S)
+        assert ns + Q + nr == T and Q % G == 0 and Q >= prev_q
+        assert nr >= min(n, R)              # the most recent R are exact
+        assert nr <= R + G - 1               # never more than R + G - 1
+        assert Q - prev_q in (0, G)          # one group freezes at a time
+        prev_q = Q
+
+
+# --------------------------------------------------------------- attention
+def test_attention_matches_torch_sdpa_with_gqa():
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, T, D = 2, 8, 2, 37, 16
+    q = rng.standard_normal((B, Hq, D))
+    K = rng.standard_normal((B, Hkv, T, D)) * 3
+    V = rng.standard_normal((B, Hkv, T, D))
+    ours = O.attention(q, K, V)
+    tq = torch.from_numpy(q)[:, :, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, torch.from_numpy(K), torch.from_numpy(V), enable_gqa=True)[:, :, 0, :].numpy()
+    assert np.abs(ours - ref).max() < 1e-12
+    ours2 = O.attention(q, K, V, scale=0.3)
+    ref2 = torch.nn.functional.scaled_dot_product_attention(
+        tq, torch.from_numpy(K), torch.from_numpy(V), enable_gqa=True, scale=0.3)[:, :, 0, :].numpy()
+    assert np.abs(ours2 - ref2).max() < 1e-12
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(12)
+    D = 8
+    K = rng.standard_normal((1, 1, 1, D))
+    V = rng.standard_normal((1, 1, 1, D))
+    q = rng.standard_normal((1, 3, D))
+    # one token: the output is that token's value
+    assert np.abs(O.attention(q, K, V) - V[0, 0, 0]).max() < 1e-15
+    # constant scores: the mean of the values
+    K = rng.standard_normal((1, 1, 20, D))
+    V = rng.standard_normal((1, 1, 20, D))
+    assert np.abs(O.attention(np.zeros((1, 2, D)), K, V) - V[0, 0].mean(0)).max() < 1e-14
+
+
+# --------------------------------------------------------------- streaming
+@pytest.mark.parametrize("S,R,G,bits,dtype", [
+    (2, 32, 32, 4, "f32"), (0, 0, 32, 2, "f16"), (3, 64, 32, 8, "bf16"),
+    (1, 32, 64, 2, "bf16"), (4, 0, 64, 4, "f16")])
+def test_prefill_equals_streaming_appends(S, R, G, bits, dtype):
+    """[STORE-PR] tests of accumulation vs a plain concat and block-wise
+    per-channel consistency over a growing range: the state after n single
+    appends equals the state of loading n tokens at once, byte for byte."""
+    B, H, D = 1, 2, 64
+    Tmax = S + 3 * (R + G) + 3
+    case = synth.random_case(7, B, H, H, D, Tmax, dtype)
+    K, V = case["K"], case["V"]
+    geo = O.CacheGeometry(B, H, D, bits, G, S, R, Tmax, dtype)
+    st = geo.empty_state()
+    for n in range(Tmax):
+        st = O.append(geo, st, n, K[:, :, n], V[:, :, n])
+        T = n + 1
+        if T % 7 and T not in (S + R + G, S + R + 2 * G, Tmax):
+            continue
+        ref = O.prefill(geo, K, V, T)
+        vm = O.valid_masks(geo, T)
+        Q = vm["Q"]
+        assert (st["k_codes"][:, :, :Q] == ref["k_codes"][:, :, :Q]).all()
+        assert (st["k_scale"][:, :, :Q // G] == ref["k_scale"][:, :, :Q // G]).all()
+        assert (st["k_zero"][:, :, :Q // G] == ref["k_zero"][:, :, :Q // G]).all()
+        assert (st["v_scale"][:, :, :Q] == ref["v_scale"][:, :, :Q]).all()
+        assert (st["v_codes"][:, :, vm["v_bytes"]] == ref["v_codes"][:, :, vm["v_bytes"]]).all()
+        assert (st["k_sink"][:, :, :vm["n_sink"]] == ref["k_sink"][:, :, :vm["n_sink"]]).all()
+        assert (st["v_resid"][:, :, vm["ring"]] == ref["v_resid"][:, :, vm["ring"]]).all()
+        assert (st["k_resid"][:, :, vm["ring"]] == ref["k_resid"][:, :, vm["ring"]]).all()
+        # and the attention over both states is identical
+        q = case["q"][:, :, :]
+        a = O.decode(geo, st, T, q, H)
+        b = O.decode(geo, ref, T, q, H)
+        assert (a == b).all()
+
+
+def test_all_full_precision_reduces_to_plain_attention():
+    """With T <= S + R + G - 1 nothing is quantized: decode equals attention
+    on the raw inputs (torch SDPA as the library reference)."""
+    S, R, G, D = 4, 32, 32, 64
+    T = S + R + G - 1
+    case = synth.random_case(3, 1, 4, 2, D, T, "f16")
+    geo = O.CacheGeometry(1, 2, D, 4, G, S, R, T, "f16")
+    st = O.prefill(geo, case["K"], case["V"], T)
+    assert O.partition(T, S, R, G)[1] == 0
+    out = O.decode(geo, st, T, case["q"], 4)
+    Kf = torch.from_numpy(case["K"].astype(np.float64))
+    Vf = torch.from_numpy(case["V"].astype(np.float64))
+    qf = torch.from_numpy(case["q"].astype(np.float64))[:, :, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(qf, Kf, Vf, enable_gqa=True)[:, :, 0].numpy()
+    assert np.abs(out - ref).max() < 1e-12
+
+
+def test_on_grid_cache_decodes_to_plain_attention():
+    """On-grid keys and values dequantize losslessly, so decode over a
+    quantized cache equals plain attention on the inputs."""
+    bits, G, S, R, D = 4, 32, 2, 32, 64
+    T = S + 5 * G + R
+    rng = np.random.default_rng(21)
+    L = 2 ** bits - 1
+    step = np.float32(2.0 ** -3)
+    kc = rng.integers(0, L + 1, size=(1, 2, T, D))
+    kc[:, :, ::G] = 0
+    kc[:, :, 1::G] = L
+    K = (np.float32(-1) + kc * step).astype(np.float32)
+    vc = rng.integers(0, L + 1, size=(1, 2, T, D))
+    vc[..., 0] = 0
+    vc[..., 1] = L
+    V = (np.float32(0.25) + vc * step).astype(np.float32)
+    q = rng.standard_normal((1, 4, D)).astype(np.float32)
+    geo = O.CacheGeometry(1, 2, D, bits, G, S, R, T, "f32")
+    st = O.prefill(geo, K, V, T)
+    assert O.partition(T, S, R, G)[1] > 0
+    Kh, Vh = O.dequant_cache(geo, st, T)
+    assert (Kh == K).all() and (Vh == V).all()
+    out = O.decode(geo, st, T, q, 4)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[:, :, None], torch.from_numpy(K.astype(np.float64)),
+        torch.from_numpy(V.astype(np.float64)), enable_gqa=True)[:, :, 0].numpy()
+    assert np.abs(out - ref).max() < 1e-12
+
+
+def test_decode_rows_subset_matches_full():
+    case = synth.random_case(4, 2, 4, 2, 64, 200, "bf16")
+    geo = O.CacheGeometry(2, 2, 64, 2, 32, 4, 32, 200, "bf16")
+    st = O.prefill(geo, case["K"], case["V"], 200)
+    full = O.decode(geo, st, 200, case["q"], 4)
+    rows = [(0, 3), (1, 0), (1, 1)]
+    part = O.decode(geo, st, 200, case["q"], 4, rows=rows)
+    for b, h in rows:
+        assert (part[b, h] == full[b, h]).all()
+
+
+def test_row_rel_error_definition():
+    ref = np.array([[[1.0, -2.0], [0.5, 0.25]]])
+    o = ref.copy()
+    o[0, 0, 1] += 0.002
+    o[0, 1, 0] -= 0.0001
+    assert O.row_rel_error(o, ref) == pytest.approx(max(0.002 / 2.0, 0.0001 / 0.5))

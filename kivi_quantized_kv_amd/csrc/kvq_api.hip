@@ -1,0 +1,259 @@
+// Host side of libkvq: the four C-ABI entry points.  Each validates its
+// arguments on the host, derives the token partition and launch geometry,
+// and enqueues kernels on the caller's stream.  Nothing here allocates,
+// frees or synchronizes.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/kvq.h"
+#include "kvq_kernels.h"
+
+using namespace kvq;
+
+namespace {
+
+constexpr int kTargetWorkgroups = 1024;  // ~4 workgroups of 4 waves per CU
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvq_status check_config(const kvq_config* c) {
+  if (!c) return KVQ_EINVAL;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->sink < 0 || c->residual < 0 || c->capacity < 1)
+    return KVQ_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_EUNSUPPORTED;
+  if (c->bits != 2 && c->bits != 4 && c->bits != 8) return KVQ_EUNSUPPORTED;
+  if (c->group != 32 && c->group != 64 && c->group != 128) return KVQ_EUNSUPPORTED;
+  if (c->dtype != KVQ_F32 && c->dtype != KVQ_F16 && c->dtype != KVQ_BF16) return KVQ_EUNSUPPORTED;
+  if (c->capacity > (int64_t(1) << 40)) return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+// Rows of 16-bit tensors are read 8 or 16 bytes at a time: every row must
+// start on a 16-byte boundary.
+kvq_status check_tensor(const kvq_tensor& t, int32_t dtype, bool needs_t) {
+  if (!t.ptr || !aligned16(t.ptr)) return KVQ_EINVAL;
+  const int64_t eb = kvq_dtype_bytes(dtype);
+  if (t.stride_b < 0 || t.stride_h < 0 || (needs_t && t.stride_t < 0)) return KVQ_EINVAL;
+  if ((t.stride_b * eb) % 16 || (t.stride_h * eb) % 16 || (needs_t && (t.stride_t * eb) % 16))
+    return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_config* c, const kvq_cache* k) {
+  if (!k) return KVQ_EINVAL;
+  const bool q = kvq_qcap(c) > 0;
+  if (q && (!k->k_codes || !k->v_codes || !k->k_scale || !k->k_zero || !k->v_scale || !k->v_zero))
+    return KVQ_EINVAL;
+  if (c->sink > 0 && (!k->k_sink || !k->v_sink)) return KVQ_EINVAL;
+  if (!k->k_resid || !k->v_resid) return KVQ_EINVAL;
+  const void* ptrs[] = {k->k_codes, k->v_codes, k->k_scale, k->k_zero, k->v_scale,
+                        k->v_zero,  k->k_sink,  k->v_sink,  k->k_resid, k->v_resid};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+// dispatch over (dtype, head_dim, bits)
+template <template <int, int, int> class Fn, typename... Args>
+hipError_t dispatch3(const kvq_config* c, Args&&... args) {
+#define KVQ_CASE_B(DT, D)                                                \
+  switch (c->bits) {                                                     \
+    case 2: return Fn<DT, D, 2>::run(args...);                           \
+    case 4: return Fn<DT, D, 4>::run(args...);                           \
+    default: return Fn<DT, D, 8>::run(args...);                          \
+  }
+#define KVQ_CASE_D(DT)                                                   \
+  if (c->head_dim == 64) { KVQ_CASE_B(DT, 64) } else { KVQ_CASE_B(DT, 128) }
+  switch (c->dtype) {
+    case KVQ_F32: KVQ_CASE_D(DT_F32)
+    case KVQ_F16: KVQ_CASE_D(DT_F16)
+    default: KVQ_CASE_D(DT_BF16)
+  }
+#undef KVQ_CASE_D
+#undef KVQ_CASE_B
+}
+
+template <int DT, int D, int BITS> struct QuantKeysFn {
+  static hipError_t run(const QuantArgs& a, int64_t n, int B, int H, hipStream_t s) {
+    return launch_quant_keys<DT, D, BITS>(a, n, B, H, s);
+  }
+};
+template <int DT, int D, int BITS> struct QuantValuesFn {
+  static hipError_t run(const QuantArgs& a, int64_t n, int B, int H, hipStream_t s) {
+    return launch_quant_values<DT, D, BITS>(a, n, B, H, s);
+  }
+};
+template <int DT, int D, int BITS> struct CopyFpFn {
+  static hipError_t run(const FpCopyArgs& a, int64_t n, int B, int H, hipStream_t s) {
+    return launch_copy_fp<DT, D>(a, n, B, H, s);
+  }
+};
+template <int DT, int D, int BITS> struct AppendFn {
+  static hipError_t run(const AppendArgs& a, int B, int H, hipStream_t s) {
+    return launch_append<DT, D, BITS>(a, B, H, s);
+  }
+};
+template <int DT, int D, int BITS> struct AttnValuFn {
+  static hipError_t run(const AttnArgs& a, int B, hipStream_t s) {
+    return launch_attn_valu<DT, D, BITS>(a, B, s);
+  }
+};
+
+// Prefill of one half: fp copies of sinks and residual tokens, then the
+// quantized range (keys per group or values per 32-token step).
+kvq_status prefill_half(const kvq_config* c, const kvq_cache* k, const kvq_tensor& x,
+                        int64_t n_tokens, void* stream, bool keys) {
+  kvq_status st = check_config(c);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(c, k)) != KVQ_OK) return st;
+  if ((st = check_tensor(x, c->dtype, true)) != KVQ_OK) return st;
+  if (n_tokens < 0) return KVQ_EINVAL;
+  if (n_tokens > c->capacity) return KVQ_ECAPACITY;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t S = c->sink, R = c->residual, G = c->group;
+  const int64_t Q = quantized_count(n_tokens, S, R, G);
+  const int64_t n_sink = n_tokens < S ? n_tokens : S;
+  const int64_t n_res = n_tokens > S ? n_tokens - S - Q : 0;
+  const int B = c->batch, H = c->n_kv_heads;
+  if (n_sink + n_res > 0) {
+    FpCopyArgs f{};
+    f.src = x.ptr; f.sb = x.stride_b; f.sh = x.stride_h; f.st = x.stride_t;
+    f.sink = keys ? k->k_sink : k->v_sink;
+    f.resid = keys ? k->k_resid : k->v_resid;
+    f.n_sink = n_sink; f.first_resid = S + Q; f.S = S; f.ring = R + G; f.H = H;
+    if (dispatch3<CopyFpFn>(c, f, n_sink + n_res, B, H, s) != hipSuccess) return KVQ_EHIP;
+  }
+  if (Q > 0) {
+    QuantArgs q{};
+    q.src = x.ptr; q.sb = x.stride_b; q.sh = x.stride_h; q.st = x.stride_t;
+    q.codes = keys ? k->k_codes : k->v_codes;
+    q.scale = keys ? k->k_scale : k->v_scale;
+    q.zero = keys ? k->k_zero : k->v_zero;
+    q.S = S; q.qcap = kvq_qcap(c); q.H = H; q.G = int(G);
+    hipError_t e = keys ? dispatch3<QuantKeysFn>(c, q, Q / G, B, H, s)
+                        : dispatch3<QuantValuesFn>(c, q, Q / 32, B, H, s);
+    if (e != hipSuccess) return KVQ_EHIP;
+  }
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" kvq_status kvq_quantize_keys(const kvq_config* cfg, const kvq_cache* cache,
+                                        kvq_tensor k, int64_t n_tokens, void* stream) {
+  try {
+    return prefill_half(cfg, cache, k, n_tokens, stream, true);
+  } catch (...) {
+    return KVQ_EINVAL;
+  }
+}
+
+extern "C" kvq_status kvq_quantize_values(const kvq_config* cfg, const kvq_cache* cache,
+                                          kvq_tensor v, int64_t n_tokens, void* stream) {
+  try {
+    return prefill_half(cfg, cache, v, n_tokens, stream, false);
+  } catch (...) {
+    return KVQ_EINVAL;
+  }
+}
+
+extern "C" kvq_status kvq_append_token(const kvq_config* cfg, const kvq_cache* cache,
+                                       int64_t n_before, kvq_tensor k_new, kvq_tensor v_new,
+                                       void* stream) {
+  try {
+    kvq_status st = check_config(cfg);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+    if ((st = check_tensor(k_new, cfg->dtype, false)) != KVQ_OK) return st;
+    if ((st = check_tensor(v_new, cfg->dtype, false)) != KVQ_OK) return st;
+    if (n_before < 0) return KVQ_EINVAL;
+    if (n_before + 1 > cfg->capacity) return KVQ_ECAPACITY;
+    const int64_t S = cfg->sink, R = cfg->residual, G = cfg->group;
+    const int64_t q_old = quantized_count(n_before, S, R, G);
+    const int64_t q_new = quantized_count(n_before + 1, S, R, G);
+    AppendArgs a{};
+    a.k_new = k_new.ptr; a.v_new = v_new.ptr;
+    a.k_sb = k_new.stride_b; a.k_sh = k_new.stride_h;
+    a.v_sb = v_new.stride_b; a.v_sh = v_new.stride_h;
+    a.k_codes = cache->k_codes; a.v_codes = cache->v_codes;
+    a.k_scale = cache->k_scale; a.k_zero = cache->k_zero;
+    a.v_scale = cache->v_scale; a.v_zero = cache->v_zero;
+    a.k_sink = cache->k_sink; a.v_sink = cache->v_sink;
+    a.k_resid = cache->k_resid; a.v_resid = cache->v_resid;
+    a.n_before = n_before; a.q_old = q_old; a.S = S; a.R = R; a.qcap = kvq_qcap(cfg);
+    a.H = cfg->n_kv_heads; a.G = int(G); a.flush = q_new > q_old ? 1 : 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (dispatch3<AppendFn>(cfg, a, cfg->batch, cfg->n_kv_heads, s) != hipSuccess) return KVQ_EHIP;
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EINVAL;
+  }
+}
+
+extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
+                                           int64_t n_tokens, int32_t n_q_heads, kvq_tensor q,
+                                           float softmax_scale, float* out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  try {
+    kvq_status st = check_config(cfg);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+    if ((st = check_tensor(q, cfg->dtype, false)) != KVQ_OK) return st;
+    if (!out || !workspace || !aligned16(out) || !aligned16(workspace)) return KVQ_EINVAL;
+    if (n_q_heads < 1 || n_q_heads % cfg->n_kv_heads) return KVQ_EINVAL;
+    if (n_tokens < 1) return KVQ_EINVAL;
+    if (n_tokens > cfg->capacity) return KVQ_ECAPACITY;
+    if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale)) return KVQ_EINVAL;
+
+    const int B = cfg->batch, H = cfg->n_kv_heads, D = cfg->head_dim;
+    const int64_t S = cfg->sink, R = cfg->residual, G = cfg->group;
+    const int64_t T = n_tokens;
+    const int64_t Q = quantized_count(T, S, R, G);
+    const int64_t n_sink = T < S ? T : S;
+    const int64_t n_res = T > S ? T - S - Q : 0;
+    const int64_t n_fp = n_sink + n_res;
+    const int64_t per_split_bytes = int64_t(B) * n_q_heads * (D + 2) * 4;
+    int64_t cap_splits = int64_t(workspace_bytes) / per_split_bytes;
+    if (cap_splits > KVQ_MAX_SPLITS) cap_splits = KVQ_MAX_SPLITS;
+    if (int64_t(workspace_bytes) < kvq_workspace_bytes_min(cfg, n_q_heads) || cap_splits < 2)
+      return KVQ_EWORKSPACE;
+
+    const int64_t L = cfg->bits == 2 ? 64 : 32;
+    const int64_t nblk = (Q + L - 1) / L;
+    int64_t fp_per_split = 32;
+    int64_t want_q = (kTargetWorkgroups + int64_t(B) * n_q_heads - 1) / (int64_t(B) * n_q_heads);
+    if (want_q > nblk) want_q = nblk;
+    int64_t bps = want_q > 0 ? (nblk + want_q - 1) / want_q : 1;
+    auto splits_q = [&]() { return nblk > 0 ? (nblk + bps - 1) / bps : 0; };
+    auto splits_fp = [&]() { return (n_fp + fp_per_split - 1) / fp_per_split; };
+    while (splits_q() + splits_fp() > cap_splits) {
+      if (splits_fp() > 1 && (splits_fp() >= splits_q() || splits_q() <= 1)) fp_per_split *= 2;
+      else bps *= 2;
+    }
+    AttnArgs a{};
+    a.k_codes = cache->k_codes; a.v_codes = cache->v_codes;
+    a.k_scale = cache->k_scale; a.k_zero = cache->k_zero;
+    a.v_scale = cache->v_scale; a.v_zero = cache->v_zero;
+    a.k_sink = cache->k_sink; a.v_sink = cache->v_sink;
+    a.k_resid = cache->k_resid; a.v_resid = cache->v_resid;
+    a.q = q.ptr; a.q_sb = q.stride_b; a.q_sh = q.stride_h;
+    a.ws = reinterpret_cast<float*>(workspace);
+    a.out = out;
+    const double scale = softmax_scale > 0 ? double(softmax_scale) : 1.0 / std::sqrt(double(D));
+    a.sm_scale_log2 = float(scale * 1.4426950408889634);
+    a.T = T; a.S = S; a.Q = Q; a.qcap = kvq_qcap(cfg); a.ring = R + G;
+    a.first_resid = S + Q; a.n_sink = n_sink; a.n_fp = n_fp;
+    a.H = H; a.Hq = n_q_heads; a.gqa = n_q_heads / H; a.G = int(G);
+    a.n_split_q = int(splits_q());
+    a.n_split = int(splits_q() + splits_fp());
+    a.blocks_per_split = int(bps);
+    a.fp_per_split = int(fp_per_split);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (dispatch3<AttnValuFn>(cfg, a, B, s) != hipSuccess) return KVQ_EHIP;
+    hipError_t e = D == 64 ? launch_merge<64>(a, B, s) : launch_merge<128>(a, B, s);
+    if (e != hipSuccess) return KVQ_EHIP;
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EINVAL;
+  }
+}

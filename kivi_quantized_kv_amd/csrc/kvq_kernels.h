@@ -1,0 +1,78 @@
+// Kernel argument blocks and launcher declarations shared by the libkvq
+// host API and its kernels.
+#pragma once
+
+#include "kvq_common.h"
+
+namespace kvq {
+
+// Copy full-precision rows (sinks [0, n_sink), then residual tokens
+// [first_resid, first_resid + n_rows - n_sink)) from an input tensor into
+// the sink array / residual ring.
+struct FpCopyArgs {
+  const void* src;
+  int64_t sb, sh, st;       // input strides (elements)
+  void* sink;               // [B][H][S][D]
+  void* resid;              // [B][H][ring][D]
+  int64_t n_sink, first_resid, S, ring;
+  int H;
+};
+
+// Prefill quantization of one half (keys or values).
+struct QuantArgs {
+  const void* src;
+  int64_t sb, sh, st;
+  uint8_t* codes;
+  float* scale;
+  float* zero;
+  int64_t S, qcap;
+  int H, G;
+};
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  int64_t k_sb, k_sh, v_sb, v_sh;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float *k_scale, *k_zero, *v_scale, *v_zero;
+  void *k_sink, *v_sink, *k_resid, *v_resid;
+  int64_t n_before, q_old, S, R, qcap;
+  int H, G, flush;
+};
+
+// Decode attention.  Partials: ws[((b*Hq + hq)*n_split + split)*(D+2) + ...]
+// holds o (D floats, unnormalized), then m (log2 domain), then l.
+struct AttnArgs {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float *k_scale, *k_zero, *v_scale, *v_zero;
+  const void *k_sink, *v_sink, *k_resid, *v_resid;
+  const void* q;
+  int64_t q_sb, q_sh;
+  float* ws;
+  float* out;
+  float sm_scale_log2;      // softmax scale * log2(e)
+  int64_t T, S, Q, qcap, ring, first_resid, n_sink, n_fp;
+  int H, Hq, gqa, G;
+  int n_split, n_split_q;   // total splits; the first n_split_q cover the quantized range
+  int blocks_per_split;     // value-code blocks per quantized split
+  int fp_per_split;         // full-precision tokens per fp split
+};
+
+template <int DT, int D, int BITS>
+hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_groups, int B, int H, hipStream_t s);
+template <int DT, int D, int BITS>
+hipError_t launch_quant_values(const QuantArgs& a, int64_t n_steps, int B, int H, hipStream_t s);
+template <int DT, int D>
+hipError_t launch_copy_fp(const FpCopyArgs& a, int64_t n_rows, int B, int H, hipStream_t s);
+template <int DT, int D, int BITS>
+hipError_t launch_append(const AppendArgs& a, int B, int H, hipStream_t s);
+template <int DT, int D, int BITS>
+hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s);
+template <int DT, int D, int BITS, int GQA>
+hipError_t launch_attn_mfma(const AttnArgs& a, int B, hipStream_t s);
+template <int D>
+hipError_t launch_merge(const AttnArgs& a, int B, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,226 @@
+"""Decode benchmark of the quantized KV cache on one MI355X.
+
+One step = one pass of the whole hot path for one layer: kvq_append_token
+(write the new K/V token, freezing a key group when the residual window
+fills) followed by kvq_decode_attention over the whole packed cache.  The
+default workload is the long-context 70B-shaped layer (B 1, 64 q heads,
+8 KV heads, head_dim 128, 131072 cached tokens, bf16 inputs, int4, G 64,
+R 128, 4 sinks).  Steps rotate over several layer caches whose total size
+exceeds the last-level cache, so every attention call streams its packed
+cache from HBM as in a real multi-layer decode.
+
+Prints one JSON line (metric, value, roofline, cpu_baseline, ...).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn tokens/s + effective packed-KV HBM GB/s (% of peak), int4 GQA"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def partition(T, S, R, G):
+    n_sink = min(T, S)
+    n = max(0, T - S)
+    Q = G * ((n - R) // G) if n >= R else 0
+    return n_sink, Q, n - Q
+
+
+def algorithmic_bytes(w, T: int) -> int:
+    """Bytes one decode-attention call must read: packed K and V codes, key
+    group (delta, zero) pairs, value token (delta, zero) pairs and the
+    full-precision sink + residual tokens, over all (batch, KV head)."""
+    ns, Q, nr = partition(T, w.sink, w.residual, w.group)
+    D, b = w.head_dim, w.bits
+    eb = 4 if w.dtype == "f32" else 2
+    per_head = (2 * Q * D * b // 8 + (Q // w.group) * D * 8 + Q * 8 + 2 * (ns + nr) * D * eb)
+    return per_head * w.batch * w.n_kv_heads
+
+
+def cpu_baseline(w, data, sample_seconds: float):
+    """Time the CPU oracle on a bounded sample of the same step: the decode
+    attention of the q heads of one KV head (append is negligible), scaled
+    to the whole step.  BLAS pools pinned to one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import kvq_oracle as O
+
+    T = w.n_tokens
+    geo = O.CacheGeometry(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink,
+                          w.residual, w.capacity, w.dtype)
+    t0 = time.time()
+    st = O.prefill(geo, data["K"], data["V"], T)
+    log(f"oracle prefill {time.time() - t0:.1f}s")
+    g = w.gqa
+    rows = [(0, h) for h in range(g)]          # the q heads of KV head 0
+    times = []
+    with threadpool_limits(limits=1):
+        t_end = time.time() + sample_seconds
+        while time.time() < t_end or not times:
+            t0 = time.perf_counter()
+            O.decode(geo, st, T, data["q"], w.n_q_heads, rows=rows)
+            times.append(time.perf_counter() - t0)
+    per_kv_head = sum(times) / len(times)
+    step_s = per_kv_head * w.n_kv_heads * w.batch
+    return {
+        "value": w.batch / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": (f"oracle decode attention (fp64, dequantize then attend) for the {g} q heads "
+                   f"of one KV head at T={T}, {len(times)} runs, mean {per_kv_head:.3f}s, "
+                   f"scaled x{w.n_kv_heads * w.batch} to one step; append not timed"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama70b")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="layer caches the steps rotate over (1 = warm, cache-resident)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kivi_quantized_kv_amd import kvq, synth
+
+    kvq.load_library()
+    w = synth.WORKLOADS[args.workload]
+    n_layers = max(1, args.layers)
+    per_layer_steps = -(-(args.steps + args.warmup) // n_layers)
+    n_gen = max(w.steps, 64)                    # distinct appended tokens / queries
+    steps_cap = max(n_gen, per_layer_steps)
+    t0 = time.time()
+    data = synth.generate(w, steps=n_gen)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    cfg = kvq.Config(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink, w.residual,
+                     w.n_tokens + steps_cap, w.dtype)
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    K, V = dev(data["K"]), dev(data["V"])
+    kn, vn, qn = dev(data["k_new"]), dev(data["v_new"]), dev(data["q_new"])
+    layers = [kvq.Cache(cfg)]
+    kvq.prefill(cfg, layers[0], K, V, w.n_tokens)
+    for _ in range(1, n_layers):
+        c = kvq.Cache(cfg)
+        for name in kvq.Cache.BUFFERS:
+            getattr(c, name).copy_(getattr(layers[0], name))
+        layers.append(c)
+    del K, V
+    torch.cuda.synchronize()
+    log(f"{n_layers} layer caches of {layers[0].nbytes() / 2**20:.1f} MiB prefilled")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ws = torch.empty(cfg.workspace_bytes(w.n_q_heads), dtype=torch.uint8, device="cuda")
+    n_tok = [w.n_tokens] * n_layers
+
+    def step(i):
+        li = i % n_layers
+        j = (n_tok[li] - w.n_tokens) % n_gen
+        kvq.kvq_append_token(cfg, layers[li], n_tok[li], kn[j], vn[j])
+        n_tok[li] += 1
+        kvq.kvq_decode_attention(cfg, layers[li], n_tok[li], qn[j], out=out, workspace=ws)
+        return n_tok[li]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K_ = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K_)]
+    tokens_T = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(K_):
+        li = (args.warmup + i) % n_layers
+        j = (n_tok[li] - w.n_tokens) % n_gen
+        kvq.kvq_append_token(cfg, layers[li], n_tok[li], kn[j], vn[j])
+        n_tok[li] += 1
+        ev[i][0].record()
+        kvq.kvq_decode_attention(cfg, layers[li], n_tok[li], qn[j], out=out, workspace=ws)
+        ev[i][1].record()
+        tokens_T.append(n_tok[li])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / K_
+    value = w.batch * K_ / (total_ms / 1e3)
+    bytes_per_call = [algorithmic_bytes(w, T) for T in tokens_T]
+    mean_attn_ms = sum(attn_ms) / K_
+    achieved = (sum(bytes_per_call) / K_) / (mean_attn_ms / 1e3) / 1e9
+    attn_sorted = sorted(attn_ms)
+    detail = {
+        "attn_us_mean": mean_attn_ms * 1e3,
+        "attn_us_p10": attn_sorted[K_ // 10] * 1e3,
+        "attn_us_p50": attn_sorted[K_ // 2] * 1e3,
+        "attn_us_p90": attn_sorted[(9 * K_) // 10] * 1e3,
+        "append_plus_gaps_us_mean": (total_ms - sum(attn_ms)) / K_ * 1e3,
+        "algorithmic_bytes_per_call": sum(bytes_per_call) // K_,
+        "layer_caches": n_layers,
+        "cache_mib_per_layer": round(layers[0].nbytes() / 2**20, 1),
+        "host_wall_s": round(wall, 3),
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int%d-codes/fp32-accumulate" % w.bits,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: long-context layer B{w.batch} Hq{w.n_q_heads} Hkv{w.n_kv_heads} "
+                        f"D{w.head_dim} T{w.n_tokens}+decode {w.dtype} inputs int{w.bits} "
+                        f"G{w.group} R{w.residual} S{w.sink}",
+            "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim, "cached_tokens": w.n_tokens, "bits": w.bits,
+            "group": w.group, "residual": w.residual, "sink": w.sink, "input_dtype": w.dtype,
+            "step": "append + decode attention, one layer",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kvq_decode_attention (split-K attention + merge)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "detail": detail,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

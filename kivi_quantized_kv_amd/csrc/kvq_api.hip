@@ -2,6 +2,7 @@
 // arguments on the host, derives the token partition and launch geometry,
 // and enqueues kernels on the caller's stream.  Nothing here allocates,
 // frees or synchronizes.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -12,9 +13,25 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kTargetWorkgroups = 1024;  // ~4 workgroups of 4 waves per CU
+constexpr int kTargetWorkgroups = 1024;      // VALU kernel: ~4 workgroups of 4 waves per CU
+constexpr int kTargetWorkgroupsMfma = 512;   // matrix-core kernel: ~2 per CU
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device (cached per device id; a host query,
+// no allocation).  Falls back to 256 if the query fails.
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 kvq_status check_config(const kvq_config* c) {
   if (!c) return KVQ_EINVAL;
@@ -91,6 +108,18 @@ template <int DT, int D, int BITS> struct CopyFpFn {
 template <int DT, int D, int BITS> struct AppendFn {
   static hipError_t run(const AppendArgs& a, int B, int H, hipStream_t s) {
     return launch_append<DT, D, BITS>(a, B, H, s);
+  }
+};
+template <int DT, int D, int BITS> struct AttnMfma4Fn {
+  static hipError_t run(const AttnArgs& a, int B, hipStream_t s) {
+    if constexpr (BITS == 8) return hipErrorInvalidValue;
+    else return launch_attn_mfma<DT, D, BITS, 4>(a, B, s);
+  }
+};
+template <int DT, int D, int BITS> struct AttnMfma8Fn {
+  static hipError_t run(const AttnArgs& a, int B, hipStream_t s) {
+    if constexpr (BITS == 8) return hipErrorInvalidValue;
+    else return launch_attn_mfma<DT, D, BITS, 8>(a, B, s);
   }
 };
 template <int DT, int D, int BITS> struct AttnValuFn {
@@ -218,17 +247,47 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     if (int64_t(workspace_bytes) < kvq_workspace_bytes_min(cfg, n_q_heads) || cap_splits < 2)
       return KVQ_EWORKSPACE;
 
-    const int64_t L = cfg->bits == 2 ? 64 : 32;
+    // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit
+    // codes.  It works per KV head on 64-token chunks, with the grid sized
+    // to one round of two workgroups per CU, and spreads the full-precision
+    // tokens evenly over its splits.  Everything else runs the VALU kernel
+    // per query head on value-code blocks, with the full-precision tokens in
+    // splits of their own.
+    const int gqa = n_q_heads / H;
+    const bool mfma = (gqa == 4 || gqa == 8) && cfg->bits != 8;
+    const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
     const int64_t nblk = (Q + L - 1) / L;
     int64_t fp_per_split = 32;
-    int64_t want_q = (kTargetWorkgroups + int64_t(B) * n_q_heads - 1) / (int64_t(B) * n_q_heads);
-    if (want_q > nblk) want_q = nblk;
-    int64_t bps = want_q > 0 ? (nblk + want_q - 1) / want_q : 1;
-    auto splits_q = [&]() { return nblk > 0 ? (nblk + bps - 1) / bps : 0; };
-    auto splits_fp = [&]() { return (n_fp + fp_per_split - 1) / fp_per_split; };
-    while (splits_q() + splits_fp() > cap_splits) {
-      if (splits_fp() > 1 && (splits_fp() >= splits_q() || splits_q() <= 1)) fp_per_split *= 2;
-      else bps *= 2;
+    int64_t bps = 1;
+    int64_t n_split_q = 0, n_split = 0;
+    if (mfma) {
+      const int64_t slots = 2 * int64_t(device_cu_count());
+      const int64_t rows = int64_t(B) * H;
+      int64_t want = slots / rows > 0 ? slots / rows : 1;
+      if (want > nblk) want = nblk;
+      if (want > cap_splits) want = cap_splits;
+      bps = want > 0 ? (nblk + want - 1) / want : 1;
+      n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
+      // at most ~64 exact tokens per split: splits past the chunks, if any,
+      // take exact tokens only
+      int64_t want_fp = (n_fp + 63) / 64;
+      if (want_fp > cap_splits) want_fp = cap_splits;
+      if (n_split < want_fp) n_split = want_fp;
+      if (n_split < 1) n_split = 1;
+      fp_per_split = (n_fp + n_split - 1) / n_split;
+      n_split_q = n_split;
+    } else {
+      int64_t want_q = (kTargetWorkgroups + int64_t(B) * n_q_heads - 1) / (int64_t(B) * n_q_heads);
+      if (want_q > nblk) want_q = nblk;
+      bps = want_q > 0 ? (nblk + want_q - 1) / want_q : 1;
+      auto splits_q = [&]() { return nblk > 0 ? (nblk + bps - 1) / bps : 0; };
+      auto splits_fp = [&]() { return (n_fp + fp_per_split - 1) / fp_per_split; };
+      while (splits_q() + splits_fp() > cap_splits) {
+        if (splits_fp() > 1 && (splits_fp() >= splits_q() || splits_q() <= 1)) fp_per_split *= 2;
+        else bps *= 2;
+      }
+      n_split_q = splits_q();
+      n_split = splits_q() + splits_fp();
     }
     AttnArgs a{};
     a.k_codes = cache->k_codes; a.v_codes = cache->v_codes;
@@ -243,14 +302,28 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     a.sm_scale_log2 = float(scale * 1.4426950408889634);
     a.T = T; a.S = S; a.Q = Q; a.qcap = kvq_qcap(cfg); a.ring = R + G;
     a.first_resid = S + Q; a.n_sink = n_sink; a.n_fp = n_fp;
+    a.kgroups = kvq_qcap(cfg) / G;
+    a.resid_slot0 = Q % (R + G);
     a.H = H; a.Hq = n_q_heads; a.gqa = n_q_heads / H; a.G = int(G);
-    a.n_split_q = int(splits_q());
-    a.n_split = int(splits_q() + splits_fp());
+    a.g_shift = G == 32 ? 5 : (G == 64 ? 6 : 7);
+    a.n_split_q = int(n_split_q);
+    a.n_split = int(n_split);
     a.blocks_per_split = int(bps);
     a.fp_per_split = int(fp_per_split);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (dispatch3<AttnValuFn>(cfg, a, B, s) != hipSuccess) return KVQ_EHIP;
-    hipError_t e = D == 64 ? launch_merge<64>(a, B, s) : launch_merge<128>(a, B, s);
+    // With nothing quantized yet the matrix-core path has no splits: the
+    // merge kernel alone attends the full-precision tokens.
+    hipError_t ea = hipSuccess;
+    if (a.n_split > 0) {
+      if (mfma && gqa == 8) ea = dispatch3<AttnMfma8Fn>(cfg, a, B, s);
+      else if (mfma) ea = dispatch3<AttnMfma4Fn>(cfg, a, B, s);
+      else ea = dispatch3<AttnValuFn>(cfg, a, B, s);
+    }
+    if (ea != hipSuccess) return KVQ_EHIP;
+    hipError_t e;
+    if (cfg->dtype == KVQ_F32) e = D == 64 ? launch_merge<DT_F32, 64>(a, B, s) : launch_merge<DT_F32, 128>(a, B, s);
+    else if (cfg->dtype == KVQ_F16) e = D == 64 ? launch_merge<DT_F16, 64>(a, B, s) : launch_merge<DT_F16, 128>(a, B, s);
+    else e = D == 64 ? launch_merge<DT_BF16, 64>(a, B, s) : launch_merge<DT_BF16, 128>(a, B, s);
     if (e != hipSuccess) return KVQ_EHIP;
     return KVQ_OK;
   } catch (...) {

@@ -110,11 +110,11 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
       for (int st = 0; st < kNST; ++st) {
         if (st * 16 >= nvalid) { sc[st] = -__builtin_inff(); continue; }
         const int64_t u = base_u + st * 16 + tl;
-        const int64_t grp = (base_u + st * 16) / a.G;
+        const int64_t grp = (base_u + st * 16) >> a.g_shift;
         if (grp != cur_grp) {
           cur_grp = grp;
-          const float* ks = a.k_scale + (bh * (a.qcap / a.G) + grp) * D + qt * kQuarterCh;
-          const float* kz = a.k_zero + (bh * (a.qcap / a.G) + grp) * D + qt * kQuarterCh;
+          const float* ks = a.k_scale + (bh * a.kgroups + grp) * D + qt * kQuarterCh;
+          const float* kz = a.k_zero + (bh * a.kgroups + grp) * D + qt * kQuarterCh;
           float kp = 0.f;
 #pragma unroll
           for (int c = 0; c < kQuarterCh; ++c) {
@@ -202,14 +202,15 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
     const int64_t f0 = int64_t(split - a.n_split_q) * a.fp_per_split;
     const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
     for (int64_t i = f0 + wave; i < f1; i += 4) {
-      const int64_t t = i < a.n_sink ? i : a.first_resid + (i - a.n_sink);
       const void* kb;
       const void* vb;
       int64_t off;
-      if (t < a.S) {
-        kb = a.k_sink; vb = a.v_sink; off = (bh * a.S + t) * D;
+      if (i < a.n_sink) {
+        kb = a.k_sink; vb = a.v_sink; off = (bh * a.S + i) * D;
       } else {
-        kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + (t - a.S) % a.ring) * D;
+        int64_t slot = a.resid_slot0 + (i - a.n_sink);   // < 2 * ring
+        if (slot >= a.ring) slot -= a.ring;
+        kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + slot) * D;
       }
       float dot = 0.f;
 #pragma unroll
@@ -255,30 +256,52 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials: one wave per (q head, batch).
+// Log-sum-exp merge of the split partials: one workgroup per (q head, batch).
 // M = max_j m_j, L = sum_j 2^(m_j - M) l_j, out = sum_j 2^(m_j - M) o_j / L.
+// All partial loads are independent: splits spread over the threads for M
+// and the weights, then (channel, split-subset) pairs for the outputs.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(64) void k_merge(AttnArgs a) {
+template <int DT, int D>
+__global__ __launch_bounds__(256) void k_merge(AttnArgs a) {
+  constexpr int kSub = 256 / D;             // token / split subsets per channel
+  __shared__ float s_w[KVQ_MAX_SPLITS_DEV];
+  __shared__ float s_red[8];
+  __shared__ float s_part[kSub][D];
   const int hq = blockIdx.x, b = blockIdx.y;
-  const float* src = a.ws + (int64_t(b) * a.Hq + hq) * a.n_split * (D + 2);
-  float M = -__builtin_inff();
-  for (int j = 0; j < a.n_split; ++j) M = __builtin_fmaxf(M, src[j * (D + 2) + D]);
-  constexpr int kC = D / 64;
-  float o[kC], L = 0.f;
-#pragma unroll
-  for (int k = 0; k < kC; ++k) o[k] = 0.f;
-  for (int j = 0; j < a.n_split; ++j) {
-    const float* pj = src + j * (D + 2);
-    const float e = __builtin_amdgcn_exp2f(pj[D] - M);
-    L = __builtin_fmaf(e, pj[D + 1], L);
-#pragma unroll
-    for (int k = 0; k < kC; ++k) o[k] = __builtin_fmaf(e, pj[threadIdx.x + 64 * k], o[k]);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int d = t % D, sub = t / D;
+
+  // ---- split partials
+  const int ns = a.n_split;
+  const float* src = a.ws + (int64_t(b) * a.Hq + hq) * ns * (D + 2);
+  float mx = -__builtin_inff();
+  for (int j = t; j < ns; j += 256) mx = __builtin_fmaxf(mx, src[j * (D + 2) + D]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  const float M = __builtin_fmaxf(__builtin_fmaxf(s_red[0], s_red[1]),
+                                  __builtin_fmaxf(s_red[2], s_red[3]));
+  float lsum = 0.f;
+  for (int j = t; j < ns; j += 256) {
+    const float e = __builtin_amdgcn_exp2f(src[j * (D + 2) + D] - M);
+    s_w[j] = e;
+    lsum = __builtin_fmaf(e, src[j * (D + 2) + D + 1], lsum);
   }
-  float* dst = a.out + (int64_t(b) * a.Hq + hq) * D;
-  const float inv = 1.0f / L;
+  lsum = wave_sum(lsum);
+  __syncthreads();
+  if (lane == 0) s_red[4 + wave] = lsum;
+  float o = 0.f;
+#pragma unroll 8
+  for (int j = sub; j < ns; j += kSub) o = __builtin_fmaf(s_w[j], src[j * (D + 2) + d], o);
+  s_part[sub][d] = o;
+  __syncthreads();
+  if (t < D) {
+    const float L = s_red[4] + s_red[5] + s_red[6] + s_red[7];
+    float acc = 0.f;
 #pragma unroll
-  for (int k = 0; k < kC; ++k) dst[threadIdx.x + 64 * k] = o[k] * inv;
+    for (int k = 0; k < kSub; ++k) acc += s_part[k][t];
+    a.out[(int64_t(b) * a.Hq + hq) * D + t] = acc / L;
+  }
 }
 
 template <int DT, int D, int BITS>
@@ -286,9 +309,9 @@ hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s) {
   hipLaunchKernelGGL((k_attn_valu<DT, D, BITS>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
-template <int D>
+template <int DT, int D>
 hipError_t launch_merge(const AttnArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((k_merge<D>), dim3(a.Hq, B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((k_merge<DT, D>), dim3(a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -302,7 +325,11 @@ KVQ_INST_VALU(DT_F16, 64)
 KVQ_INST_VALU(DT_F16, 128)
 KVQ_INST_VALU(DT_BF16, 64)
 KVQ_INST_VALU(DT_BF16, 128)
-template hipError_t launch_merge<64>(const AttnArgs&, int, hipStream_t);
-template hipError_t launch_merge<128>(const AttnArgs&, int, hipStream_t);
+#define KVQ_INST_MERGE(DT)                                                     \
+  template hipError_t launch_merge<DT, 64>(const AttnArgs&, int, hipStream_t); \
+  template hipError_t launch_merge<DT, 128>(const AttnArgs&, int, hipStream_t);
+KVQ_INST_MERGE(DT_F32)
+KVQ_INST_MERGE(DT_F16)
+KVQ_INST_MERGE(DT_BF16)
 
 }  // namespace kvq

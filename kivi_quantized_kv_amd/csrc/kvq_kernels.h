@@ -54,10 +54,12 @@ struct AttnArgs {
   float* out;
   float sm_scale_log2;      // softmax scale * log2(e)
   int64_t T, S, Q, qcap, ring, first_resid, n_sink, n_fp;
-  int H, Hq, gqa, G;
+  int64_t kgroups;          // qcap / G
+  int64_t resid_slot0;      // ring slot of the first residual token, Q mod ring
+  int H, Hq, gqa, G, g_shift;
   int n_split, n_split_q;   // total splits; the first n_split_q cover the quantized range
   int blocks_per_split;     // value-code blocks per quantized split
-  int fp_per_split;         // full-precision tokens per fp split
+  int fp_per_split;         // full-precision tokens per split that takes them
 };
 
 template <int DT, int D, int BITS>
@@ -72,7 +74,7 @@ template <int DT, int D, int BITS>
 hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s);
 template <int DT, int D, int BITS, int GQA>
 hipError_t launch_attn_mfma(const AttnArgs& a, int B, hipStream_t s);
-template <int D>
+template <int DT, int D>
 hipError_t launch_merge(const AttnArgs& a, int B, hipStream_t s);
 
 }  // namespace kvq

@@ -1,0 +1,633 @@
+// Split-K decode attention on the matrix cores, for GQA groups of 4 or 8
+// query heads per KV head (the group makes q.K^T and P.V dense tiles),
+// with 2- or 4-bit codes.
+//
+// Method: softmax(scale * q K^T) V over the cache dequantized inside the
+// kernel (pigeon guide "KV-cache quantization", How it works step 5), GQA
+// as in tract PR "KIVI-style KV-cache quantization", What's in the PR.
+//
+// Per wave and 64-token chunk:
+//   q.K^T : S^T[16 tokens x 16 cols] = C[16 x D] . Q'[D x 16] per 16-token
+//           tile, v_mfma_f32_16x16x32_f16.  C holds each code as the fp16
+//           value u = 1 + c * 2^(a-10) (code bits placed at mantissa bit a
+//           under a 1.0 exponent: exact, one and-or per two codes); Q'
+//           holds q''_d = 2^(10-a) * scale*log2e * q_d * delta_d split into
+//           an fp16 high part (cols 0..GQA-1) and low part (cols GQA..2GQA-1),
+//           so the product keeps ~22 bits of q''.  The accumulator starts at
+//           kappa = sum_d scale*log2e * q_d * (zero_d - 2^(10-a) delta_d) in
+//           the high columns; hi + lo columns are joined with one DPP rotate.
+//   P.V   : O[16 rows x 16 ch] += P'[16 x 32 tokens] . Vc[32 x 16 ch],
+//           v_mfma_f32_16x16x32_bf16, rows = heads (bf16 high and low parts
+//           of P''_t = 2^(7-a) p_t delta_t), Vc = codes as bf16 1 + c 2^(a-7).
+//           sum_t p_t (zero_t - 2^(7-a) delta_t) is added per head at the end.
+// The value-code layout puts, for each 32-token step, the 8 tokens a lane
+// holds in the S^T accumulator for one channel in one 32-bit unit, so the
+// P' operand comes straight from the q.K^T output registers.
+//
+// Memory pipeline: a wave walks a contiguous run of chunks; while it
+// computes chunk c the codes of chunk c+1 are already in flight into
+// registers, and so are its key/value parameters, which are staged through
+// wave-private LDS (broadcast reads) when the chunk comes up.
+//
+// MFMA operand layout (16x16x32, 64 lanes): lane l holds A[row l%16][k in
+// group l/16] and B[k in group l/16][col l%16] (8 values each, the same
+// k order for A and B), and D[rows 4*(l/16) .. +3][col l%16].
+#include <type_traits>
+
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Round-to-nearest-even packing of two floats (v_cvt_pk_f16_f32 /
+// v_cvt_pk_bf16_f32).  Nearest rounding keeps the high/low splits
+// unbiased, so their errors do not accumulate over long token ranges.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
+}
+
+// (x & mask) | one.  With the two constants held in registers (see opaque)
+// rather than as literals, which the three-operand encoding cannot take,
+// the compiler selects a single v_and_or_b32.  Written in C, not inline
+// assembly, so the compiler's hazard tracking sees every register write
+// next to in-flight matrix instructions.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t one) {
+  return (x & mask) | one;
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Two codes of a 32-bit word at bit offsets POS and POS + 16 as a pair of
+// 16-bit floats whose mantissa holds the code at bit A.
+template <int A, int POS>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t mask_at_a, uint32_t one) {
+  constexpr int kNet = A - POS;
+  uint32_t x;
+  if constexpr (kNet > 0) x = w << kNet;
+  else if constexpr (kNet < 0) x = w >> (-kNet);
+  else x = w;
+  return and_or(x, mask_at_a, one);
+}
+
+// Where each code sits in the fp16 mantissa on the key side, per code index
+// ci of the low half of a 32-bit word (pairs are (ci, ci + 16/BITS)):
+//   4-bit: all at bit 4 (nibble ci at bit 4ci: shifts <<4, 0, >>4, >>8);
+//   2-bit: crumbs 0..2 at bit 4, crumb 3 at bit 6, crumbs 4..7 at bit 8
+//          (crumbs 2, 3 and 4 need no shift).
+template <int BITS>
+__host__ __device__ constexpr int key_mant_bit(int ci) {
+  return BITS == 4 ? 4 : (ci < 3 ? 4 : (ci == 3 ? 6 : 8));
+}
+// Value side (bf16): 4-bit codes at bit 3, 2-bit codes at bit 5.
+template <int BITS>
+__host__ __device__ constexpr int val_mant_bit() { return BITS == 4 ? 3 : 5; }
+
+template <int BITS>
+__host__ __device__ constexpr uint32_t field_mask(int a) {
+  return (((1u << BITS) - 1u) << a) * 0x00010001u;
+}
+
+// The four fp16 pairs (one MFMA operand) of key-side K-step SP of word w.
+template <int BITS, int SP>
+__device__ __forceinline__ u32x4_t key_operand(uint32_t w, const uint32_t* km, uint32_t one) {
+  u32x4_t r;
+  if constexpr (BITS == 4) {
+    r[0] = code_pair<4, 0>(w, km[0], one);
+    r[1] = code_pair<4, 4>(w, km[0], one);
+    r[2] = code_pair<4, 8>(w, km[0], one);
+    r[3] = code_pair<4, 12>(w, km[0], one);
+  } else if constexpr (SP == 0) {
+    r[0] = code_pair<4, 0>(w, km[0], one);
+    r[1] = code_pair<4, 2>(w, km[0], one);
+    r[2] = code_pair<4, 4>(w, km[0], one);
+    r[3] = code_pair<6, 6>(w, km[1], one);
+  } else {
+    r[0] = code_pair<8, 8>(w, km[2], one);
+    r[1] = code_pair<8, 10>(w, km[2], one);
+    r[2] = code_pair<8, 12>(w, km[2], one);
+    r[3] = code_pair<8, 14>(w, km[2], one);
+  }
+  return r;
+}
+
+// The four bf16 pairs of value-side step S (slots r + 4S, r + 4S + U/2).
+template <int BITS, int S>
+__device__ __forceinline__ u32x4_t value_operand(uint32_t w, uint32_t vm, uint32_t one) {
+  constexpr int A = val_mant_bit<BITS>();
+  u32x4_t r;
+  r[0] = code_pair<A, BITS * (0 + 4 * S)>(w, vm, one);
+  r[1] = code_pair<A, BITS * (1 + 4 * S)>(w, vm, one);
+  r[2] = code_pair<A, BITS * (2 + 4 * S)>(w, vm, one);
+  r[3] = code_pair<A, BITS * (3 + 4 * S)>(w, vm, one);
+  return r;
+}
+
+// N consecutive 32-bit words from a 4*N-byte aligned address, as wide loads.
+template <int N>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* out) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const u32x4_t v = reinterpret_cast<const u32x4_t*>(p)[i / 4];
+      out[i] = v[0]; out[i + 1] = v[1]; out[i + 2] = v[2]; out[i + 3] = v[3];
+    }
+  } else if constexpr (N == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    out[0] = v.x; out[1] = v.y;
+  } else {
+    out[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// Registers of one 64-token chunk in flight.
+template <int D, int BITS>
+struct ChunkRegs {
+  static constexpr int kQW = (D / 4) * BITS / 32;    // key words per lane per tile
+  static constexpr int kNB = D / 16;                 // value words per lane per block
+  static constexpr int kVB = 64 / VLayout<BITS>::L;  // value blocks per chunk
+  static constexpr int kKP = 2 * D / 64;             // key-param floats per lane per group
+  uint32_t kw[4][kQW];
+  uint32_t vw[kVB][kNB];
+  float kp[2][kKP];   // key (delta | zero) of up to two groups, one slice per lane
+  float vp[2];        // value delta (lanes 0..31) or zero (32..63), two tokens
+};
+
+template <int DT, int D, int BITS, int GQA, bool G32>
+__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
+  using VLy = VLayout<BITS>;
+  using CR = ChunkRegs<D, BITS>;
+  constexpr int kRB = D * BITS / 8;        // bytes per key row
+  constexpr int kQCH = D / 4;              // channels of a lane's quarter row
+  constexpr int kCPW = 32 / BITS;          // codes per 32-bit word
+  constexpr int kQW = CR::kQW;
+  constexpr int kKS = D / 32;              // K-steps of q.K^T
+  constexpr int kNB = CR::kNB;
+  constexpr int kVB = CR::kVB;
+  constexpr int kKP = CR::kKP;
+  constexpr int kStepsPerWord = kCPW / 8;  // K-steps covered by one code word
+  constexpr int kVA = val_mant_bit<BITS>();
+  constexpr float FV = float(1 << (7 - kVA));
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = int64_t(b) * a.H + h;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, lg = lane >> 4;
+  const int hh = col % GQA;                          // head of this column
+  const bool is_lo = ((col / GQA) & 1) != 0;         // low part column
+  const bool owner = col < GQA;                      // counts l and z once
+
+  __shared__ float s_q[GQA][D];
+  __shared__ float s_qf[GQA][D];   // s_q times the key-side factor 2^(10-a) of channel d
+  __shared__ float s_o[4][GQA][D];
+  __shared__ float s_m[4][GQA], s_l[4][GQA], s_z[4][GQA];
+  // wave-private staging of the current chunk's parameters
+  __shared__ float4 s_kp[4][2][2 * D / 4];   // [wave][group][delta | zero]
+  __shared__ float4 s_vp[4][2][16];          // [wave][delta | zero][64 tokens]
+
+  for (int x = threadIdx.x; x < GQA * D; x += 256) {
+    const int qh = x / D, d = x % D;
+    const float qv = load1<DT>(a.q, b * a.q_sb + (h * GQA + qh) * a.q_sh + d) * a.sm_scale_log2;
+    // channel d is code index d % kCPW of its word; its pair index is that
+    // modulo kCPW / 2
+    const int ci = (d % kCPW) % (kCPW / 2);
+    s_q[qh][d] = qv;
+    s_qf[qh][d] = qv * float(1 << (10 - key_mant_bit<BITS>(ci)));
+  }
+  __syncthreads();
+
+  {
+    // ------------------------------------------------------------ quantized
+    const uint32_t one16 = opaque(0x3C003C00u), one_bf = opaque(0x3F803F80u);
+    uint32_t km[3];
+    if constexpr (BITS == 4) {
+      km[0] = opaque(field_mask<4>(4));
+      km[1] = km[0];
+      km[2] = km[0];
+    } else {
+      km[0] = opaque(field_mask<2>(4));
+      km[1] = opaque(field_mask<2>(6));
+      km[2] = opaque(field_mask<2>(8));
+    }
+    const uint32_t vmask = opaque(field_mask<BITS>(kVA));
+
+    f32x4_t acc[kNB];
+#pragma unroll
+    for (int n = 0; n < kNB; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -__builtin_inff(), l = 0.f, z = 0.f;
+    u32x4_t qB[kKS];
+    float kap = 0.f;
+    int64_t cur_grp = -1;
+    const float neg_lo = is_lo ? -1.0f : 0.0f;
+
+    const int64_t nch = (a.Q + 63) >> 6;
+    // chunk range of this split (empty for splits that only take exact tokens)
+    const int64_t c0_raw = int64_t(split) * a.blocks_per_split;
+    const int64_t c0 = c0_raw < nch ? c0_raw : nch;
+    const int64_t c1 = c0 + a.blocks_per_split < nch ? c0 + a.blocks_per_split : nch;
+    const int64_t per_wave = (c1 - c0 + 3) >> 2;
+    const int64_t wc0 = c0 + wave * per_wave;
+    const int64_t wc1 = wc0 + per_wave < c1 ? wc0 + per_wave : c1;
+    const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRB;
+    const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRB;
+    const float* vs_head = a.v_scale + bh * a.qcap;
+    const float* vz_head = a.v_zero + bh * a.qcap;
+    const float* ks_head = a.k_scale + bh * a.kgroups * D;
+    const float* kz_head = a.k_zero + bh * a.kgroups * D;
+    const int gsh = a.g_shift;
+    const int G = a.G;
+
+    // Key groups a chunk needs: G = 32: two (one per half); G >= 64: one,
+    // loaded when the chunk starts a group or is the wave's first chunk.
+    auto need_group = [&](int64_t ch, int gi, int nv) {
+      if constexpr (G32) return gi == 0 || nv > 32;
+      else return gi == 0 && (((ch << 6) & (G - 1)) == 0 || ch == wc0);
+    };
+
+    // issue the loads of chunk ch into r (all addresses inside the cache)
+    auto load_chunk = [&](int64_t ch, CR& r) {
+      const int64_t base = ch << 6;
+      const int nv = int(a.Q - base < 64 ? a.Q - base : 64);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t * 16 < nv)
+          load_words<kQW>(kc_head + (base + 16 * t + col) * kRB + lg * (kQW * 4), r.kw[t]);
+#pragma unroll
+      for (int vb = 0; vb < kVB; ++vb)
+        if (vb * VLy::L < nv)
+          load_words<kNB>(vc_head + (base / VLy::L + vb) * (VLy::L * kRB) + (lg * 16 + col) * kNB * 4,
+                          r.vw[vb]);
+      const int64_t g0 = base >> gsh;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        if (need_group(ch, gi, nv)) {
+          const int off = lane * kKP;   // slice of [delta (D) | zero (D)]
+          const float* src = off < D ? ks_head + (g0 + gi) * D + off
+                                     : kz_head + (g0 + gi) * D + (off - D);
+          if constexpr (kKP == 4) {
+            const float4 v = *reinterpret_cast<const float4*>(src);
+            r.kp[gi][0] = v.x; r.kp[gi][1] = v.y; r.kp[gi][2] = v.z; r.kp[gi][3] = v.w;
+          } else {
+            const float2 v = *reinterpret_cast<const float2*>(src);
+            r.kp[gi][0] = v.x; r.kp[gi][1] = v.y;
+          }
+        }
+      }
+      const int tok = (lane & 31) * 2;
+      if (tok < nv) {
+        const float2 v = *reinterpret_cast<const float2*>((lane < 32 ? vs_head : vz_head) + base + tok);
+        r.vp[0] = v.x;
+        r.vp[1] = v.y;
+      } else {
+        r.vp[0] = 0.f;
+        r.vp[1] = 0.f;
+      }
+    };
+
+    auto process_chunk = [&](int64_t ch, CR& r, auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      const int64_t base = ch << 6;
+      const int nv = FULL ? 64 : 32;           // a partial chunk holds 32 tokens
+      const int ntile = FULL ? 4 : 2;
+      const int64_t g0 = base >> gsh;
+      // ---- stage this chunk's parameters in LDS (wave-private)
+      {
+        float* kpd = reinterpret_cast<float*>(&s_kp[wave][0][0]);
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+          if (need_group(ch, gi, nv))
+#pragma unroll
+            for (int i = 0; i < kKP; ++i) kpd[gi * 2 * D + lane * kKP + i] = r.kp[gi][i];
+        // values: fd = FV * delta (lanes 0..31) and w = zero - FV * delta
+        // (lanes 32..63, which fetch delta from the partner lane)
+        float* vpd = reinterpret_cast<float*>(&s_vp[wave][0][0]);
+        const int tok = (lane & 31) * 2;
+        const float o0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                      (lane ^ 32) << 2, __builtin_bit_cast(int, r.vp[0])));
+        const float o1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                      (lane ^ 32) << 2, __builtin_bit_cast(int, r.vp[1])));
+        const float fd0 = FV * (lane < 32 ? r.vp[0] : o0);
+        const float fd1 = FV * (lane < 32 ? r.vp[1] : o1);
+        vpd[(lane >> 5) * 64 + tok] = lane < 32 ? fd0 : r.vp[0] - fd0;
+        vpd[(lane >> 5) * 64 + tok + 1] = lane < 32 ? fd1 : r.vp[1] - fd1;
+      }
+      wave_lds_sync();
+      // ---- q.K^T: per key-group segment, K-steps outer, tiles inner
+      f32x4_t sc[4];
+#pragma unroll
+      for (int seg = 0; seg < 2; ++seg) {
+        constexpr int kSegTiles = G32 ? 2 : 4;
+        const int t_begin = seg * kSegTiles;
+        const int t_end = t_begin + kSegTiles;
+        if (t_begin >= ntile) break;
+        const int64_t grp = g0 + (G32 ? seg : 0);
+        if (grp != cur_grp) {
+          cur_grp = grp;
+          const float* kpd = reinterpret_cast<const float*>(&s_kp[wave][G32 ? seg : 0][0]);
+          float kpart = 0.f;
+#pragma unroll
+          for (int kk = 0; kk < kKS; ++kk) {
+            const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
+            // the 8 channels of this K-step: code indices r + 4sp and
+            // r + 4sp + kCPW/2 of word wk (r = 0..3), as two runs of 4
+            const int cA = lg * kQCH + wk * kCPW + 4 * sp;
+            const int cB = cA + kCPW / 2;
+            const float4 qa = *reinterpret_cast<const float4*>(&s_q[hh][cA]);
+            const float4 qb = *reinterpret_cast<const float4*>(&s_q[hh][cB]);
+            const float4 fa = *reinterpret_cast<const float4*>(&s_qf[hh][cA]);
+            const float4 fb = *reinterpret_cast<const float4*>(&s_qf[hh][cB]);
+            const float4 da = *reinterpret_cast<const float4*>(kpd + cA);
+            const float4 db = *reinterpret_cast<const float4*>(kpd + cB);
+            const float4 za = *reinterpret_cast<const float4*>(kpd + D + cA);
+            const float4 zb = *reinterpret_cast<const float4*>(kpd + D + cB);
+            const float sqa[4] = {qa.x, qa.y, qa.z, qa.w}, sqb[4] = {qb.x, qb.y, qb.z, qb.w};
+            const float sfa[4] = {fa.x, fa.y, fa.z, fa.w}, sfb[4] = {fb.x, fb.y, fb.z, fb.w};
+            const float dla[4] = {da.x, da.y, da.z, da.w}, dlb[4] = {db.x, db.y, db.z, db.w};
+            const float zra[4] = {za.x, za.y, za.z, za.w}, zrb[4] = {zb.x, zb.y, zb.z, zb.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float x0 = sfa[r] * dla[r];
+              const float x1 = sfb[r] * dlb[r];
+              kpart = __builtin_fmaf(sqa[r], zra[r], kpart) - x0;
+              kpart = __builtin_fmaf(sqb[r], zrb[r], kpart) - x1;
+              // high part in the high columns, x - high in the low columns
+              const h2_t hv = __builtin_bit_cast(h2_t, pack_f16(x0, x1));
+              const float r0 = __builtin_fmaf((float)hv[0], neg_lo, x0);
+              const float r1 = __builtin_fmaf((float)hv[1], neg_lo, x1);
+              qB[kk][r] = pack_f16(r0, r1);
+            }
+          }
+          kpart += swz_xor16(kpart);
+          kap = kpart + xor32(kpart);
+        }
+        const float init = is_lo ? 0.f : kap;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (t >= t_begin && t < t_end) sc[t] = f32x4_t{init, init, init, init};
+#pragma unroll
+        for (int kk = 0; kk < kKS; ++kk) {
+          const int wk = kk / kStepsPerWord;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (t < t_begin || t >= t_end || (!FULL && t >= 2)) continue;
+            u32x4_t av;
+            if (kk % kStepsPerWord == 0) av = key_operand<BITS, 0>(r.kw[t][wk], km, one16);
+            else av = key_operand<BITS, 1>(r.kw[t][wk], km, one16);
+            sc[t] = mfma_f16(av, qB[kk], sc[t]);
+          }
+        }
+      }
+      // join the high and low columns of each head
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t >= ntile) {
+          sc[t] = f32x4_t{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+          continue;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float other;
+          if constexpr (GQA == 8) other = dpp_mov<kRowRor8>(sc[t][i]);
+          else other = dpp_mov<kRowRor4>(sc[t][i]);
+          sc[t][i] += other;
+        }
+      }
+      // ---- online softmax (log2 domain); m is per head, uniform over lanes
+      float cmax = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cmax = __builtin_fmaxf(cmax, sc[t][i]);
+      cmax = __builtin_fmaxf(cmax, swz_xor16(cmax));
+      cmax = __builtin_fmaxf(cmax, xor32(cmax));
+      const float new_m = __builtin_fmaxf(m, cmax);
+      if (__builtin_amdgcn_ballot_w64(new_m > m) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m - new_m);
+        l *= alpha;
+        z *= alpha;
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ar[i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                ((4 * lg + i) % GQA) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+        for (int n = 0; n < kNB; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[n][i] *= ar[i];
+        m = new_m;
+      }
+      // ---- P.V per 32-token step (tiles 2ps, 2ps+1)
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+        if (ps * 32 >= nv) break;
+        const int t0 = 2 * ps, t1 = 2 * ps + 1;
+        const float4 d0v = s_vp[wave][0][4 * t0 + lg];
+        const float4 d1v = s_vp[wave][0][4 * t1 + lg];
+        const float4 w0v = s_vp[wave][1][4 * t0 + lg];
+        const float4 w1v = s_vp[wave][1][4 * t1 + lg];
+        const float d0s[4] = {d0v.x, d0v.y, d0v.z, d0v.w}, d1s[4] = {d1v.x, d1v.y, d1v.z, d1v.w};
+        const float w0s[4] = {w0v.x, w0v.y, w0v.z, w0v.w}, w1s[4] = {w1v.x, w1v.y, w1v.z, w1v.w};
+        u32x4_t ap;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[t0][rr] - m);
+          const float p1 = __builtin_amdgcn_exp2f(sc[t1][rr] - m);
+          l += p0 + p1;                       // every lane; owners are kept at the end
+          z = __builtin_fmaf(p0, w0s[rr], z);
+          z = __builtin_fmaf(p1, w1s[rr], z);
+          const float x0 = p0 * d0s[rr];
+          const float x1 = p1 * d1s[rr];
+          // bf16 high part in the high rows, bf16(x - high) in the low rows
+          const uint32_t hb = pack_bf16(x0, x1);
+          const float y0 = __builtin_fmaf(__builtin_bit_cast(float, hb << 16), neg_lo, x0);
+          const float y1 = __builtin_fmaf(__builtin_bit_cast(float, hb & 0xFFFF0000u), neg_lo, x1);
+          ap[rr] = pack_bf16(y0, y1);
+        }
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) {
+          u32x4_t bv;
+          if constexpr (kVB == 2) {
+            bv = value_operand<BITS, 0>(r.vw[ps][n], vmask, one_bf);
+          } else {
+            if (ps == 0) bv = value_operand<BITS, 0>(r.vw[0][n], vmask, one_bf);
+            else bv = value_operand<BITS, 1>(r.vw[0][n], vmask, one_bf);
+          }
+          acc[n] = mfma_bf16(ap, bv, acc[n]);
+        }
+      }
+      wave_lds_sync();
+    };
+
+    // only the last chunk of the quantized range can be a half chunk
+    const int64_t full_end = (a.Q & 63) ? nch - 1 : nch;
+    auto run_chunk = [&](int64_t ch, CR& r) {
+      if (ch < full_end) process_chunk(ch, r, std::true_type{});
+      else process_chunk(ch, r, std::false_type{});
+    };
+    CR ra, rb;
+    if (wc0 < wc1) load_chunk(wc0, ra);
+    for (int64_t ch = wc0; ch < wc1; ch += 2) {
+      if (ch + 1 < wc1) load_chunk(ch + 1, rb);
+      run_chunk(ch, ra);
+      if (ch + 1 >= wc1) break;
+      if (ch + 2 < wc1) load_chunk(ch + 2, ra);
+      run_chunk(ch + 1, rb);
+    }
+    // ---- full-precision tokens of this split (sinks and the residual
+    // window), one per wave in turn, folded into the same softmax state and
+    // accumulator rows: scores as fp32 dot products, values added to the
+    // high rows.
+    {
+      const int64_t f0 = int64_t(split) * a.fp_per_split;
+      const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
+      for (int64_t i = f0 + wave; i < f1; i += 4) {
+        const void* kb;
+        const void* vb;
+        int64_t off;
+        if (i < a.n_sink) {
+          kb = a.k_sink; vb = a.v_sink; off = (bh * a.S + i) * D;
+        } else {
+          int64_t slot = a.resid_slot0 + (i - a.n_sink);   // < 2 * ring
+          if (slot >= a.ring) slot -= a.ring;
+          kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + slot) * D;
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int c = 0; c < kQCH; c += 4) {
+          float k4[4];
+          load4<DT>(kb, off + lg * kQCH + c, k4);
+          const float4 q4 = *reinterpret_cast<const float4*>(&s_q[hh][lg * kQCH + c]);
+          part = __builtin_fmaf(k4[0], q4.x, part);
+          part = __builtin_fmaf(k4[1], q4.y, part);
+          part = __builtin_fmaf(k4[2], q4.z, part);
+          part = __builtin_fmaf(k4[3], q4.w, part);
+        }
+        part += swz_xor16(part);
+        const float sc = part + xor32(part);          // score of head hh
+        const float new_m = __builtin_fmaxf(m, sc);
+        if (__builtin_amdgcn_ballot_w64(new_m > m) != 0) {
+          const float alpha = __builtin_amdgcn_exp2f(m - new_m);
+          l *= alpha;
+          z *= alpha;
+          float ar[4];
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2)
+            ar[i2] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                   ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+          for (int n = 0; n < kNB; ++n)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] *= ar[i2];
+          m = new_m;
+        }
+        const float p = __builtin_amdgcn_exp2f(sc - m);
+        if (lg == 0) l += p;                          // one lane group per column
+        float pr[4];
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                        ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, p)));
+          pr[i2] = (4 * lg + i2) < GQA ? v : 0.f;     // high rows only
+        }
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) {
+          const float v = load1<DT>(vb, off + 16 * n + col);
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] = __builtin_fmaf(pr[i2], v, acc[n][i2]);
+        }
+      }
+    }
+    // ---- wave result: join high and low rows, reduce l and z over the
+    // lane groups of the owner columns
+    if (!owner) {
+      l = 0.f;
+      z = 0.f;
+    }
+    l += swz_xor16(l);
+    l += xor32(l);
+    z += swz_xor16(z);
+    z += xor32(z);
+    if (lane < GQA) {
+      s_m[wave][lane] = m;
+      s_l[wave][lane] = l;
+      s_z[wave][lane] = z;
+    }
+#pragma unroll
+    for (int n = 0; n < kNB; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[n][i];
+        if constexpr (GQA == 8) v += xor32(v);       // rows r and r + 8
+        else v += swz_xor16(v);                      // rows r and r + 4
+        const int row = 4 * lg + i;
+        if (row < GQA) s_o[wave][row][n * 16 + col] = v;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- merge the four waves; write this split's partial for each head
+  for (int x = threadIdx.x; x < GQA * D; x += 256) {
+    const int qh = x / D, d = x % D;
+    float M = s_m[0][qh];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, s_m[w][qh]);
+    // a split with no tokens at all leaves m = -inf, l = 0, o = 0
+    const float Mref = M == -__builtin_inff() ? 0.f : M;
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = __builtin_amdgcn_exp2f(s_m[w][qh] - Mref);
+      o = __builtin_fmaf(f, s_o[w][qh][d] + s_z[w][qh], o);
+      L = __builtin_fmaf(f, s_l[w][qh], L);
+    }
+    float* dst = a.ws + ((int64_t(b) * a.Hq + h * GQA + qh) * a.n_split + split) * (D + 2);
+    dst[d] = o;
+    if (d == 0) {
+      dst[D] = M;
+      dst[D + 1] = L;
+    }
+  }
+}
+
+template <int DT, int D, int BITS, int GQA>
+hipError_t launch_attn_mfma(const AttnArgs& a, int B, hipStream_t s) {
+  if (a.G == 32)
+    hipLaunchKernelGGL((k_attn_mfma<DT, D, BITS, GQA, true>), dim3(a.n_split, a.H, B), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_mfma<DT, D, BITS, GQA, false>), dim3(a.n_split, a.H, B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+#define KVQ_INST_MFMA(DT, D)                                                           \
+  template hipError_t launch_attn_mfma<DT, D, 2, 4>(const AttnArgs&, int, hipStream_t); \
+  template hipError_t launch_attn_mfma<DT, D, 2, 8>(const AttnArgs&, int, hipStream_t); \
+  template hipError_t launch_attn_mfma<DT, D, 4, 4>(const AttnArgs&, int, hipStream_t); \
+  template hipError_t launch_attn_mfma<DT, D, 4, 8>(const AttnArgs&, int, hipStream_t);
+KVQ_INST_MFMA(DT_F32, 64)
+KVQ_INST_MFMA(DT_F32, 128)
+KVQ_INST_MFMA(DT_F16, 64)
+KVQ_INST_MFMA(DT_F16, 128)
+KVQ_INST_MFMA(DT_BF16, 64)
+KVQ_INST_MFMA(DT_BF16, 128)
+
+}  // namespace kvq

@@ -52,6 +52,15 @@ SMALL = [
     (1, 32, 8, 128, 4, 32, 4, 128, 2048, "bf16"),
     (1, 16, 4, 128, 2, 32, 4, 128, 2080, "bf16"),
     (2, 2, 2, 64, 2, 32, 2, 32, 98, "f32"),        # 2-bit with a half value block
+    # matrix-core path: GQA 4 / 8, 2 / 4 bits, D 64 / 128, G 32 / 64 / 128,
+    # chunks of 64 tokens with a half chunk at the end
+    (1, 8, 1, 64, 4, 32, 4, 32, 1000, "f16"),
+    (2, 16, 4, 64, 2, 64, 1, 64, 1377, "bf16"),
+    (1, 8, 2, 128, 4, 128, 0, 0, 1000, "f32"),
+    (1, 4, 1, 128, 2, 128, 3, 128, 2999, "f16"),
+    (3, 24, 3, 128, 4, 64, 4, 128, 4100, "bf16"),
+    (1, 32, 4, 128, 2, 32, 4, 32, 548, "bf16"),     # Q % 64 == 32
+    (1, 64, 8, 128, 4, 64, 4, 128, 70000, "bf16"),
 ]
 
 
@@ -143,6 +152,8 @@ STREAM = [
     (1, 8, 2, 128, 8, 64, 3, 64, 100, 140, "f16"),
     (1, 8, 1, 128, 4, 64, 1, 128, 200, 150, "bf16"),
     (1, 4, 4, 128, 2, 32, 5, 32, 40, 130, "f16"),
+    (1, 16, 4, 128, 2, 32, 4, 128, 100, 140, "bf16"),   # matrix-core path, GQA 4
+    (2, 16, 2, 64, 4, 64, 2, 0, 30, 150, "f16"),        # matrix-core path, GQA 8, R 0
 ]
 
 

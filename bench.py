@@ -91,6 +91,9 @@ def main():
                     help="layer caches the steps rotate over (1 = warm, cache-resident)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a reference "
+                         "kernel of known traffic for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
@@ -142,6 +145,14 @@ def main():
         kvq.kvq_decode_attention(cfg, layers[li], n_tok[li], qn[j], out=out, workspace=ws)
         return n_tok[li]
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * 2**20 // 4
+        src_probe = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst_probe = torch.empty_like(src_probe)
+        torch.cuda.synchronize()
+        dst_probe.copy_(src_probe)
+        torch.cuda.synchronize()
+        del src_probe, dst_probe
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

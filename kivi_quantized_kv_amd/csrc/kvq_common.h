@@ -76,6 +76,13 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+// Row rotation with bound_ctrl set: every lane has a source in a rotation,
+// and the form lets the compiler fold the move into the consuming add.
+template <int CTRL>
+__device__ __forceinline__ float dpp_rot(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;

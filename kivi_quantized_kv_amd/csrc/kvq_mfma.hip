@@ -197,8 +197,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const bool is_lo = ((col / GQA) & 1) != 0;         // low part column
   const bool owner = col < GQA;                      // counts l and z once
 
-  __shared__ float s_q[GQA][D];
-  __shared__ float s_qf[GQA][D];   // s_q times the key-side factor 2^(10-a) of channel d
+  __shared__ float s_q[GQA][D + 4];   // rows padded so the heads fall in different banks
   __shared__ float s_o[4][GQA][D];
   __shared__ float s_m[4][GQA], s_l[4][GQA], s_z[4][GQA];
   // wave-private staging of the current chunk's parameters
@@ -207,12 +206,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 
   for (int x = threadIdx.x; x < GQA * D; x += 256) {
     const int qh = x / D, d = x % D;
-    const float qv = load1<DT>(a.q, b * a.q_sb + (h * GQA + qh) * a.q_sh + d) * a.sm_scale_log2;
-    // channel d is code index d % kCPW of its word; its pair index is that
-    // modulo kCPW / 2
-    const int ci = (d % kCPW) % (kCPW / 2);
-    s_q[qh][d] = qv;
-    s_qf[qh][d] = qv * float(1 << (10 - key_mant_bit<BITS>(ci)));
+    s_q[qh][d] = load1<DT>(a.q, b * a.q_sb + (h * GQA + qh) * a.q_sh + d) * a.sm_scale_log2;
   }
   __syncthreads();
 
@@ -312,12 +306,27 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const int64_t g0 = base >> gsh;
       // ---- stage this chunk's parameters in LDS (wave-private)
       {
+        // keys: lanes 0..D/kKP-1 hold delta, the rest zero; stage fd = F*delta
+        // and w = zero - F*delta, F = 2^(10-a) of the channel's code index
+        // (the zero lanes fetch delta from the lane D/kKP below)
         float* kpd = reinterpret_cast<float*>(&s_kp[wave][0][0]);
+        constexpr int kDL = D / kKP;                 // lanes holding delta (32)
+        const bool kdl = lane < kDL;
+        const int kch = (lane % kDL) * kKP;          // first channel of this lane's slice
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-          if (need_group(ch, gi, nv))
+        for (int gi = 0; gi < 2; ++gi) {
+          if (need_group(ch, gi, nv)) {
 #pragma unroll
-            for (int i = 0; i < kKP; ++i) kpd[gi * 2 * D + lane * kKP + i] = r.kp[gi][i];
+            for (int i = 0; i < kKP; ++i) {
+              const int ci = ((kch + i) % kCPW) % (kCPW / 2);
+              const float F = float(1 << (10 - key_mant_bit<BITS>(ci)));
+              const float dl = kdl ? r.kp[gi][i] : 0.f;
+              const float partner_dl = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                                    ((lane - kDL) & 63) << 2, __builtin_bit_cast(int, r.kp[gi][i])));
+              kpd[gi * 2 * D + lane * kKP + i] = kdl ? F * dl : r.kp[gi][i] - F * partner_dl;
+            }
+          }
+        }
         // values: fd = FV * delta (lanes 0..31) and w = zero - FV * delta
         // (lanes 32..63, which fetch delta from the partner lane)
         float* vpd = reinterpret_cast<float*>(&s_vp[wave][0][0]);
@@ -354,22 +363,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
             const int cB = cA + kCPW / 2;
             const float4 qa = *reinterpret_cast<const float4*>(&s_q[hh][cA]);
             const float4 qb = *reinterpret_cast<const float4*>(&s_q[hh][cB]);
-            const float4 fa = *reinterpret_cast<const float4*>(&s_qf[hh][cA]);
-            const float4 fb = *reinterpret_cast<const float4*>(&s_qf[hh][cB]);
-            const float4 da = *reinterpret_cast<const float4*>(kpd + cA);
+            const float4 da = *reinterpret_cast<const float4*>(kpd + cA);       // F * delta
             const float4 db = *reinterpret_cast<const float4*>(kpd + cB);
-            const float4 za = *reinterpret_cast<const float4*>(kpd + D + cA);
+            const float4 za = *reinterpret_cast<const float4*>(kpd + D + cA);   // zero - F * delta
             const float4 zb = *reinterpret_cast<const float4*>(kpd + D + cB);
             const float sqa[4] = {qa.x, qa.y, qa.z, qa.w}, sqb[4] = {qb.x, qb.y, qb.z, qb.w};
-            const float sfa[4] = {fa.x, fa.y, fa.z, fa.w}, sfb[4] = {fb.x, fb.y, fb.z, fb.w};
             const float dla[4] = {da.x, da.y, da.z, da.w}, dlb[4] = {db.x, db.y, db.z, db.w};
             const float zra[4] = {za.x, za.y, za.z, za.w}, zrb[4] = {zb.x, zb.y, zb.z, zb.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float x0 = sfa[r] * dla[r];
-              const float x1 = sfb[r] * dlb[r];
-              kpart = __builtin_fmaf(sqa[r], zra[r], kpart) - x0;
-              kpart = __builtin_fmaf(sqb[r], zrb[r], kpart) - x1;
+              const float x0 = sqa[r] * dla[r];
+              const float x1 = sqb[r] * dlb[r];
+              kpart = __builtin_fmaf(sqa[r], zra[r], kpart);
+              kpart = __builtin_fmaf(sqb[r], zrb[r], kpart);
               // high part in the high columns, x - high in the low columns
               const h2_t hv = __builtin_bit_cast(h2_t, pack_f16(x0, x1));
               const float r0 = __builtin_fmaf((float)hv[0], neg_lo, x0);
@@ -407,8 +413,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float other;
-          if constexpr (GQA == 8) other = dpp_mov<kRowRor8>(sc[t][i]);
-          else other = dpp_mov<kRowRor4>(sc[t][i]);
+          if constexpr (GQA == 8) other = dpp_rot<kRowRor8>(sc[t][i]);
+          else other = dpp_rot<kRowRor4>(sc[t][i]);
           sc[t][i] += other;
         }
       }

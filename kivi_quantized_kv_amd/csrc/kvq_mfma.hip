@@ -6,20 +6,32 @@
 // kernel (pigeon guide "KV-cache quantization", How it works step 5), GQA
 // as in tract PR "KIVI-style KV-cache quantization", What's in the PR.
 //
+// Codes enter the matrix cores as fp16 subnormals: a 32-bit code word
+// masked to a few bits per 16-bit half is, bit for bit, a pair of fp16
+// numbers n * 2^-24 with n the masked field, and the matrix instructions
+// take subnormal inputs exactly.  A field can hold several codes at once:
+// with 4-bit codes a byte field is c0 + 16 c1, and the pair (byte, low
+// nibble) carries (c0, c1) with weights (w1/16, w0 - w1/16); with 2-bit
+// codes the fields are nested masks 0xFF, 0x3F, 0x0F, 0x03 of a byte, with
+// weights (w3/64, w2/16 - w3/64, w1/4 - w2/16, w0 - w1/4).  So four
+// and/perm instructions turn a word into one 8-element operand, and the
+// per-code scale factors 2^-(bits * position) ride on the other operand.
+//
 // Per wave and 64-token chunk:
-//   q.K^T : S^T[16 tokens x 16 cols] = C[16 x D] . Q'[D x 16] per 16-token
-//           tile, v_mfma_f32_16x16x32_f16.  C holds each code as the fp16
-//           value u = 1 + c * 2^(a-10) (code bits placed at mantissa bit a
-//           under a 1.0 exponent: exact, one and-or per two codes); Q'
-//           holds q''_d = 2^(10-a) * scale*log2e * q_d * delta_d split into
-//           an fp16 high part (cols 0..GQA-1) and low part (cols GQA..2GQA-1),
-//           so the product keeps ~22 bits of q''.  The accumulator starts at
-//           kappa = sum_d scale*log2e * q_d * (zero_d - 2^(10-a) delta_d) in
-//           the high columns; hi + lo columns are joined with one DPP rotate.
+//   q.K^T : S^T[16 tokens x 16 cols] = C[16 x D] . W[D x 16] per 16-token
+//           tile, v_mfma_f32_16x16x32_f16.  W holds the field weights of
+//           w_d = scale*log2e * q_d * delta_d split into an fp16 high part
+//           (cols 0..GQA-1) and low part (cols GQA..2GQA-1), ~22 bits in
+//           all; the accumulator starts at kappa * 2^-24 with kappa =
+//           sum_d scale*log2e * q_d * zero_d, and the high and low columns
+//           are joined with one DPP rotate-add.  Scores are acc * 2^24.
 //   P.V   : O[16 rows x 16 ch] += P'[16 x 32 tokens] . Vc[32 x 16 ch],
-//           v_mfma_f32_16x16x32_bf16, rows = heads (bf16 high and low parts
-//           of P''_t = 2^(7-a) p_t delta_t), Vc = codes as bf16 1 + c 2^(a-7).
-//           sum_t p_t (zero_t - 2^(7-a) delta_t) is added per head at the end.
+//           v_mfma_f32_16x16x32_f16, rows = heads (fp16 high and low parts
+//           of the field weights of P''_t = p_t delta_t 2^k), Vc = code
+//           fields.  sum_t p_t zero_t is kept per head on the side.  The
+//           exponent k puts the largest value scale seen so far at
+//           [2^14, 2^15) so P'' stays in fp16's normal range; it only ever
+//           decreases, with an exact power-of-two rescale of O.
 // The value-code layout puts, for each 32-token step, the 8 tokens a lane
 // holds in the S^T accumulator for one channel in one 32-bit unit, so the
 // P' operand comes straight from the q.K^T output registers.
@@ -39,108 +51,81 @@
 namespace kvq {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 // Round-to-nearest-even packing of two floats (v_cvt_pk_f16_f32 /
 // v_cvt_pk_bf16_f32).  Nearest rounding keeps the high/low splits
 // unbiased, so their errors do not accumulate over long token ranges.
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
 }
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
+
+// (a, b) as an fp16 pair for the high columns/rows, (a - high(a), b -
+// high(b)) for the low ones (neg_lo = 0 / -1).
+__device__ __forceinline__ uint32_t split_pack(float a, float b, float neg_lo) {
+  const h2_t hv = __builtin_bit_cast(h2_t, pack_f16(a, b));
+  const float r0 = __builtin_fmaf((float)hv[0], neg_lo, a);
+  const float r1 = __builtin_fmaf((float)hv[1], neg_lo, b);
+  return pack_f16(r0, r1);
 }
 
-// (x & mask) | one.  With the two constants held in registers (see opaque)
-// rather than as literals, which the three-operand encoding cannot take,
-// the compiler selects a single v_and_or_b32.  Written in C, not inline
-// assembly, so the compiler's hazard tracking sees every register write
-// next to in-flight matrix instructions.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t one) {
-  return (x & mask) | one;
-}
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-// Two codes of a 32-bit word at bit offsets POS and POS + 16 as a pair of
-// 16-bit floats whose mantissa holds the code at bit A.
-template <int A, int POS>
-__device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t mask_at_a, uint32_t one) {
-  constexpr int kNet = A - POS;
-  uint32_t x;
-  if constexpr (kNet > 0) x = w << kNet;
-  else if constexpr (kNet < 0) x = w >> (-kNet);
-  else x = w;
-  return and_or(x, mask_at_a, one);
-}
-
-// Where each code sits in the fp16 mantissa on the key side, per code index
-// ci of the low half of a 32-bit word (pairs are (ci, ci + 16/BITS)):
-//   4-bit: all at bit 4 (nibble ci at bit 4ci: shifts <<4, 0, >>4, >>8);
-//   2-bit: crumbs 0..2 at bit 4, crumb 3 at bit 6, crumbs 4..7 at bit 8
-//          (crumbs 2, 3 and 4 need no shift).
-template <int BITS>
-__host__ __device__ constexpr int key_mant_bit(int ci) {
-  return BITS == 4 ? 4 : (ci < 3 ? 4 : (ci == 3 ? 6 : 8));
-}
-// Value side (bf16): 4-bit codes at bit 3, 2-bit codes at bit 5.
-template <int BITS>
-__host__ __device__ constexpr int val_mant_bit() { return BITS == 4 ? 3 : 5; }
-
-template <int BITS>
-__host__ __device__ constexpr uint32_t field_mask(int a) {
-  return (((1u << BITS) - 1u) << a) * 0x00010001u;
-}
-
-// The four fp16 pairs (one MFMA operand) of key-side K-step SP of word w.
-template <int BITS, int SP>
-__device__ __forceinline__ u32x4_t key_operand(uint32_t w, const uint32_t* km, uint32_t one) {
+// The four fp16-subnormal fields of a code word that make one operand.
+// 4-bit: bytes 0|2, nibbles 0|4, bytes 1|3, nibbles 2|6 (low|high half).
+// 2-bit, PART 0 / 1: nested masks of bytes 0|2 / bytes 1|3.
+template <int BITS, int PART>
+__device__ __forceinline__ u32x4_t code_fields(uint32_t w) {
   u32x4_t r;
   if constexpr (BITS == 4) {
-    r[0] = code_pair<4, 0>(w, km[0], one);
-    r[1] = code_pair<4, 4>(w, km[0], one);
-    r[2] = code_pair<4, 8>(w, km[0], one);
-    r[3] = code_pair<4, 12>(w, km[0], one);
-  } else if constexpr (SP == 0) {
-    r[0] = code_pair<4, 0>(w, km[0], one);
-    r[1] = code_pair<4, 2>(w, km[0], one);
-    r[2] = code_pair<4, 4>(w, km[0], one);
-    r[3] = code_pair<6, 6>(w, km[1], one);
+    const uint32_t t = __builtin_amdgcn_perm(w, w, 0x0C030C01u);   // bytes 1, 3 down
+    r[0] = w & 0x00FF00FFu;
+    r[1] = w & 0x000F000Fu;
+    r[2] = t;
+    r[3] = t & 0x000F000Fu;
+  } else if constexpr (PART == 0) {
+    r[0] = w & 0x00FF00FFu;
+    r[1] = w & 0x003F003Fu;
+    r[2] = w & 0x000F000Fu;
+    r[3] = w & 0x00030003u;
   } else {
-    r[0] = code_pair<8, 8>(w, km[2], one);
-    r[1] = code_pair<8, 10>(w, km[2], one);
-    r[2] = code_pair<8, 12>(w, km[2], one);
-    r[3] = code_pair<8, 14>(w, km[2], one);
+    const uint32_t t = __builtin_amdgcn_perm(w, w, 0x0C030C01u);
+    r[0] = t;
+    r[1] = t & 0x003F003Fu;
+    r[2] = t & 0x000F000Fu;
+    r[3] = t & 0x00030003u;
   }
   return r;
 }
 
-// The four bf16 pairs of value-side step S (slots r + 4S, r + 4S + U/2).
-template <int BITS, int S>
-__device__ __forceinline__ u32x4_t value_operand(uint32_t w, uint32_t vm, uint32_t one) {
-  constexpr int A = val_mant_bit<BITS>();
-  u32x4_t r;
-  r[0] = code_pair<A, BITS * (0 + 4 * S)>(w, vm, one);
-  r[1] = code_pair<A, BITS * (1 + 4 * S)>(w, vm, one);
-  r[2] = code_pair<A, BITS * (2 + 4 * S)>(w, vm, one);
-  r[3] = code_pair<A, BITS * (3 + 4 * S)>(w, vm, one);
-  return r;
+// Field weights of four codes at byte positions 0..3 of their run, from
+// per-code factors x_j * f_j, where f_j already carries 2^-(bits * (j mod
+// codes-per-byte)); the order matches code_fields.
+template <int BITS>
+__device__ __forceinline__ void field_weights(const float x[4], const float f[4], float w[4]) {
+  if constexpr (BITS == 4) {
+    w[0] = x[1] * f[1];                          // c0 + 16 c1 : w1 / 16
+    w[1] = __builtin_fmaf(x[0], f[0], -w[0]);    // c0         : w0 - w1 / 16
+    w[2] = x[3] * f[3];
+    w[3] = __builtin_fmaf(x[2], f[2], -w[2]);
+  } else {
+    const float y3 = x[3] * f[3], y2 = x[2] * f[2], y1 = x[1] * f[1];
+    w[0] = y3;                                   // c0 + 4c1 + 16c2 + 64c3
+    w[1] = y2 - y3;                              // c0 + 4c1 + 16c2
+    w[2] = y1 - y2;                              // c0 + 4c1
+    w[3] = __builtin_fmaf(x[0], f[0], -y1);      // c0
+  }
+}
+
+// 2^-(bits * (j mod codes-per-byte)): the field scale of code index j.
+template <int BITS>
+__device__ __forceinline__ float field_scale(int j) {
+  return __builtin_amdgcn_ldexpf(1.0f, -BITS * (j % (8 / BITS)));
 }
 
 // N consecutive 32-bit words from a 4*N-byte aligned address, as wide loads.
@@ -186,8 +171,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int kVB = CR::kVB;
   constexpr int kKP = CR::kKP;
   constexpr int kStepsPerWord = kCPW / 8;  // K-steps covered by one code word
-  constexpr int kVA = val_mant_bit<BITS>();
-  constexpr float FV = float(1 << (7 - kVA));
+  constexpr int kJoin = GQA == 8 ? kRowRor8 : kRowRor4;   // high <-> low column
+  constexpr float kS = 16777216.0f;        // 2^24: unit of a subnormal code field
+  constexpr float kInvS = 1.0f / 16777216.0f;
+  constexpr int kNoScale = 100;            // value exponent before any scale is seen
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = int64_t(b) * a.H + h;
@@ -201,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   __shared__ float s_o[4][GQA][D];
   __shared__ float s_m[4][GQA], s_l[4][GQA], s_z[4][GQA];
   // wave-private staging of the current chunk's parameters
-  __shared__ float4 s_kp[4][2][2 * D / 4];   // [wave][group][delta | zero]
-  __shared__ float4 s_vp[4][2][16];          // [wave][delta | zero][64 tokens]
+  __shared__ float4 s_kp[4][2][2 * D / 4];   // [wave][group][delta * field scale | zero]
+  __shared__ float4 s_vp[4][2][16];          // [wave][delta * field scale * 2^k | zero][64 tokens]
 
   for (int x = threadIdx.x; x < GQA * D; x += 256) {
     const int qh = x / D, d = x % D;
@@ -210,29 +197,34 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   }
   __syncthreads();
 
+  f32x4_t acc[kNB];
+#pragma unroll
+  for (int n = 0; n < kNB; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), l = 0.f, z = 0.f;
+  int kexp = kNoScale;                               // P'' = p * delta * 2^kexp
+  const float neg_lo = is_lo ? -1.0f : 0.0f;
+
   {
     // ------------------------------------------------------------ quantized
-    const uint32_t one16 = opaque(0x3C003C00u), one_bf = opaque(0x3F803F80u);
-    uint32_t km[3];
-    if constexpr (BITS == 4) {
-      km[0] = opaque(field_mask<4>(4));
-      km[1] = km[0];
-      km[2] = km[0];
-    } else {
-      km[0] = opaque(field_mask<2>(4));
-      km[1] = opaque(field_mask<2>(6));
-      km[2] = opaque(field_mask<2>(8));
-    }
-    const uint32_t vmask = opaque(field_mask<BITS>(kVA));
-
-    f32x4_t acc[kNB];
+    constexpr int kDL = D / kKP;                     // lanes holding key deltas
+    // field scales of the key deltas this lane stages (zero points: 1)
+    float kfac[kKP];
 #pragma unroll
-    for (int n = 0; n < kNB; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = -__builtin_inff(), l = 0.f, z = 0.f;
+    for (int i = 0; i < kKP; ++i) kfac[i] = lane < kDL ? field_scale<BITS>(lane * kKP + i) : 1.0f;
+    // field scales of the two value deltas (lanes 0..31) this lane stages
+    const int vtok = (lane & 31) * 2;
+    const float vf0 = lane < 32 ? field_scale<BITS>(vtok) : 1.0f;
+    const float vf1 = lane < 32 ? field_scale<BITS>(vtok + 1) : 1.0f;
+    float vfk0 = vf0, vfk1 = vf1;                    // times 2^kexp in lanes 0..31
+    float vthr = lane < 32 ? __builtin_amdgcn_ldexpf(1.0f, 15 - kNoScale) : __builtin_inff();
+    if (lane < 32) {
+      vfk0 = __builtin_amdgcn_ldexpf(vf0, kNoScale);
+      vfk1 = __builtin_amdgcn_ldexpf(vf1, kNoScale);
+    }
+
     u32x4_t qB[kKS];
     float kap = 0.f;
     int64_t cur_grp = -1;
-    const float neg_lo = is_lo ? -1.0f : 0.0f;
 
     const int64_t nch = (a.Q + 63) >> 6;
     // chunk range of this split (empty for splits that only take exact tokens)
@@ -287,9 +279,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           }
         }
       }
-      const int tok = (lane & 31) * 2;
-      if (tok < nv) {
-        const float2 v = *reinterpret_cast<const float2*>((lane < 32 ? vs_head : vz_head) + base + tok);
+      if (vtok < nv) {
+        const float2 v = *reinterpret_cast<const float2*>((lane < 32 ? vs_head : vz_head) + base + vtok);
         r.vp[0] = v.x;
         r.vp[1] = v.y;
       } else {
@@ -304,41 +295,34 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const int nv = FULL ? 64 : 32;           // a partial chunk holds 32 tokens
       const int ntile = FULL ? 4 : 2;
       const int64_t g0 = base >> gsh;
+      // ---- value scale: a delta at or above 2^(15-kexp) lowers kexp so
+      // that the largest delta seen sits in [2^14, 2^15)
+      if (__builtin_amdgcn_ballot_w64(__builtin_fmaxf(r.vp[0], r.vp[1]) >= vthr) != 0) {
+        const float dmax = wave_max(lane < 32 ? __builtin_fmaxf(r.vp[0], r.vp[1]) : 0.0f);
+        const int knew = 15 - __builtin_amdgcn_frexp_expf(dmax);
+        const float f = __builtin_amdgcn_ldexpf(1.0f, knew - kexp);
+#pragma unroll
+        for (int n = 0; n < kNB; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[n][i] *= f;
+        kexp = knew;
+        if (lane < 32) {
+          vthr = __builtin_amdgcn_ldexpf(1.0f, 15 - kexp);
+          vfk0 = __builtin_amdgcn_ldexpf(vf0, kexp);
+          vfk1 = __builtin_amdgcn_ldexpf(vf1, kexp);
+        }
+      }
       // ---- stage this chunk's parameters in LDS (wave-private)
       {
-        // keys: lanes 0..D/kKP-1 hold delta, the rest zero; stage fd = F*delta
-        // and w = zero - F*delta, F = 2^(10-a) of the channel's code index
-        // (the zero lanes fetch delta from the lane D/kKP below)
         float* kpd = reinterpret_cast<float*>(&s_kp[wave][0][0]);
-        constexpr int kDL = D / kKP;                 // lanes holding delta (32)
-        const bool kdl = lane < kDL;
-        const int kch = (lane % kDL) * kKP;          // first channel of this lane's slice
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          if (need_group(ch, gi, nv)) {
+        for (int gi = 0; gi < 2; ++gi)
+          if (need_group(ch, gi, nv))
 #pragma unroll
-            for (int i = 0; i < kKP; ++i) {
-              const int ci = ((kch + i) % kCPW) % (kCPW / 2);
-              const float F = float(1 << (10 - key_mant_bit<BITS>(ci)));
-              const float dl = kdl ? r.kp[gi][i] : 0.f;
-              const float partner_dl = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                                    ((lane - kDL) & 63) << 2, __builtin_bit_cast(int, r.kp[gi][i])));
-              kpd[gi * 2 * D + lane * kKP + i] = kdl ? F * dl : r.kp[gi][i] - F * partner_dl;
-            }
-          }
-        }
-        // values: fd = FV * delta (lanes 0..31) and w = zero - FV * delta
-        // (lanes 32..63, which fetch delta from the partner lane)
+            for (int i = 0; i < kKP; ++i) kpd[gi * 2 * D + lane * kKP + i] = r.kp[gi][i] * kfac[i];
         float* vpd = reinterpret_cast<float*>(&s_vp[wave][0][0]);
-        const int tok = (lane & 31) * 2;
-        const float o0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                      (lane ^ 32) << 2, __builtin_bit_cast(int, r.vp[0])));
-        const float o1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                      (lane ^ 32) << 2, __builtin_bit_cast(int, r.vp[1])));
-        const float fd0 = FV * (lane < 32 ? r.vp[0] : o0);
-        const float fd1 = FV * (lane < 32 ? r.vp[1] : o1);
-        vpd[(lane >> 5) * 64 + tok] = lane < 32 ? fd0 : r.vp[0] - fd0;
-        vpd[(lane >> 5) * 64 + tok + 1] = lane < 32 ? fd1 : r.vp[1] - fd1;
+        vpd[(lane >> 5) * 64 + vtok] = r.vp[0] * vfk0;
+        vpd[(lane >> 5) * 64 + vtok + 1] = r.vp[1] * vfk1;
       }
       wave_lds_sync();
       // ---- q.K^T: per key-group segment, K-steps outer, tiles inner
@@ -353,38 +337,50 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         if (grp != cur_grp) {
           cur_grp = grp;
           const float* kpd = reinterpret_cast<const float*>(&s_kp[wave][G32 ? seg : 0][0]);
-          float kpart = 0.f;
 #pragma unroll
           for (int kk = 0; kk < kKS; ++kk) {
             const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
-            // the 8 channels of this K-step: code indices r + 4sp and
-            // r + 4sp + kCPW/2 of word wk (r = 0..3), as two runs of 4
+            // the 8 channels of this K-step: runs [cA, cA+4) (low halves of
+            // the fields) and [cB, cB+4) (high halves) of word wk
             const int cA = lg * kQCH + wk * kCPW + 4 * sp;
             const int cB = cA + kCPW / 2;
             const float4 qa = *reinterpret_cast<const float4*>(&s_q[hh][cA]);
             const float4 qb = *reinterpret_cast<const float4*>(&s_q[hh][cB]);
-            const float4 da = *reinterpret_cast<const float4*>(kpd + cA);       // F * delta
+            const float4 da = *reinterpret_cast<const float4*>(kpd + cA);
             const float4 db = *reinterpret_cast<const float4*>(kpd + cB);
-            const float4 za = *reinterpret_cast<const float4*>(kpd + D + cA);   // zero - F * delta
-            const float4 zb = *reinterpret_cast<const float4*>(kpd + D + cB);
-            const float sqa[4] = {qa.x, qa.y, qa.z, qa.w}, sqb[4] = {qb.x, qb.y, qb.z, qb.w};
-            const float dla[4] = {da.x, da.y, da.z, da.w}, dlb[4] = {db.x, db.y, db.z, db.w};
-            const float zra[4] = {za.x, za.y, za.z, za.w}, zrb[4] = {zb.x, zb.y, zb.z, zb.w};
+            const float xa[4] = {qa.x, qa.y, qa.z, qa.w}, xb[4] = {qb.x, qb.y, qb.z, qb.w};
+            const float fa[4] = {da.x, da.y, da.z, da.w}, fb[4] = {db.x, db.y, db.z, db.w};
+            float wa[4], wb[4];
+            field_weights<BITS>(xa, fa, wa);
+            field_weights<BITS>(xb, fb, wb);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float x0 = sqa[r] * dla[r];
-              const float x1 = sqb[r] * dlb[r];
-              kpart = __builtin_fmaf(sqa[r], zra[r], kpart);
-              kpart = __builtin_fmaf(sqb[r], zrb[r], kpart);
-              // high part in the high columns, x - high in the low columns
-              const h2_t hv = __builtin_bit_cast(h2_t, pack_f16(x0, x1));
-              const float r0 = __builtin_fmaf((float)hv[0], neg_lo, x0);
-              const float r1 = __builtin_fmaf((float)hv[1], neg_lo, x1);
-              qB[kk][r] = pack_f16(r0, r1);
-            }
+            for (int r2 = 0; r2 < 4; ++r2) qB[kk][r2] = split_pack(wa[r2], wb[r2], neg_lo);
           }
+          // kappa = sum_d q_d zero_d: high columns take the first half of
+          // the K-steps, low columns the second, joined by the rotate-add
+          float kpart = 0.f;
+#pragma unroll
+          for (int j = 0; j < kKS / 2; ++j) {
+            const int kk = j + (is_lo ? kKS / 2 : 0);
+            const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
+            const int cA = lg * kQCH + wk * kCPW + 4 * sp;
+            const int cB = cA + kCPW / 2;
+            const float4 qa = *reinterpret_cast<const float4*>(&s_q[hh][cA]);
+            const float4 qb = *reinterpret_cast<const float4*>(&s_q[hh][cB]);
+            const float4 za = *reinterpret_cast<const float4*>(kpd + D + cA);
+            const float4 zb = *reinterpret_cast<const float4*>(kpd + D + cB);
+            kpart = __builtin_fmaf(qa.x, za.x, kpart);
+            kpart = __builtin_fmaf(qa.y, za.y, kpart);
+            kpart = __builtin_fmaf(qa.z, za.z, kpart);
+            kpart = __builtin_fmaf(qa.w, za.w, kpart);
+            kpart = __builtin_fmaf(qb.x, zb.x, kpart);
+            kpart = __builtin_fmaf(qb.y, zb.y, kpart);
+            kpart = __builtin_fmaf(qb.z, zb.z, kpart);
+            kpart = __builtin_fmaf(qb.w, zb.w, kpart);
+          }
+          kpart += dpp_rot<kJoin>(kpart);
           kpart += swz_xor16(kpart);
-          kap = kpart + xor32(kpart);
+          kap = (kpart + xor32(kpart)) * kInvS;
         }
         const float init = is_lo ? 0.f : kap;
 #pragma unroll
@@ -397,13 +393,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           for (int t = 0; t < 4; ++t) {
             if (t < t_begin || t >= t_end || (!FULL && t >= 2)) continue;
             u32x4_t av;
-            if (kk % kStepsPerWord == 0) av = key_operand<BITS, 0>(r.kw[t][wk], km, one16);
-            else av = key_operand<BITS, 1>(r.kw[t][wk], km, one16);
+            if (kk % kStepsPerWord == 0) av = code_fields<BITS, 0>(r.kw[t][wk]);
+            else av = code_fields<BITS, 1>(r.kw[t][wk]);
             sc[t] = mfma_f16(av, qB[kk], sc[t]);
           }
         }
       }
-      // join the high and low columns of each head
+      // join the high and low columns of each head (scores * 2^-24)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t >= ntile) {
@@ -411,12 +407,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           continue;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float other;
-          if constexpr (GQA == 8) other = dpp_rot<kRowRor8>(sc[t][i]);
-          else other = dpp_rot<kRowRor4>(sc[t][i]);
-          sc[t][i] += other;
-        }
+        for (int i = 0; i < 4; ++i) sc[t][i] += dpp_rot<kJoin>(sc[t][i]);
       }
       // ---- online softmax (log2 domain); m is per head, uniform over lanes
       float cmax = -__builtin_inff();
@@ -426,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         for (int i = 0; i < 4; ++i) cmax = __builtin_fmaxf(cmax, sc[t][i]);
       cmax = __builtin_fmaxf(cmax, swz_xor16(cmax));
       cmax = __builtin_fmaxf(cmax, xor32(cmax));
-      const float new_m = __builtin_fmaxf(m, cmax);
+      const float new_m = __builtin_fmaxf(m, cmax * kS);
       if (__builtin_amdgcn_ballot_w64(new_m > m) != 0) {
         const float alpha = __builtin_amdgcn_exp2f(m - new_m);
         l *= alpha;
@@ -449,36 +440,35 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         const int t0 = 2 * ps, t1 = 2 * ps + 1;
         const float4 d0v = s_vp[wave][0][4 * t0 + lg];
         const float4 d1v = s_vp[wave][0][4 * t1 + lg];
-        const float4 w0v = s_vp[wave][1][4 * t0 + lg];
-        const float4 w1v = s_vp[wave][1][4 * t1 + lg];
+        const float4 z0v = s_vp[wave][1][4 * t0 + lg];
+        const float4 z1v = s_vp[wave][1][4 * t1 + lg];
         const float d0s[4] = {d0v.x, d0v.y, d0v.z, d0v.w}, d1s[4] = {d1v.x, d1v.y, d1v.z, d1v.w};
-        const float w0s[4] = {w0v.x, w0v.y, w0v.z, w0v.w}, w1s[4] = {w1v.x, w1v.y, w1v.z, w1v.w};
+        const float z0s[4] = {z0v.x, z0v.y, z0v.z, z0v.w}, z1s[4] = {z1v.x, z1v.y, z1v.z, z1v.w};
+        float p0[4], p1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t0][i], kS, -m));
+          p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t1][i], kS, -m));
+          l += p0[i] + p1[i];                 // every lane; owners are kept at the end
+          z = __builtin_fmaf(p0[i], z0s[i], z);
+          z = __builtin_fmaf(p1[i], z1s[i], z);
+        }
+        float w0[4], w1[4];
+        field_weights<BITS>(p0, d0s, w0);
+        field_weights<BITS>(p1, d1s, w1);
         u32x4_t ap;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float p0 = __builtin_amdgcn_exp2f(sc[t0][rr] - m);
-          const float p1 = __builtin_amdgcn_exp2f(sc[t1][rr] - m);
-          l += p0 + p1;                       // every lane; owners are kept at the end
-          z = __builtin_fmaf(p0, w0s[rr], z);
-          z = __builtin_fmaf(p1, w1s[rr], z);
-          const float x0 = p0 * d0s[rr];
-          const float x1 = p1 * d1s[rr];
-          // bf16 high part in the high rows, bf16(x - high) in the low rows
-          const uint32_t hb = pack_bf16(x0, x1);
-          const float y0 = __builtin_fmaf(__builtin_bit_cast(float, hb << 16), neg_lo, x0);
-          const float y1 = __builtin_fmaf(__builtin_bit_cast(float, hb & 0xFFFF0000u), neg_lo, x1);
-          ap[rr] = pack_bf16(y0, y1);
-        }
+        for (int r2 = 0; r2 < 4; ++r2) ap[r2] = split_pack(w0[r2], w1[r2], neg_lo);
 #pragma unroll
         for (int n = 0; n < kNB; ++n) {
           u32x4_t bv;
           if constexpr (kVB == 2) {
-            bv = value_operand<BITS, 0>(r.vw[ps][n], vmask, one_bf);
+            bv = code_fields<BITS, 0>(r.vw[ps][n]);
           } else {
-            if (ps == 0) bv = value_operand<BITS, 0>(r.vw[0][n], vmask, one_bf);
-            else bv = value_operand<BITS, 1>(r.vw[0][n], vmask, one_bf);
+            if (ps == 0) bv = code_fields<BITS, 0>(r.vw[0][n]);
+            else bv = code_fields<BITS, 1>(r.vw[0][n]);
           }
-          acc[n] = mfma_bf16(ap, bv, acc[n]);
+          acc[n] = mfma_f16(ap, bv, acc[n]);
         }
       }
       wave_lds_sync();
@@ -499,72 +489,83 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       if (ch + 2 < wc1) load_chunk(ch + 2, ra);
       run_chunk(ch + 1, rb);
     }
-    // ---- full-precision tokens of this split (sinks and the residual
-    // window), one per wave in turn, folded into the same softmax state and
-    // accumulator rows: scores as fp32 dot products, values added to the
-    // high rows.
-    {
-      const int64_t f0 = int64_t(split) * a.fp_per_split;
-      const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
-      for (int64_t i = f0 + wave; i < f1; i += 4) {
-        const void* kb;
-        const void* vb;
-        int64_t off;
-        if (i < a.n_sink) {
-          kb = a.k_sink; vb = a.v_sink; off = (bh * a.S + i) * D;
-        } else {
-          int64_t slot = a.resid_slot0 + (i - a.n_sink);   // < 2 * ring
-          if (slot >= a.ring) slot -= a.ring;
-          kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + slot) * D;
-        }
-        float part = 0.f;
+  }
+  // ---- full-precision tokens of this split (sinks and the residual
+  // window), one per wave in turn, folded into the same softmax state and
+  // accumulator rows: scores as fp32 dot products, values added to the
+  // high rows in the accumulator's unit 2^(kexp-24).
+  {
+    if (kexp > 24) {
+      const float f = __builtin_amdgcn_ldexpf(1.0f, 24 - kexp);
 #pragma unroll
-        for (int c = 0; c < kQCH; c += 4) {
-          float k4[4];
-          load4<DT>(kb, off + lg * kQCH + c, k4);
-          const float4 q4 = *reinterpret_cast<const float4*>(&s_q[hh][lg * kQCH + c]);
-          part = __builtin_fmaf(k4[0], q4.x, part);
-          part = __builtin_fmaf(k4[1], q4.y, part);
-          part = __builtin_fmaf(k4[2], q4.z, part);
-          part = __builtin_fmaf(k4[3], q4.w, part);
-        }
-        part += swz_xor16(part);
-        const float sc = part + xor32(part);          // score of head hh
-        const float new_m = __builtin_fmaxf(m, sc);
-        if (__builtin_amdgcn_ballot_w64(new_m > m) != 0) {
-          const float alpha = __builtin_amdgcn_exp2f(m - new_m);
-          l *= alpha;
-          z *= alpha;
-          float ar[4];
+      for (int n = 0; n < kNB; ++n)
 #pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2)
-            ar[i2] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                   ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, alpha)));
+        for (int i = 0; i < 4; ++i) acc[n][i] *= f;
+      kexp = 24;
+    }
+    const float fp_unit = __builtin_amdgcn_ldexpf(1.0f, kexp - 24);
+    const int64_t f0 = int64_t(split) * a.fp_per_split;
+    const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
+    for (int64_t i = f0 + wave; i < f1; i += 4) {
+      const void* kb;
+      const void* vb;
+      int64_t off;
+      if (i < a.n_sink) {
+        kb = a.k_sink; vb = a.v_sink; off = (bh * a.S + i) * D;
+      } else {
+        int64_t slot = a.resid_slot0 + (i - a.n_sink);   // < 2 * ring
+        if (slot >= a.ring) slot -= a.ring;
+        kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + slot) * D;
+      }
+      float part = 0.f;
 #pragma unroll
-          for (int n = 0; n < kNB; ++n)
+      for (int c = 0; c < kQCH; c += 4) {
+        float k4[4];
+        load4<DT>(kb, off + lg * kQCH + c, k4);
+        const float4 q4 = *reinterpret_cast<const float4*>(&s_q[hh][lg * kQCH + c]);
+        part = __builtin_fmaf(k4[0], q4.x, part);
+        part = __builtin_fmaf(k4[1], q4.y, part);
+        part = __builtin_fmaf(k4[2], q4.z, part);
+        part = __builtin_fmaf(k4[3], q4.w, part);
+      }
+      part += swz_xor16(part);
+      const float sc = part + xor32(part);          // score of head hh
+      const float new_m = __builtin_fmaxf(m, sc);
+      if (__builtin_amdgcn_ballot_w64(new_m > m) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m - new_m);
+        l *= alpha;
+        z *= alpha;
+        float ar[4];
 #pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] *= ar[i2];
-          m = new_m;
-        }
-        const float p = __builtin_amdgcn_exp2f(sc - m);
-        if (lg == 0) l += p;                          // one lane group per column
-        float pr[4];
+        for (int i2 = 0; i2 < 4; ++i2)
+          ar[i2] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                 ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, alpha)));
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                        ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, p)));
-          pr[i2] = (4 * lg + i2) < GQA ? v : 0.f;     // high rows only
-        }
+        for (int n = 0; n < kNB; ++n)
 #pragma unroll
-        for (int n = 0; n < kNB; ++n) {
-          const float v = load1<DT>(vb, off + 16 * n + col);
+          for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] *= ar[i2];
+        m = new_m;
+      }
+      const float p = __builtin_amdgcn_exp2f(sc - m);
+      if (lg == 0) l += p;                          // one lane group per column
+      float pr[4];
 #pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] = __builtin_fmaf(pr[i2], v, acc[n][i2]);
-        }
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                      ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, p)));
+        pr[i2] = (4 * lg + i2) < GQA ? v * fp_unit : 0.f;   // high rows only
+      }
+#pragma unroll
+      for (int n = 0; n < kNB; ++n) {
+        const float v = load1<DT>(vb, off + 16 * n + col);
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] = __builtin_fmaf(pr[i2], v, acc[n][i2]);
       }
     }
-    // ---- wave result: join high and low rows, reduce l and z over the
-    // lane groups of the owner columns
+  }
+  // ---- wave result: join high and low rows (in real units), reduce l and
+  // z over the lane groups of the owner columns
+  {
     if (!owner) {
       l = 0.f;
       z = 0.f;
@@ -578,6 +579,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       s_l[wave][lane] = l;
       s_z[wave][lane] = z;
     }
+    const float unit = __builtin_amdgcn_ldexpf(1.0f, 24 - kexp);
 #pragma unroll
     for (int n = 0; n < kNB; ++n) {
 #pragma unroll
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         if constexpr (GQA == 8) v += xor32(v);       // rows r and r + 8
         else v += swz_xor16(v);                      // rows r and r + 4
         const int row = 4 * lg + i;
-        if (row < GQA) s_o[wave][row][n * 16 + col] = v;
+        if (row < GQA) s_o[wave][row][n * 16 + col] = v * unit;
       }
     }
   }

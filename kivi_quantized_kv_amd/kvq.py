@@ -53,11 +53,13 @@ class c_tensor(ctypes.Structure):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH):
-    """Load libkvq.so and declare its signatures (no GPU work)."""
+def load_library(path: str | None = None):
+    """Load libkvq.so (or the library at `path`) and declare its signatures
+    (no GPU work).  The first library loaded stays bound."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
     lib = ctypes.CDLL(path)

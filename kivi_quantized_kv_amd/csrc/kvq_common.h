@@ -96,6 +96,51 @@ __device__ __forceinline__ float xor32(float v) {
                                        (int)((threadIdx.x ^ 32u) & 63u) << 2, __builtin_bit_cast(int, v)));
 }
 
+// v combined with its partner lane l ^ 16 / l ^ 32 by a symmetric op, on
+// the VALU: the gfx950 permlane swaps with both operands holding v leave
+// {own, partner} in the two results, in lane-dependent order.  The second
+// operand and both results pass through empty asm statements: the compiler
+// otherwise takes the two results of such a swap to be equal.
+__device__ __forceinline__ float opaque_f(unsigned u) {
+  asm volatile("" : "+v"(u));
+  return __builtin_bit_cast(float, u);
+}
+template <bool X32>
+__device__ __forceinline__ void partner_pair(float v, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  unsigned w = u;
+  asm volatile("" : "+v"(w));
+  if constexpr (X32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, w, false, false);
+    a = opaque_f(r[0]);
+    b = opaque_f(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, w, false, false);
+    a = opaque_f(r[0]);
+    b = opaque_f(r[1]);
+  }
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  float a, b;
+  partner_pair<false>(v, a, b);
+  return __builtin_fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  float a, b;
+  partner_pair<true>(v, a, b);
+  return __builtin_fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  float a, b;
+  partner_pair<false>(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  float a, b;
+  partner_pair<true>(v, a, b);
+  return a + b;
+}
+
 // All-reduce over the 4 lanes of a quad.
 __device__ __forceinline__ float quad_sum(float v) {
   v += dpp_mov<kQuadXor1>(v);

@@ -145,18 +145,41 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* out) {
   }
 }
 
-// Registers of one 64-token chunk in flight.
+// Code registers of one 64-token chunk in flight.
 template <int D, int BITS>
 struct ChunkRegs {
   static constexpr int kQW = (D / 4) * BITS / 32;    // key words per lane per tile
   static constexpr int kNB = D / 16;                 // value words per lane per block
   static constexpr int kVB = 64 / VLayout<BITS>::L;  // value blocks per chunk
-  static constexpr int kKP = 2 * D / 64;             // key-param floats per lane per group
   uint32_t kw[4][kQW];
   uint32_t vw[kVB][kNB];
-  float kp[2][kKP];   // key (delta | zero) of up to two groups, one slice per lane
-  float vp[2];        // value delta (lanes 0..31) or zero (32..63), two tokens
 };
+
+// Asynchronous copy of 4 or 16 bytes per lane from global memory into LDS
+// (lane l's bytes land at lds + l * bytes, lds wave-uniform), counted by
+// vmcnt like a load.  Written as assembly so that the compiler, which
+// would otherwise hold every later LDS read behind the newest copy in
+// flight, leaves the ordering to the explicit waits of the caller; the
+// memory clobber keeps the copy in place relative to the wave's other
+// memory instructions.  M0 carries the LDS address, as the instruction
+// requires.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(const void* src, const void* lds) {
+  static_assert(BYTES == 4 || BYTES == 16, "copy size");
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(l) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(l) : "memory", "m0");
+}
+
+// s_waitcnt for the vector-memory counter only (expcnt and lgkmcnt left
+// at their maxima), N < 16.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 template <int DT, int D, int BITS, int GQA, bool G32>
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
@@ -169,31 +192,116 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int kKS = D / 32;              // K-steps of q.K^T
   constexpr int kNB = CR::kNB;
   constexpr int kVB = CR::kVB;
-  constexpr int kKP = CR::kKP;
+  constexpr int kNG = G32 ? 2 : 1;         // key groups per chunk
   constexpr int kStepsPerWord = kCPW / 8;  // K-steps covered by one code word
   constexpr int kJoin = GQA == 8 ? kRowRor8 : kRowRor4;   // high <-> low column
   constexpr float kS = 16777216.0f;        // 2^24: unit of a subnormal code field
-  constexpr float kInvS = 1.0f / 16777216.0f;
+  constexpr float kSlack = 8.0f;           // running max kept within 2^8 of the true one
   constexpr int kNoScale = 100;            // value exponent before any scale is seen
+  // vector-memory instructions per chunk batch: code loads, then the
+  // parameter copies (key groups: one 16-byte copy per group at D = 128,
+  // two 4-byte copies at D = 64; values: delta and zero, 4 bytes each)
+  constexpr int kCodeLoads = 4 * ((kQW * 4 + 15) / 16) + kVB * ((kNB * 4 + 15) / 16);
+  constexpr int kBatch = kCodeLoads + kNG * (D == 128 ? 1 : 2) + 2;
+  static_assert(kBatch < 16, "batch must fit the vmcnt field");
+  static_assert(D == 64 || D == 128, "head_dim");
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = int64_t(b) * a.H + h;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: kept in a scalar register, it makes the LDS
+  // copy destinations scalar as the copy instructions require
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, lg = lane >> 4;
   const int hh = col % GQA;                          // head of this column
   const bool is_lo = ((col / GQA) & 1) != 0;         // low part column
   const bool owner = col < GQA;                      // counts l and z once
 
-  __shared__ float s_q[GQA][D + 4];   // rows padded so the heads fall in different banks
+  __shared__ float s_q[GQA][D + 4];    // scale*log2e * q; rows padded against bank conflicts
+  __shared__ float s_qf[GQA][D + 4];   // the same times each channel's field scale
   __shared__ float s_o[4][GQA][D];
   __shared__ float s_m[4][GQA], s_l[4][GQA], s_z[4][GQA];
-  // wave-private staging of the current chunk's parameters
-  __shared__ float4 s_kp[4][2][2 * D / 4];   // [wave][group][delta * field scale | zero]
-  __shared__ float4 s_vp[4][2][16];          // [wave][delta * field scale * 2^k | zero][64 tokens]
+  // wave-private parameter buffers of the chunks at even / odd positions
+  // of the wave's run, filled by LDS copies.  Two separate arrays, so that
+  // the compiler, which orders reads of an array after the copies in flight
+  // into it, does not hold the reads of one buffer behind the other's copies.
+  __shared__ float4 s_kp0[4][2][2 * D / 4], s_kp1[4][2][2 * D / 4];   // [wave][group][delta | zero]
+  __shared__ float s_vp0[4][2][64], s_vp1[4][2][64];                  // [wave][delta | zero][token]
 
-  for (int x = threadIdx.x; x < GQA * D; x += 256) {
-    const int qh = x / D, d = x % D;
-    s_q[qh][d] = load1<DT>(a.q, b * a.q_sb + (h * GQA + qh) * a.q_sh + d) * a.sm_scale_log2;
+  // chunk range of this split and wave (empty for splits that only take
+  // exact tokens)
+  const int64_t nch = (a.Q + 63) >> 6;
+  const int64_t c0_raw = int64_t(split) * a.blocks_per_split;
+  const int64_t c0 = c0_raw < nch ? c0_raw : nch;
+  const int64_t c1 = c0 + a.blocks_per_split < nch ? c0 + a.blocks_per_split : nch;
+  const int64_t per_wave = (c1 - c0 + 3) >> 2;
+  const int64_t wc0 = c0 + wave * per_wave;
+  const int64_t wc1 = wc0 + per_wave < c1 ? wc0 + per_wave : c1;
+  const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRB;
+  const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRB;
+  const float* vs_head = a.v_scale + bh * a.qcap;
+  const float* vz_head = a.v_zero + bh * a.qcap;
+  const float* ks_head = a.k_scale + bh * a.kgroups * D;
+  const float* kz_head = a.k_zero + bh * a.kgroups * D;
+  const int gsh = a.g_shift;
+
+  // Issue the batch of chunk ch: its code words into r, then its key and
+  // value parameters into parameter buffer ch & 1.  Every address lies
+  // inside the allocation (qcap >= 64 * ceil(Q / 64) tokens, qcap / G key
+  // groups); whatever lies past the quantized range is skipped or masked
+  // later.  The instruction count is fixed (kBatch), so waiting for
+  // vmcnt <= kBatch completes every batch but the last one issued.
+  auto issue_batch = [&](int64_t ch, CR& r, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
+    auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
+    const int64_t base = ch << 6;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      load_words<kQW>(kc_head + (base + 16 * t + col) * kRB + lg * (kQW * 4), r.kw[t]);
+#pragma unroll
+    for (int vb = 0; vb < kVB; ++vb)
+      load_words<kNB>(vc_head + (base / VLy::L + vb) * (VLy::L * kRB) + (lg * 16 + col) * kNB * 4,
+                      r.vw[vb]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t g0 = base >> gsh;
+#pragma unroll
+    for (int gi = 0; gi < kNG; ++gi) {
+      float* dst = reinterpret_cast<float*>(&kpb[wave][gi][0]);
+      if constexpr (D == 128) {
+        // lanes 0..31: delta[4l..4l+3], lanes 32..63: zero[4(l-32)..]
+        const float* src = (lane < 32 ? ks_head : kz_head) + (g0 + gi) * D + (lane & 31) * 4;
+        copy_to_lds<16>(src, dst);
+      } else {
+        copy_to_lds<4>(ks_head + (g0 + gi) * D + lane, dst);
+        copy_to_lds<4>(kz_head + (g0 + gi) * D + lane, dst + D);
+      }
+    }
+    copy_to_lds<4>(vs_head + base + lane, &vpb[wave][0][0]);
+    copy_to_lds<4>(vz_head + base + lane, &vpb[wave][1][0]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // q first (its loads complete before the chunk batches), then the first
+  // two batches, then q into LDS
+  constexpr int kQPer = GQA * D / 256;
+  float qv[kQPer];
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
+    qv[j] = load1<DT>(a.q, b * a.q_sb + (h * GQA + qh) * a.q_sh + d);
+  }
+  CR ra, rb;
+  if (wc0 < wc1) {
+    issue_batch(wc0, ra, std::integral_constant<int, 0>{});
+    issue_batch(wc0 + 1 < wc1 ? wc0 + 1 : wc0, rb, std::integral_constant<int, 1>{});
+  }
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
+    const float v = qv[j] * a.sm_scale_log2;
+    s_q[qh][d] = v;
+    s_qf[qh][d] = v * field_scale<BITS>(d);
   }
   __syncthreads();
 
@@ -204,139 +312,83 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   int kexp = kNoScale;                               // P'' = p * delta * 2^kexp
   const float neg_lo = is_lo ? -1.0f : 0.0f;
 
+  // Running-max update shared by both token kinds: the max moves only when
+  // a score exceeds it by more than the slack, so p <= 2^8 in between.
+  auto raise_max = [&](float cm) {
+    if (__builtin_amdgcn_ballot_w64(cm > m + kSlack) != 0) {
+      const float new_m = __builtin_fmaxf(m, cm);
+      const float alpha = __builtin_amdgcn_exp2f(m - new_m);
+      l *= alpha;
+      z *= alpha;
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ar[i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                              ((4 * lg + i) % GQA) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+      for (int n = 0; n < kNB; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[n][i] *= ar[i];
+      m = new_m;
+    }
+  };
+
   {
     // ------------------------------------------------------------ quantized
-    constexpr int kDL = D / kKP;                     // lanes holding key deltas
-    // field scales of the key deltas this lane stages (zero points: 1)
-    float kfac[kKP];
+    // value field scales of rows i (token 4g + i of a tile) times 2^kexp
+    float vfk[4];
+    auto set_vfk = [&]() {
 #pragma unroll
-    for (int i = 0; i < kKP; ++i) kfac[i] = lane < kDL ? field_scale<BITS>(lane * kKP + i) : 1.0f;
-    // field scales of the two value deltas (lanes 0..31) this lane stages
-    const int vtok = (lane & 31) * 2;
-    const float vf0 = lane < 32 ? field_scale<BITS>(vtok) : 1.0f;
-    const float vf1 = lane < 32 ? field_scale<BITS>(vtok + 1) : 1.0f;
-    float vfk0 = vf0, vfk1 = vf1;                    // times 2^kexp in lanes 0..31
-    float vthr = lane < 32 ? __builtin_amdgcn_ldexpf(1.0f, 15 - kNoScale) : __builtin_inff();
-    if (lane < 32) {
-      vfk0 = __builtin_amdgcn_ldexpf(vf0, kNoScale);
-      vfk1 = __builtin_amdgcn_ldexpf(vf1, kNoScale);
-    }
+      for (int i = 0; i < 4; ++i) vfk[i] = __builtin_amdgcn_ldexpf(field_scale<BITS>(i), kexp);
+    };
+    set_vfk();
+    const int vtok = (lane & 31) * 2;                // value deltas this lane checks
 
     u32x4_t qB[kKS];
-    float kap = 0.f;
+    float kap[2] = {0.f, 0.f};                       // kappa of each segment's group
     int64_t cur_grp = -1;
 
-    const int64_t nch = (a.Q + 63) >> 6;
-    // chunk range of this split (empty for splits that only take exact tokens)
-    const int64_t c0_raw = int64_t(split) * a.blocks_per_split;
-    const int64_t c0 = c0_raw < nch ? c0_raw : nch;
-    const int64_t c1 = c0 + a.blocks_per_split < nch ? c0 + a.blocks_per_split : nch;
-    const int64_t per_wave = (c1 - c0 + 3) >> 2;
-    const int64_t wc0 = c0 + wave * per_wave;
-    const int64_t wc1 = wc0 + per_wave < c1 ? wc0 + per_wave : c1;
-    const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRB;
-    const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRB;
-    const float* vs_head = a.v_scale + bh * a.qcap;
-    const float* vz_head = a.v_zero + bh * a.qcap;
-    const float* ks_head = a.k_scale + bh * a.kgroups * D;
-    const float* kz_head = a.k_zero + bh * a.kgroups * D;
-    const int gsh = a.g_shift;
-    const int G = a.G;
-
-    // Key groups a chunk needs: G = 32: two (one per half); G >= 64: one,
-    // loaded when the chunk starts a group or is the wave's first chunk.
-    auto need_group = [&](int64_t ch, int gi, int nv) {
-      if constexpr (G32) return gi == 0 || nv > 32;
-      else return gi == 0 && (((ch << 6) & (G - 1)) == 0 || ch == wc0);
-    };
-
-    // issue the loads of chunk ch into r (all addresses inside the cache)
-    auto load_chunk = [&](int64_t ch, CR& r) {
-      const int64_t base = ch << 6;
-      const int nv = int(a.Q - base < 64 ? a.Q - base : 64);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t * 16 < nv)
-          load_words<kQW>(kc_head + (base + 16 * t + col) * kRB + lg * (kQW * 4), r.kw[t]);
-#pragma unroll
-      for (int vb = 0; vb < kVB; ++vb)
-        if (vb * VLy::L < nv)
-          load_words<kNB>(vc_head + (base / VLy::L + vb) * (VLy::L * kRB) + (lg * 16 + col) * kNB * 4,
-                          r.vw[vb]);
-      const int64_t g0 = base >> gsh;
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        if (need_group(ch, gi, nv)) {
-          const int off = lane * kKP;   // slice of [delta (D) | zero (D)]
-          const float* src = off < D ? ks_head + (g0 + gi) * D + off
-                                     : kz_head + (g0 + gi) * D + (off - D);
-          if constexpr (kKP == 4) {
-            const float4 v = *reinterpret_cast<const float4*>(src);
-            r.kp[gi][0] = v.x; r.kp[gi][1] = v.y; r.kp[gi][2] = v.z; r.kp[gi][3] = v.w;
-          } else {
-            const float2 v = *reinterpret_cast<const float2*>(src);
-            r.kp[gi][0] = v.x; r.kp[gi][1] = v.y;
-          }
-        }
-      }
-      if (vtok < nv) {
-        const float2 v = *reinterpret_cast<const float2*>((lane < 32 ? vs_head : vz_head) + base + vtok);
-        r.vp[0] = v.x;
-        r.vp[1] = v.y;
-      } else {
-        r.vp[0] = 0.f;
-        r.vp[1] = 0.f;
-      }
-    };
-
-    auto process_chunk = [&](int64_t ch, CR& r, auto full_tag) {
+    auto process_chunk = [&](int64_t ch, const CR& r, auto full_tag, auto buf_tag) {
       constexpr bool FULL = decltype(full_tag)::value;
+      constexpr int BUF = decltype(buf_tag)::value;
+      const auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
+      const auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
       const int64_t base = ch << 6;
       const int nv = FULL ? 64 : 32;           // a partial chunk holds 32 tokens
       const int ntile = FULL ? 4 : 2;
       const int64_t g0 = base >> gsh;
-      // ---- value scale: a delta at or above 2^(15-kexp) lowers kexp so
-      // that the largest delta seen sits in [2^14, 2^15)
-      if (__builtin_amdgcn_ballot_w64(__builtin_fmaxf(r.vp[0], r.vp[1]) >= vthr) != 0) {
-        const float dmax = wave_max(lane < 32 ? __builtin_fmaxf(r.vp[0], r.vp[1]) : 0.0f);
-        const int knew = 15 - __builtin_amdgcn_frexp_expf(dmax);
-        const float f = __builtin_amdgcn_ldexpf(1.0f, knew - kexp);
+      constexpr int kSegTiles = G32 ? 2 : 4;
+      // this chunk's batch is complete once at most the next one is in flight
+      wait_vmcnt<kBatch>();
+      // ---- value scale: a delta at or above 2^(7-kexp) lowers kexp so
+      // that the largest delta seen sits in [2^6, 2^7); with p <= 2^8 the
+      // value weights stay below 2^15
+      {
+        const float2 dv = *reinterpret_cast<const float2*>(&vpb[wave][0][vtok]);
+        const float vmax = vtok < nv ? __builtin_fmaxf(dv.x, dv.y) : 0.0f;
+        const float vthr = __builtin_amdgcn_ldexpf(1.0f, 7 - kexp);
+        if (__builtin_amdgcn_ballot_w64(vmax >= vthr) != 0) {
+          const int knew = 7 - __builtin_amdgcn_frexp_expf(wave_max(vmax));
+          const float f = __builtin_amdgcn_ldexpf(1.0f, knew - kexp);
 #pragma unroll
-        for (int n = 0; n < kNB; ++n)
+          for (int n = 0; n < kNB; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[n][i] *= f;
-        kexp = knew;
-        if (lane < 32) {
-          vthr = __builtin_amdgcn_ldexpf(1.0f, 15 - kexp);
-          vfk0 = __builtin_amdgcn_ldexpf(vf0, kexp);
-          vfk1 = __builtin_amdgcn_ldexpf(vf1, kexp);
+            for (int i = 0; i < 4; ++i) acc[n][i] *= f;
+          kexp = knew;
+          set_vfk();
         }
       }
-      // ---- stage this chunk's parameters in LDS (wave-private)
-      {
-        float* kpd = reinterpret_cast<float*>(&s_kp[wave][0][0]);
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-          if (need_group(ch, gi, nv))
-#pragma unroll
-            for (int i = 0; i < kKP; ++i) kpd[gi * 2 * D + lane * kKP + i] = r.kp[gi][i] * kfac[i];
-        float* vpd = reinterpret_cast<float*>(&s_vp[wave][0][0]);
-        vpd[(lane >> 5) * 64 + vtok] = r.vp[0] * vfk0;
-        vpd[(lane >> 5) * 64 + vtok + 1] = r.vp[1] * vfk1;
-      }
-      wave_lds_sync();
       // ---- q.K^T: per key-group segment, K-steps outer, tiles inner
       f32x4_t sc[4];
 #pragma unroll
       for (int seg = 0; seg < 2; ++seg) {
-        constexpr int kSegTiles = G32 ? 2 : 4;
         const int t_begin = seg * kSegTiles;
         const int t_end = t_begin + kSegTiles;
         if (t_begin >= ntile) break;
         const int64_t grp = g0 + (G32 ? seg : 0);
         if (grp != cur_grp) {
           cur_grp = grp;
-          const float* kpd = reinterpret_cast<const float*>(&s_kp[wave][G32 ? seg : 0][0]);
+          const float* kpd = reinterpret_cast<const float*>(&kpb[wave][G32 ? seg : 0][0]);
 #pragma unroll
           for (int kk = 0; kk < kKS; ++kk) {
             const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
@@ -344,8 +396,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
             // the fields) and [cB, cB+4) (high halves) of word wk
             const int cA = lg * kQCH + wk * kCPW + 4 * sp;
             const int cB = cA + kCPW / 2;
-            const float4 qa = *reinterpret_cast<const float4*>(&s_q[hh][cA]);
-            const float4 qb = *reinterpret_cast<const float4*>(&s_q[hh][cB]);
+            const float4 qa = *reinterpret_cast<const float4*>(&s_qf[hh][cA]);
+            const float4 qb = *reinterpret_cast<const float4*>(&s_qf[hh][cB]);
             const float4 da = *reinterpret_cast<const float4*>(kpd + cA);
             const float4 db = *reinterpret_cast<const float4*>(kpd + cB);
             const float xa[4] = {qa.x, qa.y, qa.z, qa.w}, xb[4] = {qb.x, qb.y, qb.z, qb.w};
@@ -357,7 +409,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
             for (int r2 = 0; r2 < 4; ++r2) qB[kk][r2] = split_pack(wa[r2], wb[r2], neg_lo);
           }
           // kappa = sum_d q_d zero_d: high columns take the first half of
-          // the K-steps, low columns the second, joined by the rotate-add
+          // the K-steps, low columns the second, joined by the rotate-add;
+          // it is added to the scores after the matrix products
           float kpart = 0.f;
 #pragma unroll
           for (int j = 0; j < kKS / 2; ++j) {
@@ -379,13 +432,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
             kpart = __builtin_fmaf(qb.w, zb.w, kpart);
           }
           kpart += dpp_rot<kJoin>(kpart);
-          kpart += swz_xor16(kpart);
-          kap = (kpart + xor32(kpart)) * kInvS;
+          kpart = sum_xor16(kpart);
+          kap[seg] = sum_xor32(kpart);
+        } else if (seg == 1) {
+          kap[1] = kap[0];
         }
-        const float init = is_lo ? 0.f : kap;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          if (t >= t_begin && t < t_end) sc[t] = f32x4_t{init, init, init, init};
+          if (t >= t_begin && t < t_end) sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < kKS; ++kk) {
           const int wk = kk / kStepsPerWord;
@@ -399,7 +453,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           }
         }
       }
-      // join the high and low columns of each head (scores * 2^-24)
+      // join the high and low columns of each head (scores - kappa, times 2^-24)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t >= ntile) {
@@ -410,45 +464,35 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         for (int i = 0; i < 4; ++i) sc[t][i] += dpp_rot<kJoin>(sc[t][i]);
       }
       // ---- online softmax (log2 domain); m is per head, uniform over lanes
-      float cmax = -__builtin_inff();
+      float cm_seg[2] = {-__builtin_inff(), -__builtin_inff()};
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cmax = __builtin_fmaxf(cmax, sc[t][i]);
-      cmax = __builtin_fmaxf(cmax, swz_xor16(cmax));
-      cmax = __builtin_fmaxf(cmax, xor32(cmax));
-      const float new_m = __builtin_fmaxf(m, cmax * kS);
-      if (__builtin_amdgcn_ballot_w64(new_m > m) != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m - new_m);
-        l *= alpha;
-        z *= alpha;
-        float ar[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ar[i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                ((4 * lg + i) % GQA) << 2, __builtin_bit_cast(int, alpha)));
-#pragma unroll
-        for (int n = 0; n < kNB; ++n)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[n][i] *= ar[i];
-        m = new_m;
-      }
+        for (int i = 0; i < 4; ++i) cm_seg[t / kSegTiles] = __builtin_fmaxf(cm_seg[t / kSegTiles], sc[t][i]);
+      float cm = __builtin_fmaf(cm_seg[0], kS, kap[0]);
+      if constexpr (G32) cm = __builtin_fmaxf(cm, __builtin_fmaf(cm_seg[1], kS, kap[1]));
+      cm = max_xor16(cm);
+      cm = max_xor32(cm);
+      raise_max(cm);
+      const float km0 = kap[0] - m, km1 = kap[1] - m;
       // ---- P.V per 32-token step (tiles 2ps, 2ps+1)
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps) {
         if (ps * 32 >= nv) break;
         const int t0 = 2 * ps, t1 = 2 * ps + 1;
-        const float4 d0v = s_vp[wave][0][4 * t0 + lg];
-        const float4 d1v = s_vp[wave][0][4 * t1 + lg];
-        const float4 z0v = s_vp[wave][1][4 * t0 + lg];
-        const float4 z1v = s_vp[wave][1][4 * t1 + lg];
-        const float d0s[4] = {d0v.x, d0v.y, d0v.z, d0v.w}, d1s[4] = {d1v.x, d1v.y, d1v.z, d1v.w};
+        const float kmp = (t0 / kSegTiles) == 0 ? km0 : km1;
+        const float4 d0v = *reinterpret_cast<const float4*>(&vpb[wave][0][16 * t0 + 4 * lg]);
+        const float4 d1v = *reinterpret_cast<const float4*>(&vpb[wave][0][16 * t1 + 4 * lg]);
+        const float4 z0v = *reinterpret_cast<const float4*>(&vpb[wave][1][16 * t0 + 4 * lg]);
+        const float4 z1v = *reinterpret_cast<const float4*>(&vpb[wave][1][16 * t1 + 4 * lg]);
+        const float d0s[4] = {d0v.x * vfk[0], d0v.y * vfk[1], d0v.z * vfk[2], d0v.w * vfk[3]};
+        const float d1s[4] = {d1v.x * vfk[0], d1v.y * vfk[1], d1v.z * vfk[2], d1v.w * vfk[3]};
         const float z0s[4] = {z0v.x, z0v.y, z0v.z, z0v.w}, z1s[4] = {z1v.x, z1v.y, z1v.z, z1v.w};
         float p0[4], p1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t0][i], kS, -m));
-          p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t1][i], kS, -m));
+          p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t0][i], kS, kmp));
+          p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t1][i], kS, kmp));
           l += p0[i] + p1[i];                 // every lane; owners are kept at the end
           z = __builtin_fmaf(p0[i], z0s[i], z);
           z = __builtin_fmaf(p1[i], z1s[i], z);
@@ -471,24 +515,29 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           acc[n] = mfma_f16(ap, bv, acc[n]);
         }
       }
-      wave_lds_sync();
     };
 
     // only the last chunk of the quantized range can be a half chunk
     const int64_t full_end = (a.Q & 63) ? nch - 1 : nch;
-    auto run_chunk = [&](int64_t ch, CR& r) {
-      if (ch < full_end) process_chunk(ch, r, std::true_type{});
-      else process_chunk(ch, r, std::false_type{});
+    // After a chunk, its registers and parameter buffer are free: start
+    // the batch of the chunk after next (or re-read this one, cached, when
+    // there is none).  The copies into the buffer are ordered after this
+    // wave's reads of it by the wait on the LDS counter.
+    auto run_chunk = [&](int64_t ch, CR& r, int64_t reload, auto buf_tag) {
+      if (ch < full_end) process_chunk(ch, r, std::true_type{}, buf_tag);
+      else process_chunk(ch, r, std::false_type{}, buf_tag);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      issue_batch(reload, r, buf_tag);
     };
-    CR ra, rb;
-    if (wc0 < wc1) load_chunk(wc0, ra);
+    // ra holds chunk ch, rb chunk ch + 1 (both in flight or landed)
     for (int64_t ch = wc0; ch < wc1; ch += 2) {
-      if (ch + 1 < wc1) load_chunk(ch + 1, rb);
-      run_chunk(ch, ra);
-      if (ch + 1 >= wc1) break;
-      if (ch + 2 < wc1) load_chunk(ch + 2, ra);
-      run_chunk(ch + 1, rb);
+      const bool has1 = ch + 1 < wc1, has2 = ch + 2 < wc1, has3 = ch + 3 < wc1;
+      run_chunk(ch, ra, has2 ? ch + 2 : ch, std::integral_constant<int, 0>{});
+      if (!has1) break;
+      run_chunk(ch + 1, rb, has3 ? ch + 3 : ch + 1, std::integral_constant<int, 1>{});
     }
+    // let every copy land before the buffers are left behind
+    wait_vmcnt<0>();
   }
   // ---- full-precision tokens of this split (sinks and the residual
   // window), one per wave in turn, folded into the same softmax state and
@@ -528,24 +577,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         part = __builtin_fmaf(k4[2], q4.z, part);
         part = __builtin_fmaf(k4[3], q4.w, part);
       }
-      part += swz_xor16(part);
-      const float sc = part + xor32(part);          // score of head hh
-      const float new_m = __builtin_fmaxf(m, sc);
-      if (__builtin_amdgcn_ballot_w64(new_m > m) != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m - new_m);
-        l *= alpha;
-        z *= alpha;
-        float ar[4];
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2)
-          ar[i2] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                 ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, alpha)));
-#pragma unroll
-        for (int n = 0; n < kNB; ++n)
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] *= ar[i2];
-        m = new_m;
-      }
+      part = sum_xor16(part);
+      const float sc = sum_xor32(part);             // score of head hh
+      raise_max(sc);
       const float p = __builtin_amdgcn_exp2f(sc - m);
       if (lg == 0) l += p;                          // one lane group per column
       float pr[4];
@@ -570,10 +604,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       l = 0.f;
       z = 0.f;
     }
-    l += swz_xor16(l);
-    l += xor32(l);
-    z += swz_xor16(z);
-    z += xor32(z);
+    l = sum_xor32(sum_xor16(l));
+    z = sum_xor32(sum_xor16(z));
     if (lane < GQA) {
       s_m[wave][lane] = m;
       s_l[wave][lane] = l;
@@ -585,8 +617,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = acc[n][i];
-        if constexpr (GQA == 8) v += xor32(v);       // rows r and r + 8
-        else v += swz_xor16(v);                      // rows r and r + 4
+        if constexpr (GQA == 8) v = sum_xor32(v);    // rows r and r + 8
+        else v = sum_xor16(v);                       // rows r and r + 4
         const int row = 4 * lg + i;
         if (row < GQA) s_o[wave][row][n * 16 + col] = v * unit;
       }

@@ -104,8 +104,9 @@ class Config:
     def row_bytes(self) -> int:
         return self.head_dim * self.bits // 8
 
-    def workspace_bytes(self, n_q_heads: int) -> int:
-        return self.batch * n_q_heads * MAX_SPLITS * (self.head_dim + 2) * 4
+    def workspace_bytes(self, n_q_heads: int, splits: int = MAX_SPLITS) -> int:
+        """Room for `splits` partials per (batch, q head)."""
+        return self.batch * n_q_heads * splits * (self.head_dim + 2) * 4
 
 
 class Cache:

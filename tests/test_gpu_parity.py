@@ -195,13 +195,37 @@ def test_split_count_invariance():
     cache = _run_prefill(kvq, cfg, data, T)
     q = to_dev(data["q"], dt)
     outs = []
-    for nbytes in (cfg.workspace_bytes(Hq), B * Hq * 64 * (D + 2) * 4, B * Hq * 100 * (D + 2) * 4):
-        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for splits in (1024, 64, 100):
+        ws = torch.empty(cfg.workspace_bytes(Hq, splits), dtype=torch.uint8, device="cuda")
         outs.append(kvq.kvq_decode_attention(cfg, cache, T, q, workspace=ws).cpu().numpy())
     for o in outs[1:]:
         assert O.row_rel_error(o, outs[0]) < 1e-5
     ref = O.decode(geo, O.prefill(geo, data["K"], data["V"], T), T, data["q"], Hq)
     assert O.row_rel_error(outs[0], ref) <= ATOL_ROW_REL
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, "random"])
+def test_workspace_needs_no_initialization(fill):
+    """Whatever the workspace holds, a call gives the same result, and so
+    do repeated calls on it."""
+    kvq = _kvq()
+    B, Hq, Hkv, D, bits, G, S, R, T, dt = (2, 16, 2, 128, 4, 64, 4, 128, 3000, "bf16")
+    data = synth.random_case(7, B, Hq, Hkv, D, T, dt)
+    cfg, geo = make(_cfg_kw(B, Hkv, D, bits, G, S, R, T, dt))
+    cache = _run_prefill(kvq, cfg, data, T)
+    q = to_dev(data["q"], dt)
+    n = cfg.workspace_bytes(Hq)
+    if fill == "random":
+        g = torch.Generator(device="cpu").manual_seed(5)
+        ws = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g).cuda()
+    else:
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+    ref = O.decode(geo, O.prefill(geo, data["K"], data["V"], T), T, data["q"], Hq)
+    first = kvq.kvq_decode_attention(cfg, cache, T, q, workspace=ws).cpu().numpy()
+    assert O.row_rel_error(first, ref) <= ATOL_ROW_REL
+    for _ in range(3):
+        again = kvq.kvq_decode_attention(cfg, cache, T, q, workspace=ws).cpu().numpy()
+        assert np.array_equal(again, first)
 
 
 # ----------------------------------------------------------------- workloads

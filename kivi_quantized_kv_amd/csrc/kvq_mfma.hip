@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   CR ra, rb;
   if (wc0 < wc1) {
     issue_batch(wc0, ra, std::integral_constant<int, 0>{});
-    issue_batch(wc0 + 1 < wc1 ? wc0 + 1 : wc0, rb, std::integral_constant<int, 1>{});
+    issue_batch(wc0 + 1 < wc1 ? wc0 + 1 : 0, rb, std::integral_constant<int, 1>{});
   }
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
@@ -520,21 +520,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // only the last chunk of the quantized range can be a half chunk
     const int64_t full_end = (a.Q & 63) ? nch - 1 : nch;
     // After a chunk, its registers and parameter buffer are free: start
-    // the batch of the chunk after next (or re-read this one, cached, when
-    // there is none).  The copies into the buffer are ordered after this
-    // wave's reads of it by the wait on the LDS counter.
-    auto run_chunk = [&](int64_t ch, CR& r, int64_t reload, auto buf_tag) {
+    // the batch of the chunk after next.  Past the wave's range the batch
+    // re-reads chunk 0 of this (b, h), which every wave shares and which
+    // stays in the L2, so that a batch always follows each chunk (the
+    // counter waits assume it).  The copies into the buffer are ordered
+    // after this wave's reads of it by the wait on the LDS counter.
+    auto run_chunk = [&](int64_t ch, CR& r, auto buf_tag) {
       if (ch < full_end) process_chunk(ch, r, std::true_type{}, buf_tag);
       else process_chunk(ch, r, std::false_type{}, buf_tag);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      issue_batch(reload, r, buf_tag);
+      issue_batch(ch + 2 < wc1 ? ch + 2 : 0, r, buf_tag);
     };
     // ra holds chunk ch, rb chunk ch + 1 (both in flight or landed)
     for (int64_t ch = wc0; ch < wc1; ch += 2) {
-      const bool has1 = ch + 1 < wc1, has2 = ch + 2 < wc1, has3 = ch + 3 < wc1;
-      run_chunk(ch, ra, has2 ? ch + 2 : ch, std::integral_constant<int, 0>{});
-      if (!has1) break;
-      run_chunk(ch + 1, rb, has3 ? ch + 3 : ch + 1, std::integral_constant<int, 1>{});
+      run_chunk(ch, ra, std::integral_constant<int, 0>{});
+      if (ch + 1 >= wc1) break;
+      run_chunk(ch + 1, rb, std::integral_constant<int, 1>{});
     }
     // let every copy land before the buffers are left behind
     wait_vmcnt<0>();

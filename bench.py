@@ -25,6 +25,43 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attn tokens/s + effective packed-KV HBM GB/s (% of peak), int4 GQA"
 HBM_PEAK_GBS = 8000.0
+PMC_PROFILE = os.path.join(ROOT, "profiles", "attn_mfma_llama70b_pmc.md")
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the library sources (kernels, host code, header): a traffic
+    figure measured with hardware counters is only reported while the code
+    it was measured on is unchanged."""
+    import hashlib
+    import glob
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kivi_quantized_kv_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")))
+    files.append(os.path.join(ROOT, "include", "kvq.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode call from the committed counter summary, or None
+    when it is missing, for another workload, or stale."""
+    if workload != "llama70b" or not os.path.exists(PMC_PROFILE):
+        return None
+    fields = {}
+    with open(PMC_PROFILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "|", "#")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -194,6 +231,7 @@ def main():
         "layer_caches": n_layers,
         "cache_mib_per_layer": round(layers[0].nbytes() / 2**20, 1),
         "host_wall_s": round(wall, 3),
+        "kernel_sources_sha256": kernel_sources_sha256()[:16],
     }
     result = {
         "metric": METRIC,
@@ -219,12 +257,13 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvq_decode_attention (split-K attention + merge)",
+            "kernel": ("kvq_decode_attention: k_attn_mfma (split-K attention) + k_merge; HIP events "
+                       "on the launch stream bracket both launches"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
         },
         "detail": detail,
     }

@@ -348,14 +348,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     float kap[2] = {0.f, 0.f};                       // kappa of each segment's group
     int64_t cur_grp = -1;
 
-    auto process_chunk = [&](int64_t ch, const CR& r, auto full_tag, auto buf_tag) {
-      constexpr bool FULL = decltype(full_tag)::value;
+    auto process_chunk = [&](int64_t ch, const CR& r, bool half, auto buf_tag) {
       constexpr int BUF = decltype(buf_tag)::value;
       const auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
       const auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
       const int64_t base = ch << 6;
-      const int nv = FULL ? 64 : 32;           // a partial chunk holds 32 tokens
-      const int ntile = FULL ? 4 : 2;
+      const int nv = half ? 32 : 64;           // a half chunk (only ever the last) holds 32 tokens
       const int64_t g0 = base >> gsh;
       constexpr int kSegTiles = G32 ? 2 : 4;
       // this chunk's batch is complete once at most the next one is in flight
@@ -384,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       for (int seg = 0; seg < 2; ++seg) {
         const int t_begin = seg * kSegTiles;
         const int t_end = t_begin + kSegTiles;
-        if (t_begin >= ntile) break;
+        if (t_begin >= 4 || (seg == 1 && half)) break;
         const int64_t grp = g0 + (G32 ? seg : 0);
         if (grp != cur_grp) {
           cur_grp = grp;
@@ -445,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           const int wk = kk / kStepsPerWord;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            if (t < t_begin || t >= t_end || (!FULL && t >= 2)) continue;
+            if (t < t_begin || t >= t_end) continue;
             u32x4_t av;
             if (kk % kStepsPerWord == 0) av = code_fields<BITS, 0>(r.kw[t][wk]);
             else av = code_fields<BITS, 1>(r.kw[t][wk]);
@@ -453,15 +451,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           }
         }
       }
-      // join the high and low columns of each head (scores - kappa, times 2^-24)
+      // join the high and low columns of each head (scores - kappa, times
+      // 2^-24); the second half of a half chunk (codes past the quantized
+      // range, still finite subnormal fields) is masked out
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (t >= ntile) {
-          sc[t] = f32x4_t{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-          continue;
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[t][i] += dpp_rot<kJoin>(sc[t][i]);
+        for (int i = 0; i < 4; ++i) {
+          sc[t][i] += dpp_rot<kJoin>(sc[t][i]);
+          if (t >= 2) sc[t][i] = half ? -__builtin_inff() : sc[t][i];
+        }
       }
       // ---- online softmax (log2 domain); m is per head, uniform over lanes
       float cm_seg[2] = {-__builtin_inff(), -__builtin_inff()};
@@ -526,8 +525,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // counter waits assume it).  The copies into the buffer are ordered
     // after this wave's reads of it by the wait on the LDS counter.
     auto run_chunk = [&](int64_t ch, CR& r, auto buf_tag) {
-      if (ch < full_end) process_chunk(ch, r, std::true_type{}, buf_tag);
-      else process_chunk(ch, r, std::false_type{}, buf_tag);
+      process_chunk(ch, r, ch >= full_end, buf_tag);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       issue_batch(ch + 2 < wc1 ? ch + 2 : 0, r, buf_tag);
     };

@@ -8,71 +8,175 @@
 // quantization", What's in the PR: GQA handled).
 //
 // Dequantization is folded so the inner loops only turn codes into
-// numbers.  A code c becomes the fp16 value u = 1 + c / 2^b by placing its
-// bits at the top of a 1.0 mantissa (exact).  With F = 2^b:
-//   keys   (group delta_d, zero z_d):  q . k_hat = sum_d (F q_d delta_d) u_d
-//                                               + sum_d q_d (z_d - F delta_d)
-//   values (token delta_t, zero z_t):  sum_t p_t v_hat_t
-//                                     = sum_t (F p_t delta_t) u_t
-//                                       + (sum_t p_t (z_t - F delta_t)) * 1
+// numbers.  With key group delta_d, zero z_d and value token delta_t, zero
+// z_t:
+//   q . k_hat       = sum_d (q_d delta_d) c_d + sum_d q_d z_d
+//   sum_t p_t v_hat = sum_t (p_t delta_t) c_t + sum_t p_t z_t
+// where the codes c enter as exact fp16 subnormal bit fields (below).
 // Scores are kept in the log2 domain (scale * log2 e folded into q).
 #include "kvq_kernels.h"
 
 namespace kvq {
 
-// fp16 pair (code r, code r + 16/BITS) of a 32-bit code word, as 1 + c/2^b.
-template <int BITS, int R>
-__device__ __forceinline__ uint32_t code_pair_f16(uint32_t w) {
-  constexpr int kNet = (10 - BITS) - BITS * R;  // shift bringing code R to bit 10-b
-  constexpr uint32_t kMask = (((1u << BITS) - 1u) << (10 - BITS)) * 0x00010001u;
-  uint32_t x;
-  if constexpr (kNet > 0) x = w << kNet;
-  else if constexpr (kNet < 0) x = w >> (-kNet);
-  else x = w;
-  return (x & kMask) | 0x3C003C00u;
-}
-
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float lo_f16(uint32_t p) {
-  return (float)__builtin_bit_cast(half2_t, p)[0];
-}
-__device__ __forceinline__ float hi_f16(uint32_t p) {
-  return (float)__builtin_bit_cast(half2_t, p)[1];
-}
-
-// dot += sum over the codes of one 32-bit word of u(code) * coef[code index]
-template <int BITS, int R = 0>
-__device__ __forceinline__ void word_dot(uint32_t w, const float* coef, float& dot) {
-  if constexpr (R < 16 / BITS) {
-    const uint32_t p = code_pair_f16<BITS, R>(w);
-    dot = __builtin_fmaf(lo_f16(p), coef[R], dot);
-    dot = __builtin_fmaf(hi_f16(p), coef[R + 16 / BITS], dot);
-    word_dot<BITS, R + 1>(w, coef, dot);
+// ---------------------------------------------------------------------------
+// Codes as fp16 subnormals.  A masked bit field of one 16-bit half of a code
+// word, read as fp16, is exactly n * 2^-24 for the field's integer n < 1024;
+// the fp32 FMA that consumes it (v_fma_mix) then multiplies by an fp32
+// coefficient that carries 2^24.  Field sets of one word, each giving a
+// (low half, high half) pair:
+//   8-bit : byte 0|2, byte 1|3                               (code j  -> x_j)
+//   4-bit : byte 0|2, nibble 0|4, byte 1|3, nibble 2|6
+//   2-bit : masks 0xFF, 0x3F, 0x0F, 0x03 of bytes 0|2 (part 0) or 1|3 (part 1)
+// A run of codes sharing a byte is recovered by nested masks, so its field
+// coefficients are differences of the per-code values x_j, where x_j already
+// carries 2^-(bits * (j mod codes per byte)) (run_coefs).
+// ---------------------------------------------------------------------------
+template <int BITS, int PART>
+__device__ __forceinline__ void word_fields(uint32_t w, uint32_t f[4]) {
+  if constexpr (BITS == 8) {
+    f[0] = w & 0x00FF00FFu;
+    f[1] = __builtin_amdgcn_perm(w, w, 0x0C030C01u);   // bytes 1 and 3, zero-extended
+  } else if constexpr (BITS == 4) {
+    const uint32_t t = __builtin_amdgcn_perm(w, w, 0x0C030C01u);
+    f[0] = w & 0x00FF00FFu;
+    f[1] = w & 0x000F000Fu;
+    f[2] = t;
+    f[3] = t & 0x000F000Fu;
+  } else if constexpr (PART == 0) {
+    f[0] = w & 0x00FF00FFu;
+    f[1] = w & 0x003F003Fu;
+    f[2] = w & 0x000F000Fu;
+    f[3] = w & 0x00030003u;
+  } else {
+    const uint32_t t = __builtin_amdgcn_perm(w, w, 0x0C030C01u);
+    f[0] = t;
+    f[1] = t & 0x003F003Fu;
+    f[2] = t & 0x000F000Fu;
+    f[3] = t & 0x00030003u;
   }
 }
 
+// Codes of a word grouped as (part, half, run position): word code index
+// i = pt * kRun + hf * (32 / BITS / 2) + j sits at coefficient slot
+// (pt * 2 + hf) * kRun + j.
+template <int BITS> struct WordShape {
+  static constexpr int kCPW = 32 / BITS;            // codes per word
+  static constexpr int kParts = BITS == 2 ? 2 : 1;  // field sets per half
+  static constexpr int kRun = BITS == 8 ? 2 : 4;    // codes per half of a field set
+};
+
+// Field coefficients of one run from its per-code values x (scaled).
+template <int BITS>
+__device__ __forceinline__ void run_coefs(const float* x, float* c) {
+  if constexpr (BITS == 8) {
+    c[0] = x[0];
+    c[1] = x[1];
+  } else if constexpr (BITS == 4) {
+    c[0] = x[1];
+    c[1] = x[0] - x[1];
+    c[2] = x[3];
+    c[3] = x[2] - x[3];
+  } else {
+    c[0] = x[3];
+    c[1] = x[2] - x[3];
+    c[2] = x[1] - x[2];
+    c[3] = x[0] - x[1];
+  }
+}
+
+// Coefficients of NW words from per-code values x[NW * kCPW] in code order.
+template <int BITS, int NW>
+__device__ __forceinline__ void word_coefs(const float* x, float* c) {
+  using WS = WordShape<BITS>;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+#pragma unroll
+    for (int pt = 0; pt < WS::kParts; ++pt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        run_coefs<BITS>(x + i * WS::kCPW + pt * WS::kRun + hf * (WS::kCPW / 2),
+                        c + i * WS::kCPW + (pt * 2 + hf) * WS::kRun);
+}
+
+// acc += sum over the codes of word w of code * x (through the coefficients
+// c of that word).
+template <int BITS>
+__device__ __forceinline__ void word_dot(uint32_t w, const float* c, float& acc) {
+  using WS = WordShape<BITS>;
+  constexpr int kNF = BITS == 8 ? 2 : 4;
+#pragma unroll
+  for (int pt = 0; pt < WS::kParts; ++pt) {
+    uint32_t f[4];
+    if (pt == 0) word_fields<BITS, 0>(w, f);
+    else word_fields<BITS, 1>(w, f);
+    const float* clo = c + pt * 2 * WS::kRun;
+    const float* chi = clo + WS::kRun;
+#pragma unroll
+    for (int k = 0; k < kNF; ++k) {
+      const half2_t h = __builtin_bit_cast(half2_t, f[k]);
+      acc = __builtin_fmaf((float)h[0], clo[k], acc);
+      acc = __builtin_fmaf((float)h[1], chi[k], acc);
+    }
+  }
+}
+
+// 2^-(bits * (j mod codes per byte)): weight of code j's field position.
+template <int BITS>
+__device__ __forceinline__ float code_field_scale(int j) {
+  return BITS == 8 ? 1.0f : __builtin_amdgcn_ldexpf(1.0f, -BITS * (j % (8 / BITS)));
+}
+
+// Lane N of each row of 16, broadcast to the row.
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xF, 0xF, false));
+}
+// Sum over the wave on the VALU (row DPP, then the two permlane swaps).
+__device__ __forceinline__ float wave_sum_valu(float v) {
+  return sum_xor32(sum_xor16(row_sum(v)));
+}
+
 // ---------------------------------------------------------------------------
-// VALU kernel: one workgroup of 4 waves per (split, q head, batch).
+// VALU kernel: one workgroup of 4 waves per (split, q head, batch).  Each
+// wave walks a run of value-code blocks of L tokens (32 at 4/8 bits, 64 at 2
+// bits) with two register sets: the next block's code words, value
+// parameters and key-group parameters are in flight while a block is
+// processed.
+//
+// q . K: lane (qt, tl) takes channel quarter qt of token tl of a 16-token
+//   sub-tile; the quarter sums meet by quad DPP.  The coefficients of a key
+//   group, x_d = q_d delta_d 2^24 2^-(b (d mod codes per byte)), are formed
+//   once per 32 tokens: each lane scales D/64 channels, the wave trades them
+//   through LDS, and kappa = sum_d q_d z_d is a wave sum.
+// P . V: lane (vg, vj) holds code units of channels vj + 16n for the tokens
+//   of lane group vg; the probabilities of those tokens come from their
+//   score lanes by row broadcasts.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int BITS>
 __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   using VL = VLayout<BITS>;
-  constexpr float F = float(1 << BITS);
+  using WS = WordShape<BITS>;
+  constexpr float kS = 16777216.0f;              // 2^24: unit of a subnormal field
   constexpr int kRowBytes = D * BITS / 8;
-  constexpr int kQuarterCh = D / 4;              // channels per lane in QK
-  constexpr int kQuarterWords = kQuarterCh * BITS / 32;
+  constexpr int kQuarterCh = D / 4;              // channels per lane in q.K
+  constexpr int kQW = kQuarterCh / WS::kCPW;     // key words per lane per sub-tile
   constexpr int kNST = VL::L / 16;               // 16-token sub-tiles per block
+  constexpr int kHalves = VL::L / 32;            // 32-token key-group steps per block
   constexpr int kUnits = D / 16;                 // value units per lane per block
-  constexpr int kUnitWords = VL::UB / 4;
+  constexpr int kUW = VL::UB / 4;                // words per value unit
+  constexpr int kWC = D / 64;                    // channels per lane when scaling a group
 
   const int split = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int h = hq / a.gqa;
   const int64_t bh = int64_t(b) * a.H + h;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   __shared__ float s_q[D];
-  __shared__ float s_p[4][64];
+  __shared__ __attribute__((aligned(16))) float s_x[4][kHalves][D];
   __shared__ float s_out[4][D + 2];
 
   for (int d = threadIdx.x; d < D; d += 256)
@@ -92,103 +196,166 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
     const int64_t wb0 = blk0 + wave * per_wave;
     const int64_t wb1 = wb0 + per_wave < blk1 ? wb0 + per_wave : blk1;
 
-    const int qt = lane & 3;          // QK: channel quarter
-    const int tl = lane >> 2;         // QK: token within the 16-token sub-tile
-    const int vg = lane >> 4;         // PV: lane group g
-    const int vj = lane & 15;         // PV: channel within 16
-    float qpp[kQuarterCh];
-    float kappa = 0.f;
-    int64_t cur_grp = -1;
+    const int qt = lane & 3;          // q.K: channel quarter
+    const int tl = lane >> 2;         // q.K: token within the 16-token sub-tile
+    const int vg = lane >> 4;         // P.V: lane group
+    const int vj = lane & 15;         // P.V: channel within 16
+    // group scaling: this lane's channels lane*kWC + c
+    float sq_w[kWC], xs_w[kWC];
+#pragma unroll
+    for (int c = 0; c < kWC; ++c) {
+      const int ch = lane * kWC + c;
+      sq_w[c] = s_q[ch];
+      xs_w[c] = s_q[ch] * (kS * code_field_scale<BITS>(ch));
+    }
+    // weight of this lane's score token in its value code field
+    const float pfac = kS * code_field_scale<BITS>(tl);
     const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRowBytes;
     const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRowBytes;
+    const float* vs_head = a.v_scale + bh * a.qcap;
+    const float* vz_head = a.v_zero + bh * a.qcap;
+    const float* ks_head = a.k_scale + bh * a.kgroups * D + lane * kWC;
+    const float* kz_head = a.k_zero + bh * a.kgroups * D + lane * kWC;
 
-    for (int64_t blk = wb0; blk < wb1; ++blk) {
-      const int64_t base_u = blk * VL::L;
-      const int nvalid = int(a.Q - base_u < VL::L ? a.Q - base_u : VL::L);
-      float sc[kNST];
+    struct Blk {
+      uint32_t kw[kNST][kQW];
+      uint32_t vw[kUnits][kUW];
+      float dv[kNST], zv[kNST];
+      float ks[kHalves][kWC], kz[kHalves][kWC];
+    };
+    // Every address lies inside the allocation: qcap is a multiple of
+    // max(64, G) tokens, so whole blocks and their key groups are in range;
+    // tokens past the quantized count are masked after the loads.
+    auto load_blk = [&](int64_t blk, Blk& r) {
+      const int64_t base = blk * VL::L;
 #pragma unroll
       for (int st = 0; st < kNST; ++st) {
-        if (st * 16 >= nvalid) { sc[st] = -__builtin_inff(); continue; }
-        const int64_t u = base_u + st * 16 + tl;
-        const int64_t grp = (base_u + st * 16) >> a.g_shift;
-        if (grp != cur_grp) {
-          cur_grp = grp;
-          const float* ks = a.k_scale + (bh * a.kgroups + grp) * D + qt * kQuarterCh;
-          const float* kz = a.k_zero + (bh * a.kgroups + grp) * D + qt * kQuarterCh;
-          float kp = 0.f;
-#pragma unroll
-          for (int c = 0; c < kQuarterCh; ++c) {
-            const float sq = s_q[qt * kQuarterCh + c];
-            const float dl = ks[c];
-            qpp[c] = F * sq * dl;
-            kp = __builtin_fmaf(sq, kz[c] - F * dl, kp);
-          }
-          kappa = quad_sum(kp);
-        }
         const uint32_t* src =
-            reinterpret_cast<const uint32_t*>(kc_head + u * kRowBytes) + qt * kQuarterWords;
-        uint32_t w[kQuarterWords];
+            reinterpret_cast<const uint32_t*>(kc_head + (base + st * 16 + tl) * kRowBytes) + qt * kQW;
 #pragma unroll
-        for (int i = 0; i < kQuarterWords; ++i) w[i] = src[i];
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < kQuarterWords; ++i) word_dot<BITS>(w[i], qpp + i * (32 / BITS), dot);
-        sc[st] = quad_sum(dot) + kappa;
+        for (int i = 0; i < kQW; ++i) r.kw[st][i] = src[i];
       }
-      // online softmax (log2 domain)
-      float lmax = sc[0];
-#pragma unroll
-      for (int st = 1; st < kNST; ++st) lmax = __builtin_fmaxf(lmax, sc[st]);
-      const float bm = wave_max(lmax);
-      const float new_m = __builtin_fmaxf(m, bm);
-      const float alpha = __builtin_amdgcn_exp2f(m - new_m);
-      m = new_m;
-      l *= alpha;
-      z *= alpha;
-#pragma unroll
-      for (int n = 0; n < kUnits; ++n) acc[n] *= alpha;
-#pragma unroll
-      for (int st = 0; st < kNST; ++st) {
-        const int o = st * 16 + tl;
-        if (qt == 0) {
-          float pp = 0.f;
-          if (o < nvalid) {
-            const float p = __builtin_amdgcn_exp2f(sc[st] - m);
-            const int64_t u = base_u + o;
-            const float dv = a.v_scale[bh * a.qcap + u];
-            const float zv = a.v_zero[bh * a.qcap + u];
-            l += p;
-            z = __builtin_fmaf(p, zv - F * dv, z);
-            pp = F * p * dv;
-          }
-          s_p[wave][o] = pp;
-        }
-      }
-      wave_lds_sync();
-      // P . V over the block's value units
-      float pv[VL::U];
-#pragma unroll
-      for (int i = 0; i < VL::U; ++i) pv[i] = s_p[wave][vslot_token<BITS>(vg, i)];
       const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(
           vc_head + blk * (VL::L * kRowBytes) + (vg * 16 + vj) * kUnits * VL::UB);
 #pragma unroll
-      for (int n = 0; n < kUnits; ++n) {
+      for (int n = 0; n < kUnits; ++n)
 #pragma unroll
-        for (int wi = 0; wi < kUnitWords; ++wi) {
-          const uint32_t w = vsrc[n * kUnitWords + wi];
-          word_dot<BITS>(w, pv + wi * (32 / BITS), acc[n]);
+        for (int wi = 0; wi < kUW; ++wi) r.vw[n][wi] = vsrc[n * kUW + wi];
+#pragma unroll
+      for (int st = 0; st < kNST; ++st) {
+        r.dv[st] = vs_head[base + st * 16 + tl];
+        r.zv[st] = vz_head[base + st * 16 + tl];
+      }
+#pragma unroll
+      for (int k = 0; k < kHalves; ++k) {
+        const int64_t grp = (base + 32 * k) >> a.g_shift;
+#pragma unroll
+        for (int c = 0; c < kWC; ++c) {
+          r.ks[k][c] = ks_head[grp * D + c];
+          r.kz[k][c] = kz_head[grp * D + c];
+        }
+      }
+    };
+
+    auto process = [&](int64_t blk, const Blk& r) {
+      const int64_t base = blk * VL::L;
+      const int nvalid = int(a.Q - base < VL::L ? a.Q - base : VL::L);
+      // ---- key-group coefficients of each 32-token half
+      float kap[kHalves];
+#pragma unroll
+      for (int k = 0; k < kHalves; ++k) {
+        float kp = 0.f;
+#pragma unroll
+        for (int c = 0; c < kWC; ++c) {
+          s_x[wave][k][lane * kWC + c] = xs_w[c] * r.ks[k][c];
+          kp = __builtin_fmaf(sq_w[c], r.kz[k][c], kp);
+        }
+        kap[k] = wave_sum_valu(kp);
+      }
+      wave_lds_sync();
+      // ---- scores (log2 domain); lane (qt, tl) ends with token st*16 + tl
+      float sc[kNST];
+#pragma unroll
+      for (int k = 0; k < kHalves; ++k) {
+        float x[kQuarterCh], qc[kQuarterCh];
+#pragma unroll
+        for (int j = 0; j < kQuarterCh; ++j) x[j] = s_x[wave][k][qt * kQuarterCh + j];
+        word_coefs<BITS, kQW>(x, qc);
+#pragma unroll
+        for (int st = 2 * k; st < 2 * k + 2; ++st) {
+          float dot = 0.f;
+#pragma unroll
+          for (int i = 0; i < kQW; ++i) word_dot<BITS>(r.kw[st][i], qc + i * WS::kCPW, dot);
+          sc[st] = st * 16 + tl < nvalid ? quad_sum(dot) + kap[k] : -__builtin_inff();
         }
       }
       wave_lds_sync();
+      // ---- online softmax
+      float lmax = sc[0];
+#pragma unroll
+      for (int st = 1; st < kNST; ++st) lmax = __builtin_fmaxf(lmax, sc[st]);
+      lmax = __builtin_fmaxf(lmax, dpp_mov<kRowRor4>(lmax));
+      lmax = __builtin_fmaxf(lmax, dpp_mov<kRowRor8>(lmax));
+      const float bm = max_xor32(max_xor16(lmax));
+      const float new_m = __builtin_fmaxf(m, bm);
+      if (new_m > m) {   // wave-uniform
+        const float alpha = __builtin_amdgcn_exp2f(m - new_m);
+        l *= alpha;
+        z *= alpha;
+#pragma unroll
+        for (int n = 0; n < kUnits; ++n) acc[n] *= alpha;
+        m = new_m;
+      }
+      // every lane of a quad holds its token's p; l and z gain each token
+      // four times (exactly 4x after the quad-first reduction at the end)
+      float pp[kNST];
+#pragma unroll
+      for (int st = 0; st < kNST; ++st) {
+        const bool ok = st * 16 + tl < nvalid;
+        const float p = __builtin_amdgcn_exp2f(sc[st] - m);   // 0 past the range
+        const float dv = ok ? r.dv[st] : 0.f;
+        const float zv = ok ? r.zv[st] : 0.f;
+        l += p;
+        z = __builtin_fmaf(p, zv, z);
+        pp[st] = p * dv * pfac;
+      }
+      // ---- P . V: code slot i of lane group vg is token vslot_token(vg, i),
+      // whose p sits in lane 4 * (i & 3) of this row, sub-tile o / 16
+      float pv[VL::U], vc[VL::U];
+#pragma unroll
+      for (int i = 0; i < VL::U; ++i) {
+        const int st = vslot_token<BITS>(0, i) / 16;
+        switch (i & 3) {
+          case 0: pv[i] = row_bcast<0>(pp[st]); break;
+          case 1: pv[i] = row_bcast<4>(pp[st]); break;
+          case 2: pv[i] = row_bcast<8>(pp[st]); break;
+          default: pv[i] = row_bcast<12>(pp[st]); break;
+        }
+      }
+      word_coefs<BITS, kUW>(pv, vc);
+#pragma unroll
+      for (int n = 0; n < kUnits; ++n)
+#pragma unroll
+        for (int wi = 0; wi < kUW; ++wi) word_dot<BITS>(r.vw[n][wi], vc + wi * WS::kCPW, acc[n]);
+    };
+
+    if (wb0 < wb1) {
+      Blk ra, rb;
+      load_blk(wb0, ra);
+      for (int64_t blk = wb0;; blk += 2) {
+        load_blk(blk + 1 < wb1 ? blk + 1 : blk, rb);
+        process(blk, ra);
+        if (blk + 1 >= wb1) break;
+        load_blk(blk + 2 < wb1 ? blk + 2 : blk + 1, ra);
+        process(blk + 1, rb);
+        if (blk + 2 >= wb1) break;
+      }
     }
     // combine the four lane groups (each summed a quarter of the tokens)
 #pragma unroll
-    for (int n = 0; n < kUnits; ++n) {
-      acc[n] += swz_xor16(acc[n]);
-      acc[n] += xor32(acc[n]);
-    }
-    l = wave_sum(l);
-    z = wave_sum(z);
+    for (int n = 0; n < kUnits; ++n) acc[n] = sum_xor32(sum_xor16(acc[n]));
+    l = 0.25f * wave_sum_valu(l);
+    z = 0.25f * wave_sum_valu(z);
     if (lane < 16) {
 #pragma unroll
       for (int n = 0; n < kUnits; ++n) s_out[wave][n * 16 + lane] = acc[n] + z;

@@ -13,9 +13,6 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kTargetWorkgroups = 1024;      // VALU kernel: ~4 workgroups of 4 waves per CU
-constexpr int kTargetWorkgroupsMfma = 512;   // matrix-core kernel: ~2 per CU
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Compute units of the current device (cached per device id; a host query,
@@ -72,7 +69,7 @@ kvq_status check_cache(const kvq_config* c, const kvq_cache* k) {
 
 // dispatch over (dtype, head_dim, bits)
 template <template <int, int, int> class Fn, typename... Args>
-hipError_t dispatch3(const kvq_config* c, Args&&... args) {
+auto dispatch3(const kvq_config* c, Args&&... args) -> decltype(Fn<DT_F32, 64, 2>::run(args...)) {
 #define KVQ_CASE_B(DT, D)                                                \
   switch (c->bits) {                                                     \
     case 2: return Fn<DT, D, 2>::run(args...);                           \
@@ -126,6 +123,9 @@ template <int DT, int D, int BITS> struct AttnValuFn {
   static hipError_t run(const AttnArgs& a, int B, hipStream_t s) {
     return launch_attn_valu<DT, D, BITS>(a, B, s);
   }
+};
+template <int DT, int D, int BITS> struct AttnValuOccFn {
+  static int run() { return attn_valu_blocks_per_cu<DT, D, BITS>(); }
 };
 
 // Prefill of one half: fp copies of sinks and residual tokens, then the
@@ -251,15 +251,15 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     // codes.  It works per KV head on 64-token chunks, with the grid sized
     // to one round of two workgroups per CU, and spreads the full-precision
     // tokens evenly over its splits.  Everything else runs the VALU kernel
-    // per query head on value-code blocks, with the full-precision tokens in
-    // splits of their own.
+    // per query head on value-code blocks, again with the full-precision
+    // tokens spread evenly over the splits.
     const int gqa = n_q_heads / H;
     const bool mfma = (gqa == 4 || gqa == 8) && cfg->bits != 8;
     const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
     const int64_t nblk = (Q + L - 1) / L;
     int64_t fp_per_split = 32;
     int64_t bps = 1;
-    int64_t n_split_q = 0, n_split = 0;
+    int64_t n_split = 0;
     if (mfma) {
       const int64_t slots = 2 * int64_t(device_cu_count());
       const int64_t rows = int64_t(B) * H;
@@ -275,19 +275,20 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
       if (n_split < want_fp) n_split = want_fp;
       if (n_split < 1) n_split = 1;
       fp_per_split = (n_fp + n_split - 1) / n_split;
-      n_split_q = n_split;
     } else {
-      int64_t want_q = (kTargetWorkgroups + int64_t(B) * n_q_heads - 1) / (int64_t(B) * n_q_heads);
-      if (want_q > nblk) want_q = nblk;
-      bps = want_q > 0 ? (nblk + want_q - 1) / want_q : 1;
-      auto splits_q = [&]() { return nblk > 0 ? (nblk + bps - 1) / bps : 0; };
-      auto splits_fp = [&]() { return (n_fp + fp_per_split - 1) / fp_per_split; };
-      while (splits_q() + splits_fp() > cap_splits) {
-        if (splits_fp() > 1 && (splits_fp() >= splits_q() || splits_q() <= 1)) fp_per_split *= 2;
-        else bps *= 2;
-      }
-      n_split_q = splits_q();
-      n_split = splits_q() + splits_fp();
+      // one round of resident workgroups, at least one block per wave
+      const int64_t slots = int64_t(dispatch3<AttnValuOccFn>(cfg)) * device_cu_count();
+      const int64_t rows = int64_t(B) * n_q_heads;
+      int64_t want = slots / rows > 0 ? slots / rows : 1;
+      if (want > (nblk + 3) / 4) want = (nblk + 3) / 4;
+      if (want > cap_splits) want = cap_splits;
+      bps = want > 0 ? (nblk + want - 1) / want : 1;
+      n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
+      int64_t want_fp = (n_fp + 63) / 64;
+      if (want_fp > cap_splits) want_fp = cap_splits;
+      if (n_split < want_fp) n_split = want_fp;
+      if (n_split < 1) n_split = 1;
+      fp_per_split = (n_fp + n_split - 1) / n_split;
     }
     AttnArgs a{};
     a.k_codes = cache->k_codes; a.v_codes = cache->v_codes;
@@ -306,7 +307,6 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     a.resid_slot0 = Q % (R + G);
     a.H = H; a.Hq = n_q_heads; a.gqa = n_q_heads / H; a.G = int(G);
     a.g_shift = G == 32 ? 5 : (G == 64 ? 6 : 7);
-    a.n_split_q = int(n_split_q);
     a.n_split = int(n_split);
     a.blocks_per_split = int(bps);
     a.fp_per_split = int(fp_per_split);

@@ -139,13 +139,59 @@ __device__ __forceinline__ float wave_sum_valu(float v) {
   return sum_xor32(sum_xor16(row_sum(v)));
 }
 
+// N consecutive elements at element index i (16-byte aligned) widened to
+// fp32; N is a multiple of 8 (16-bit types) or 4 (fp32).
+template <int DT, int N>
+__device__ __forceinline__ void load_row_run(const void* base, int64_t i, float* out) {
+  if constexpr (DT == DT_F32) {
+    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + i);
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const float4 v = src[k];
+      out[4 * k] = v.x; out[4 * k + 1] = v.y; out[4 * k + 2] = v.z; out[4 * k + 3] = v.w;
+    }
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + i);
+#pragma unroll
+    for (int k = 0; k < N / 8; ++k) {
+      const uint4 v = src[k];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        out[8 * k + 2 * j] = DT == DT_F16 ? f16_bits_to_f32(w[j] & 0xFFFFu) : bf16_bits_to_f32(w[j] & 0xFFFFu);
+        out[8 * k + 2 * j + 1] = DT == DT_F16 ? f16_bits_to_f32(w[j] >> 16) : bf16_bits_to_f32(w[j] >> 16);
+      }
+    }
+  }
+}
+// N = 1 or 2 consecutive elements at element index i (aligned to N elements).
+template <int DT, int N>
+__device__ __forceinline__ void load_small(const void* base, int64_t i, float* out) {
+  if constexpr (N == 1) {
+    out[0] = load1<DT>(base, i);
+  } else if constexpr (DT == DT_F32) {
+    const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(base) + i);
+    out[0] = v.x; out[1] = v.y;
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(base) + i);
+    out[0] = DT == DT_F16 ? f16_bits_to_f32(w & 0xFFFFu) : bf16_bits_to_f32(w & 0xFFFFu);
+    out[1] = DT == DT_F16 ? f16_bits_to_f32(w >> 16) : bf16_bits_to_f32(w >> 16);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// VALU kernel: one workgroup of 4 waves per (split, q head, batch).  Each
-// wave walks a run of value-code blocks of L tokens (32 at 4/8 bits, 64 at 2
-// bits) with two register sets: the next block's code words, value
-// parameters and key-group parameters are in flight while a block is
-// processed.
+// VALU kernel: one workgroup of 4 waves per (split, q head, batch).  A split
+// owns a run of value-code blocks of L tokens (32 at 4/8 bits, 64 at 2
+// bits) and a run of the full-precision tokens; its four waves share both
+// evenly and fold them into one softmax state each.
 //
+// Full-precision tokens go first, in tiles of 16: lane (qt, tl) scores
+// token tl over channel quarter qt, and lane l then adds channels
+// l * D/64 .. of each value row.
+//
+// Quantized blocks: each wave keeps two register sets, so the next block's
+// code words, value parameters and key-group parameters are in flight while
+// a block is processed.
 // q . K: lane (qt, tl) takes channel quarter qt of token tl of a 16-token
 //   sub-tile; the quarter sums meet by quad DPP.  The coefficients of a key
 //   group, x_d = q_d delta_d 2^24 2^-(b (d mod codes per byte)), are formed
@@ -155,8 +201,13 @@ __device__ __forceinline__ float wave_sum_valu(float v) {
 //   of lane group vg; the probabilities of those tokens come from their
 //   score lanes by row broadcasts.
 // ---------------------------------------------------------------------------
+// Waves per SIMD the register budget is held to: four (128 VGPRs) where the
+// kernel fits without spilling, else three.
 template <int DT, int D, int BITS>
-__global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
+constexpr int valu_waves_per_simd() { return (D == 64 || (BITS == 4 && DT == DT_F16)) ? 4 : 3; }
+
+template <int DT, int D, int BITS>
+__global__ __launch_bounds__(256, (valu_waves_per_simd<DT, D, BITS>())) void k_attn_valu(AttnArgs a) {
   using VL = VLayout<BITS>;
   using WS = WordShape<BITS>;
   constexpr float kS = 16777216.0f;              // 2^24: unit of a subnormal field
@@ -167,15 +218,19 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   constexpr int kHalves = VL::L / 32;            // 32-token key-group steps per block
   constexpr int kUnits = D / 16;                 // value units per lane per block
   constexpr int kUW = VL::UB / 4;                // words per value unit
-  constexpr int kWC = D / 64;                    // channels per lane when scaling a group
+  constexpr int kWC = D / 64;                    // channels per lane when scaling a group / adding a row
 
   const int split = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int h = hq / a.gqa;
   const int64_t bh = int64_t(b) * a.H + h;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qt = lane & 3;          // q.K: channel quarter
+  const int tl = lane >> 2;         // q.K: token within a 16-token tile
+  const int vg = lane >> 4;         // P.V: lane group
+  const int vj = lane & 15;         // P.V: channel within 16
 
-  __shared__ float s_q[D];
+  __shared__ __attribute__((aligned(16))) float s_q[D];
   __shared__ __attribute__((aligned(16))) float s_x[4][kHalves][D];
   __shared__ float s_out[4][D + 2];
 
@@ -184,229 +239,270 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   __syncthreads();
 
   float m = -__builtin_inff(), l = 0.f, z = 0.f;
-
-  if (split < a.n_split_q) {
-    float acc[kUnits];
+  float acc[kUnits], accf[kWC];
 #pragma unroll
-    for (int n = 0; n < kUnits; ++n) acc[n] = 0.f;
-    const int64_t nblk = (a.Q + VL::L - 1) / VL::L;
-    const int64_t blk0 = int64_t(split) * a.blocks_per_split;
-    const int64_t blk1 = blk0 + a.blocks_per_split < nblk ? blk0 + a.blocks_per_split : nblk;
-    const int64_t per_wave = (blk1 - blk0 + 3) / 4;
-    const int64_t wb0 = blk0 + wave * per_wave;
-    const int64_t wb1 = wb0 + per_wave < blk1 ? wb0 + per_wave : blk1;
-
-    const int qt = lane & 3;          // q.K: channel quarter
-    const int tl = lane >> 2;         // q.K: token within the 16-token sub-tile
-    const int vg = lane >> 4;         // P.V: lane group
-    const int vj = lane & 15;         // P.V: channel within 16
-    // group scaling: this lane's channels lane*kWC + c
-    float sq_w[kWC], xs_w[kWC];
+  for (int n = 0; n < kUnits; ++n) acc[n] = 0.f;
 #pragma unroll
-    for (int c = 0; c < kWC; ++c) {
-      const int ch = lane * kWC + c;
-      sq_w[c] = s_q[ch];
-      xs_w[c] = s_q[ch] * (kS * code_field_scale<BITS>(ch));
-    }
-    // weight of this lane's score token in its value code field
-    const float pfac = kS * code_field_scale<BITS>(tl);
-    const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRowBytes;
-    const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRowBytes;
-    const float* vs_head = a.v_scale + bh * a.qcap;
-    const float* vz_head = a.v_zero + bh * a.qcap;
-    const float* ks_head = a.k_scale + bh * a.kgroups * D + lane * kWC;
-    const float* kz_head = a.k_zero + bh * a.kgroups * D + lane * kWC;
-
-    struct Blk {
-      uint32_t kw[kNST][kQW];
-      uint32_t vw[kUnits][kUW];
-      float dv[kNST], zv[kNST];
-      float ks[kHalves][kWC], kz[kHalves][kWC];
-    };
-    // Every address lies inside the allocation: qcap is a multiple of
-    // max(64, G) tokens, so whole blocks and their key groups are in range;
-    // tokens past the quantized count are masked after the loads.
-    auto load_blk = [&](int64_t blk, Blk& r) {
-      const int64_t base = blk * VL::L;
-#pragma unroll
-      for (int st = 0; st < kNST; ++st) {
-        const uint32_t* src =
-            reinterpret_cast<const uint32_t*>(kc_head + (base + st * 16 + tl) * kRowBytes) + qt * kQW;
-#pragma unroll
-        for (int i = 0; i < kQW; ++i) r.kw[st][i] = src[i];
-      }
-      const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(
-          vc_head + blk * (VL::L * kRowBytes) + (vg * 16 + vj) * kUnits * VL::UB);
-#pragma unroll
-      for (int n = 0; n < kUnits; ++n)
-#pragma unroll
-        for (int wi = 0; wi < kUW; ++wi) r.vw[n][wi] = vsrc[n * kUW + wi];
-#pragma unroll
-      for (int st = 0; st < kNST; ++st) {
-        r.dv[st] = vs_head[base + st * 16 + tl];
-        r.zv[st] = vz_head[base + st * 16 + tl];
-      }
-#pragma unroll
-      for (int k = 0; k < kHalves; ++k) {
-        const int64_t grp = (base + 32 * k) >> a.g_shift;
-#pragma unroll
-        for (int c = 0; c < kWC; ++c) {
-          r.ks[k][c] = ks_head[grp * D + c];
-          r.kz[k][c] = kz_head[grp * D + c];
-        }
-      }
-    };
-
-    auto process = [&](int64_t blk, const Blk& r) {
-      const int64_t base = blk * VL::L;
-      const int nvalid = int(a.Q - base < VL::L ? a.Q - base : VL::L);
-      // ---- key-group coefficients of each 32-token half
-      float kap[kHalves];
-#pragma unroll
-      for (int k = 0; k < kHalves; ++k) {
-        float kp = 0.f;
-#pragma unroll
-        for (int c = 0; c < kWC; ++c) {
-          s_x[wave][k][lane * kWC + c] = xs_w[c] * r.ks[k][c];
-          kp = __builtin_fmaf(sq_w[c], r.kz[k][c], kp);
-        }
-        kap[k] = wave_sum_valu(kp);
-      }
-      wave_lds_sync();
-      // ---- scores (log2 domain); lane (qt, tl) ends with token st*16 + tl
-      float sc[kNST];
-#pragma unroll
-      for (int k = 0; k < kHalves; ++k) {
-        float x[kQuarterCh], qc[kQuarterCh];
-#pragma unroll
-        for (int j = 0; j < kQuarterCh; ++j) x[j] = s_x[wave][k][qt * kQuarterCh + j];
-        word_coefs<BITS, kQW>(x, qc);
-#pragma unroll
-        for (int st = 2 * k; st < 2 * k + 2; ++st) {
-          float dot = 0.f;
-#pragma unroll
-          for (int i = 0; i < kQW; ++i) word_dot<BITS>(r.kw[st][i], qc + i * WS::kCPW, dot);
-          sc[st] = st * 16 + tl < nvalid ? quad_sum(dot) + kap[k] : -__builtin_inff();
-        }
-      }
-      wave_lds_sync();
-      // ---- online softmax
-      float lmax = sc[0];
-#pragma unroll
-      for (int st = 1; st < kNST; ++st) lmax = __builtin_fmaxf(lmax, sc[st]);
-      lmax = __builtin_fmaxf(lmax, dpp_mov<kRowRor4>(lmax));
-      lmax = __builtin_fmaxf(lmax, dpp_mov<kRowRor8>(lmax));
-      const float bm = max_xor32(max_xor16(lmax));
-      const float new_m = __builtin_fmaxf(m, bm);
-      if (new_m > m) {   // wave-uniform
-        const float alpha = __builtin_amdgcn_exp2f(m - new_m);
-        l *= alpha;
-        z *= alpha;
-#pragma unroll
-        for (int n = 0; n < kUnits; ++n) acc[n] *= alpha;
-        m = new_m;
-      }
-      // every lane of a quad holds its token's p; l and z gain each token
-      // four times (exactly 4x after the quad-first reduction at the end)
-      float pp[kNST];
-#pragma unroll
-      for (int st = 0; st < kNST; ++st) {
-        const bool ok = st * 16 + tl < nvalid;
-        const float p = __builtin_amdgcn_exp2f(sc[st] - m);   // 0 past the range
-        const float dv = ok ? r.dv[st] : 0.f;
-        const float zv = ok ? r.zv[st] : 0.f;
-        l += p;
-        z = __builtin_fmaf(p, zv, z);
-        pp[st] = p * dv * pfac;
-      }
-      // ---- P . V: code slot i of lane group vg is token vslot_token(vg, i),
-      // whose p sits in lane 4 * (i & 3) of this row, sub-tile o / 16
-      float pv[VL::U], vc[VL::U];
-#pragma unroll
-      for (int i = 0; i < VL::U; ++i) {
-        const int st = vslot_token<BITS>(0, i) / 16;
-        switch (i & 3) {
-          case 0: pv[i] = row_bcast<0>(pp[st]); break;
-          case 1: pv[i] = row_bcast<4>(pp[st]); break;
-          case 2: pv[i] = row_bcast<8>(pp[st]); break;
-          default: pv[i] = row_bcast<12>(pp[st]); break;
-        }
-      }
-      word_coefs<BITS, kUW>(pv, vc);
-#pragma unroll
-      for (int n = 0; n < kUnits; ++n)
-#pragma unroll
-        for (int wi = 0; wi < kUW; ++wi) word_dot<BITS>(r.vw[n][wi], vc + wi * WS::kCPW, acc[n]);
-    };
-
-    if (wb0 < wb1) {
-      Blk ra, rb;
-      load_blk(wb0, ra);
-      for (int64_t blk = wb0;; blk += 2) {
-        load_blk(blk + 1 < wb1 ? blk + 1 : blk, rb);
-        process(blk, ra);
-        if (blk + 1 >= wb1) break;
-        load_blk(blk + 2 < wb1 ? blk + 2 : blk + 1, ra);
-        process(blk + 1, rb);
-        if (blk + 2 >= wb1) break;
-      }
-    }
-    // combine the four lane groups (each summed a quarter of the tokens)
-#pragma unroll
-    for (int n = 0; n < kUnits; ++n) acc[n] = sum_xor32(sum_xor16(acc[n]));
-    l = 0.25f * wave_sum_valu(l);
-    z = 0.25f * wave_sum_valu(z);
-    if (lane < 16) {
-#pragma unroll
-      for (int n = 0; n < kUnits; ++n) s_out[wave][n * 16 + lane] = acc[n] + z;
-    }
-  } else {
-    // full-precision tokens: sinks, then the residual ring
-    constexpr int kC = D / 64;
-    float acc[kC];
-#pragma unroll
-    for (int k = 0; k < kC; ++k) acc[k] = 0.f;
-    const int64_t f0 = int64_t(split - a.n_split_q) * a.fp_per_split;
-    const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
-    for (int64_t i = f0 + wave; i < f1; i += 4) {
-      const void* kb;
-      const void* vb;
-      int64_t off;
-      if (i < a.n_sink) {
-        kb = a.k_sink; vb = a.v_sink; off = (bh * a.S + i) * D;
-      } else {
-        int64_t slot = a.resid_slot0 + (i - a.n_sink);   // < 2 * ring
-        if (slot >= a.ring) slot -= a.ring;
-        kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + slot) * D;
-      }
-      float dot = 0.f;
-#pragma unroll
-      for (int k = 0; k < kC; ++k) dot = __builtin_fmaf(load1<DT>(kb, off + lane + 64 * k), s_q[lane + 64 * k], dot);
-      const float s = wave_sum(dot);
-      const float new_m = __builtin_fmaxf(m, s);
+  for (int c = 0; c < kWC; ++c) accf[c] = 0.f;
+  // l and z gain each token once per lane of its quad (four times); the
+  // quad-first wave sums at the end divide that out exactly.
+  auto raise_max = [&](float bm) {
+    const float new_m = __builtin_fmaxf(m, bm);
+    if (new_m > m) {   // wave-uniform
       const float alpha = __builtin_amdgcn_exp2f(m - new_m);
-      const float p = __builtin_amdgcn_exp2f(s - new_m);
-      m = new_m;
-      l = l * alpha + p;
+      l *= alpha;
+      z *= alpha;
 #pragma unroll
-      for (int k = 0; k < kC; ++k) acc[k] = __builtin_fmaf(p, load1<DT>(vb, off + lane + 64 * k), acc[k] * alpha);
+      for (int n = 0; n < kUnits; ++n) acc[n] *= alpha;
+#pragma unroll
+      for (int c = 0; c < kWC; ++c) accf[c] *= alpha;
+      m = new_m;
+    }
+  };
+  auto tile_max = [&](float v) {   // over the 16 tokens of the tile(s)
+    v = __builtin_fmaxf(v, dpp_mov<kRowRor4>(v));
+    v = __builtin_fmaxf(v, dpp_mov<kRowRor8>(v));
+    return max_xor32(max_xor16(v));
+  };
+
+  const int64_t nblk = (a.Q + VL::L - 1) / VL::L;
+  const int64_t blk0 = int64_t(split) * a.blocks_per_split;
+  const int64_t blk1 = blk0 + a.blocks_per_split < nblk ? blk0 + a.blocks_per_split : nblk;
+  const int64_t per_wave = blk1 > blk0 ? (blk1 - blk0 + 3) / 4 : 0;
+  const int64_t wb0 = blk0 + wave * per_wave;
+  const int64_t wb1 = wb0 + per_wave < blk1 ? wb0 + per_wave : blk1;
+
+  // group scaling: this lane's channels lane*kWC + c
+  float sq_w[kWC], xs_w[kWC];
+#pragma unroll
+  for (int c = 0; c < kWC; ++c) {
+    const int ch = lane * kWC + c;
+    sq_w[c] = s_q[ch];
+    xs_w[c] = s_q[ch] * (kS * code_field_scale<BITS>(ch));
+  }
+  // weight of this lane's score token in its value code field
+  const float pfac = kS * code_field_scale<BITS>(tl);
+  // Uniform bases and 32-bit lane offsets (loads take the scalar-base form).
+  const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRowBytes;
+  const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRowBytes;
+  const float* vs_head = a.v_scale + bh * a.qcap;
+  const float* vz_head = a.v_zero + bh * a.qcap;
+  const float* ks_head = a.k_scale + bh * a.kgroups * D;
+  const float* kz_head = a.k_zero + bh * a.kgroups * D;
+  const uint32_t k_off = uint32_t(tl * kRowBytes + qt * kQW * 4);
+  const uint32_t v_off = uint32_t((vg * 16 + vj) * kUnits * VL::UB);
+  const uint32_t c_off = uint32_t(lane * kWC);
+
+  struct Blk {
+    uint32_t kw[kNST][kQW];
+    uint32_t vw[kUnits][kUW];
+    float dv[kNST], zv[kNST];
+    float ks[kHalves][kWC], kz[kHalves][kWC];
+  };
+  // Every address lies inside the allocation: qcap is a multiple of
+  // max(64, G) tokens, so whole blocks and their key groups are in range;
+  // tokens past the quantized count are masked after the loads.
+  auto load_blk = [&](int64_t blk, Blk& r) {
+    const int64_t base = blk * VL::L;
+    const uint8_t* kb = kc_head + base * kRowBytes;
+#pragma unroll
+    for (int st = 0; st < kNST; ++st) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(kb + k_off + st * 16 * kRowBytes);
+#pragma unroll
+      for (int i = 0; i < kQW; ++i) r.kw[st][i] = src[i];
+    }
+    const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(vc_head + base * kRowBytes + v_off);
+#pragma unroll
+    for (int n = 0; n < kUnits; ++n)
+#pragma unroll
+      for (int wi = 0; wi < kUW; ++wi) r.vw[n][wi] = vsrc[n * kUW + wi];
+    const float* vs = vs_head + base;
+    const float* vz = vz_head + base;
+#pragma unroll
+    for (int st = 0; st < kNST; ++st) {
+      r.dv[st] = vs[uint32_t(tl + st * 16)];
+      r.zv[st] = vz[uint32_t(tl + st * 16)];
     }
 #pragma unroll
-    for (int k = 0; k < kC; ++k) s_out[wave][lane + 64 * k] = acc[k];
+    for (int k = 0; k < kHalves; ++k) {
+      const int64_t grp = (base + 32 * k) >> a.g_shift;
+      const float* ks = ks_head + grp * D;
+      const float* kz = kz_head + grp * D;
+#pragma unroll
+      for (int c = 0; c < kWC; ++c) {
+        r.ks[k][c] = ks[c_off + c];
+        r.kz[k][c] = kz[c_off + c];
+      }
+    }
+  };
+
+  Blk ra, rb;
+  if (wb0 < wb1) load_blk(wb0, ra);
+
+  // ---- full-precision tokens of this split (sinks, then the residual ring)
+  {
+    const int64_t f0 = int64_t(split) * a.fp_per_split;
+    const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
+    const int64_t fpw = f1 > f0 ? (f1 - f0 + 3) / 4 : 0;
+    const int64_t fw0 = f0 + wave * fpw;
+    const int64_t fw1 = fw0 + fpw < f1 ? fw0 + fpw : f1;
+    // element offset of exact token i's row and the store holding it
+    auto fp_row = [&](int64_t i, bool& sink) {
+      sink = i < a.n_sink;
+      int64_t slot = a.resid_slot0 + (i - a.n_sink);   // < 2 * ring
+      slot -= slot >= a.ring ? a.ring : 0;
+      return (sink ? bh * a.S + i : bh * a.ring + slot) * D;
+    };
+    if (fw0 < fw1) {
+      for (int64_t t0 = fw0; t0 < fw1; t0 += 16) {
+        // scores: token t0 + tl (addresses clamped into the run)
+        bool sk;
+        const int64_t ik = t0 + tl < fw1 ? t0 + tl : fw1 - 1;
+        const int64_t ko = fp_row(ik, sk);
+        float kr[kQuarterCh];
+        load_row_run<DT, kQuarterCh>(sk ? a.k_sink : a.k_resid, ko + qt * kQuarterCh, kr);
+        float dot = 0.f;
+#pragma unroll
+        for (int j = 0; j < kQuarterCh; ++j) dot = __builtin_fmaf(kr[j], s_q[qt * kQuarterCh + j], dot);
+        // value rows of the tile's tokens, channels lane*kWC ..
+        float vr[16][kWC];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          bool sv;
+          const int64_t iv = t0 + t < fw1 ? t0 + t : fw1 - 1;
+          const int64_t vo = fp_row(iv, sv);
+          load_small<DT, kWC>(sv ? a.v_sink : a.v_resid, vo + lane * kWC, vr[t]);
+        }
+        const float sc = quad_sum(dot) + (t0 + tl < fw1 ? 0.f : -__builtin_inff());
+        raise_max(tile_max(sc));
+        const float p = __builtin_amdgcn_exp2f(sc - m);   // 0 past the run
+        l += p;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const float pt = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), 4 * t));
+#pragma unroll
+          for (int c = 0; c < kWC; ++c) accf[c] = __builtin_fmaf(pt, vr[t][c], accf[c]);
+        }
+      }
+    }
   }
+
+  // ---- quantized blocks
+  auto process = [&](int64_t blk, const Blk& r) {
+    const int64_t base = blk * VL::L;
+    const int nvalid = int(a.Q - base < VL::L ? a.Q - base : VL::L);
+    // key-group coefficients of each 32-token half
+    float kap[kHalves];
+#pragma unroll
+    for (int k = 0; k < kHalves; ++k) {
+      float kp = 0.f;
+#pragma unroll
+      for (int c = 0; c < kWC; ++c) {
+        s_x[wave][k][lane * kWC + c] = xs_w[c] * r.ks[k][c];
+        kp = __builtin_fmaf(sq_w[c], r.kz[k][c], kp);
+      }
+      kap[k] = wave_sum_valu(kp);
+    }
+    wave_lds_sync();
+    // scores (log2 domain); lane (qt, tl) ends with token st*16 + tl
+    float sc[kNST];
+#pragma unroll
+    for (int k = 0; k < kHalves; ++k) {
+      float dot[2] = {0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kQW; ++i) {   // one word's coefficients at a time
+        float x[WS::kCPW], qc[WS::kCPW];
+#pragma unroll
+        for (int j = 0; j < WS::kCPW; ++j) x[j] = s_x[wave][k][qt * kQuarterCh + i * WS::kCPW + j];
+        word_coefs<BITS, 1>(x, qc);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) word_dot<BITS>(r.kw[2 * k + u][i], qc, dot[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // -inf past the quantized count, added rather than selected so the
+        // dot products stay unconditional
+        const int st = 2 * k + u;
+        const float mask = st * 16 + tl < nvalid ? 0.f : -__builtin_inff();
+        sc[st] = quad_sum(dot[u]) + (kap[k] + mask);
+      }
+    }
+    wave_lds_sync();
+    float lmax = sc[0];
+#pragma unroll
+    for (int st = 1; st < kNST; ++st) lmax = __builtin_fmaxf(lmax, sc[st]);
+    raise_max(tile_max(lmax));
+    float pp[kNST];
+#pragma unroll
+    for (int st = 0; st < kNST; ++st) {
+      const bool ok = st * 16 + tl < nvalid;
+      const float p = __builtin_amdgcn_exp2f(sc[st] - m);   // 0 past the range
+      const float dv = ok ? r.dv[st] : 0.f;
+      const float zv = ok ? r.zv[st] : 0.f;
+      l += p;
+      z = __builtin_fmaf(p, zv, z);
+      pp[st] = p * dv * pfac;
+    }
+    // P . V: code slot i of lane group vg is token vslot_token(vg, i), whose
+    // p sits in lane 4 * (i & 3) of this row, sub-tile o / 16
+    float pv[VL::U], vc[VL::U];
+#pragma unroll
+    for (int i = 0; i < VL::U; ++i) {
+      const int st = vslot_token<BITS>(0, i) / 16;
+      switch (i & 3) {
+        case 0: pv[i] = row_bcast<0>(pp[st]); break;
+        case 1: pv[i] = row_bcast<4>(pp[st]); break;
+        case 2: pv[i] = row_bcast<8>(pp[st]); break;
+        default: pv[i] = row_bcast<12>(pp[st]); break;
+      }
+    }
+    word_coefs<BITS, kUW>(pv, vc);
+#pragma unroll
+    for (int n = 0; n < kUnits; ++n)
+#pragma unroll
+      for (int wi = 0; wi < kUW; ++wi) word_dot<BITS>(r.vw[n][wi], vc + wi * WS::kCPW, acc[n]);
+  };
+
+  if (wb0 < wb1) {
+    for (int64_t blk = wb0;; blk += 2) {
+      load_blk(blk + 1 < wb1 ? blk + 1 : blk, rb);
+      process(blk, ra);
+      if (blk + 1 >= wb1) break;
+      load_blk(blk + 2 < wb1 ? blk + 2 : blk + 1, ra);
+      process(blk + 1, rb);
+      if (blk + 2 >= wb1) break;
+    }
+  }
+
+  // ---- wave result: the four lane groups of the quantized part each hold
+  // a quarter of the tokens; exact-token sums are per channel already
+#pragma unroll
+  for (int n = 0; n < kUnits; ++n) acc[n] = sum_xor32(sum_xor16(acc[n]));
+  l = 0.25f * wave_sum_valu(l);
+  z = 0.25f * wave_sum_valu(z);
+  if (lane < 16) {
+#pragma unroll
+    for (int n = 0; n < kUnits; ++n) s_out[wave][n * 16 + lane] = acc[n] + z;
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int c = 0; c < kWC; ++c) s_out[wave][lane * kWC + c] += accf[c];
   if (lane == 0) {
     s_out[wave][D] = m;
     s_out[wave][D + 1] = l;
   }
   __syncthreads();
-  // merge the four waves and write this split's partial
+  // merge the four waves and write this split's partial; a wave with no
+  // tokens left m = -inf, l = 0 and a zero row
   float* dst = a.ws + ((int64_t(b) * a.Hq + hq) * a.n_split + split) * (D + 2);
   float M = s_out[0][D];
 #pragma unroll
   for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, s_out[w][D]);
+  const float Mref = M == -__builtin_inff() ? 0.f : M;
   float f[4];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) f[w] = __builtin_amdgcn_exp2f(s_out[w][D] - M);
+  for (int w = 0; w < 4; ++w) f[w] = __builtin_amdgcn_exp2f(s_out[w][D] - Mref);
   for (int d = threadIdx.x; d < D; d += 256) {
     float o = 0.f;
 #pragma unroll
@@ -425,50 +521,82 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the split partials: one workgroup per (q head, batch).
 // M = max_j m_j, L = sum_j 2^(m_j - M) l_j, out = sum_j 2^(m_j - M) o_j / L.
-// All partial loads are independent: splits spread over the threads for M
-// and the weights, then (channel, split-subset) pairs for the outputs.
+// Thread (sub, d) folds channel d of splits sub, sub + kSub, ... into its
+// own running (max, sums), loading up to kCh splits in one round; the kSub
+// subsets then meet through LDS.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_merge(AttnArgs a) {
-  constexpr int kSub = 256 / D;             // token / split subsets per channel
-  __shared__ float s_w[KVQ_MAX_SPLITS_DEV];
-  __shared__ float s_red[8];
-  __shared__ float s_part[kSub][D];
+  constexpr int kSub = 256 / D;             // split subsets per channel
+  constexpr int kCh = 32;                   // splits per thread per load round
+  __shared__ float s_m[kSub], s_o[kSub][D], s_l[kSub];
   const int hq = blockIdx.x, b = blockIdx.y;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int d = t % D, sub = t / D;
-
-  // ---- split partials
+  const int t = threadIdx.x, d = t % D, sub = t / D;
   const int ns = a.n_split;
   const float* src = a.ws + (int64_t(b) * a.Hq + hq) * ns * (D + 2);
-  float mx = -__builtin_inff();
-  for (int j = t; j < ns; j += 256) mx = __builtin_fmaxf(mx, src[j * (D + 2) + D]);
-  mx = wave_max(mx);
-  if (lane == 0) s_red[wave] = mx;
-  __syncthreads();
-  const float M = __builtin_fmaxf(__builtin_fmaxf(s_red[0], s_red[1]),
-                                  __builtin_fmaxf(s_red[2], s_red[3]));
-  float lsum = 0.f;
-  for (int j = t; j < ns; j += 256) {
-    const float e = __builtin_amdgcn_exp2f(src[j * (D + 2) + D] - M);
-    s_w[j] = e;
-    lsum = __builtin_fmaf(e, src[j * (D + 2) + D + 1], lsum);
+  float M = -__builtin_inff(), o = 0.f, L = 0.f;
+  for (int j0 = sub; j0 < ns; j0 += kSub * kCh) {
+    float mj[kCh], oj[kCh], lj[kCh];
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      const int j = j0 + kSub * i;
+      const int jj = j < ns ? j : ns - 1;   // in bounds; weight 0 below
+      const float* pj = src + int64_t(jj) * (D + 2);
+      mj[i] = j < ns ? pj[D] : -__builtin_inff();
+      oj[i] = pj[d];
+      lj[i] = pj[D + 1];
+    }
+    float cm = mj[0];
+#pragma unroll
+    for (int i = 1; i < kCh; ++i) cm = __builtin_fmaxf(cm, mj[i]);
+    if (cm > M) {
+      const float f = __builtin_amdgcn_exp2f(M - cm);   // 0 while M = -inf
+      o *= f;
+      L *= f;
+      M = cm;
+    }
+    const float Mref = M == -__builtin_inff() ? 0.f : M;
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      const float w = __builtin_amdgcn_exp2f(mj[i] - Mref);   // 0 for empty splits
+      o = __builtin_fmaf(w, oj[i], o);
+      L = __builtin_fmaf(w, lj[i], L);
+    }
   }
-  lsum = wave_sum(lsum);
-  __syncthreads();
-  if (lane == 0) s_red[4 + wave] = lsum;
-  float o = 0.f;
-#pragma unroll 8
-  for (int j = sub; j < ns; j += kSub) o = __builtin_fmaf(s_w[j], src[j * (D + 2) + d], o);
-  s_part[sub][d] = o;
+  s_o[sub][d] = o;
+  if (d == 0) {
+    s_m[sub] = M;
+    s_l[sub] = L;
+  }
   __syncthreads();
   if (t < D) {
-    const float L = s_red[4] + s_red[5] + s_red[6] + s_red[7];
-    float acc = 0.f;
+    float Mt = s_m[0];
 #pragma unroll
-    for (int k = 0; k < kSub; ++k) acc += s_part[k][t];
-    a.out[(int64_t(b) * a.Hq + hq) * D + t] = acc / L;
+    for (int k = 1; k < kSub; ++k) Mt = __builtin_fmaxf(Mt, s_m[k]);
+    const float Mref = Mt == -__builtin_inff() ? 0.f : Mt;
+    float acc = 0.f, Lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+      const float f = __builtin_amdgcn_exp2f(s_m[k] - Mref);
+      acc = __builtin_fmaf(f, s_o[k][t], acc);
+      Lt = __builtin_fmaf(f, s_l[k], Lt);
+    }
+    a.out[(int64_t(b) * a.Hq + hq) * D + t] = acc / Lt;
   }
+}
+
+// Workgroups of the VALU kernel resident per CU (its register use decides),
+// asked of the runtime once per instantiation.
+template <int DT, int D, int BITS>
+int attn_valu_blocks_per_cu() {
+  static const int n = [] {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_valu<DT, D, BITS>, 256, 0) != hipSuccess ||
+        v < 1)
+      v = 1;
+    return v;
+  }();
+  return n;
 }
 
 template <int DT, int D, int BITS>
@@ -485,7 +613,10 @@ hipError_t launch_merge(const AttnArgs& a, int B, hipStream_t s) {
 #define KVQ_INST_VALU(DT, D)                                                        \
   template hipError_t launch_attn_valu<DT, D, 2>(const AttnArgs&, int, hipStream_t); \
   template hipError_t launch_attn_valu<DT, D, 4>(const AttnArgs&, int, hipStream_t); \
-  template hipError_t launch_attn_valu<DT, D, 8>(const AttnArgs&, int, hipStream_t);
+  template hipError_t launch_attn_valu<DT, D, 8>(const AttnArgs&, int, hipStream_t); \
+  template int attn_valu_blocks_per_cu<DT, D, 2>();                                  \
+  template int attn_valu_blocks_per_cu<DT, D, 4>();                                  \
+  template int attn_valu_blocks_per_cu<DT, D, 8>();
 KVQ_INST_VALU(DT_F32, 64)
 KVQ_INST_VALU(DT_F32, 128)
 KVQ_INST_VALU(DT_F16, 64)

@@ -9,7 +9,6 @@ namespace kvq {
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 constexpr int kWave = 64;
-#define KVQ_MAX_SPLITS_DEV 1024   // equals KVQ_MAX_SPLITS of the C header
 
 // ---------------------------------------------------------------- dtypes
 template <int DT> struct Elem;

@@ -57,7 +57,7 @@ struct AttnArgs {
   int64_t kgroups;          // qcap / G
   int64_t resid_slot0;      // ring slot of the first residual token, Q mod ring
   int H, Hq, gqa, G, g_shift;
-  int n_split, n_split_q;   // total splits; the first n_split_q cover the quantized range
+  int n_split;              // splits per (batch, q head)
   int blocks_per_split;     // value-code blocks per quantized split
   int fp_per_split;         // full-precision tokens per split that takes them
 };
@@ -72,6 +72,8 @@ template <int DT, int D, int BITS>
 hipError_t launch_append(const AppendArgs& a, int B, int H, hipStream_t s);
 template <int DT, int D, int BITS>
 hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s);
+template <int DT, int D, int BITS>
+int attn_valu_blocks_per_cu();
 template <int DT, int D, int BITS, int GQA>
 hipError_t launch_attn_mfma(const AttnArgs& a, int B, hipStream_t s);
 template <int DT, int D>

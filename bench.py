@@ -64,6 +64,12 @@ def measured_traffic(workload: str):
         return None
 
 
+def attn_kernel_name(w) -> str:
+    """The split-K kernel the library picks: matrix cores for GQA groups of
+    4 and 8 with 2/4-bit codes, the VALU kernel otherwise."""
+    return "k_attn_mfma" if w.gqa in (4, 8) and w.bits != 8 else "k_attn_valu"
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -121,8 +127,9 @@ def cpu_baseline(w, data, sample_seconds: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="untimed steps first (the clocks settle within a few hundred)")
     ap.add_argument("--workload", default="llama70b")
     ap.add_argument("--layers", type=int, default=4,
                     help="layer caches the steps rotate over (1 = warm, cache-resident)")
@@ -247,7 +254,7 @@ def main():
         "dtype": "int%d-codes/fp32-accumulate" % w.bits,
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: long-context layer B{w.batch} Hq{w.n_q_heads} Hkv{w.n_kv_heads} "
+            "workload": f"{w.name}: layer B{w.batch} Hq{w.n_q_heads} Hkv{w.n_kv_heads} "
                         f"D{w.head_dim} T{w.n_tokens}+decode {w.dtype} inputs int{w.bits} "
                         f"G{w.group} R{w.residual} S{w.sink}",
             "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
@@ -257,8 +264,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("kvq_decode_attention: k_attn_mfma (split-K attention) + k_merge; HIP events "
-                       "on the launch stream bracket both launches"),
+            "kernel": (f"kvq_decode_attention: {attn_kernel_name(w)} (split-K attention) + k_merge; "
+                       "HIP events on the launch stream bracket both launches"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -301,7 +301,9 @@ __global__ __launch_bounds__(256, (valu_waves_per_simd<DT, D, BITS>())) void k_a
   };
   // Every address lies inside the allocation: qcap is a multiple of
   // max(64, G) tokens, so whole blocks and their key groups are in range;
-  // tokens past the quantized count are masked after the loads.
+  // tokens past the quantized count are masked after the loads.  Code words
+  // are read once per call: non-temporal loads keep them out of the way of
+  // the parameters in the caches.
   auto load_blk = [&](int64_t blk, Blk& r) {
     const int64_t base = blk * VL::L;
     const uint8_t* kb = kc_head + base * kRowBytes;
@@ -309,13 +311,13 @@ __global__ __launch_bounds__(256, (valu_waves_per_simd<DT, D, BITS>())) void k_a
     for (int st = 0; st < kNST; ++st) {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(kb + k_off + st * 16 * kRowBytes);
 #pragma unroll
-      for (int i = 0; i < kQW; ++i) r.kw[st][i] = src[i];
+      for (int i = 0; i < kQW; ++i) r.kw[st][i] = __builtin_nontemporal_load(src + i);
     }
     const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(vc_head + base * kRowBytes + v_off);
 #pragma unroll
     for (int n = 0; n < kUnits; ++n)
 #pragma unroll
-      for (int wi = 0; wi < kUW; ++wi) r.vw[n][wi] = vsrc[n * kUW + wi];
+      for (int wi = 0; wi < kUW; ++wi) r.vw[n][wi] = __builtin_nontemporal_load(vsrc + n * kUW + wi);
     const float* vs = vs_head + base;
     const float* vz = vz_head + base;
 #pragma unroll

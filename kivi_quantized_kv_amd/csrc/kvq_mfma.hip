@@ -36,10 +36,13 @@
 // holds in the S^T accumulator for one channel in one 32-bit unit, so the
 // P' operand comes straight from the q.K^T output registers.
 //
-// Memory pipeline: a wave walks a contiguous run of chunks; while it
-// computes chunk c the codes of chunk c+1 are already in flight into
-// registers, and so are its key/value parameters, which are staged through
-// wave-private LDS (broadcast reads) when the chunk comes up.
+// Memory pipeline: the waves of one (batch, KV head) take its chunks in
+// turn (wave w of W gets chunks w, w + W, ...), so at any moment they
+// stream one contiguous stretch of the cache; while a wave computes one
+// of its chunks the codes of its next one are already in flight into
+// registers (non-temporal loads: read once, not kept in the caches), and so
+// are its key/value parameters, which are staged through wave-private LDS
+// (broadcast reads) when the chunk comes up.
 //
 // MFMA operand layout (16x16x32, 64 lanes): lane l holds A[row l%16][k in
 // group l/16] and B[k in group l/16][col l%16] (8 values each, the same
@@ -128,13 +131,14 @@ __device__ __forceinline__ float field_scale(int j) {
   return __builtin_amdgcn_ldexpf(1.0f, -BITS * (j % (8 / BITS)));
 }
 
-// N consecutive 32-bit words from a 4*N-byte aligned address, as wide loads.
+// N consecutive 32-bit words from a 4*N-byte aligned address, as wide
+// loads (non-temporal for the 16-byte ones).
 template <int N>
 __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* out) {
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < N; i += 4) {
-      const u32x4_t v = reinterpret_cast<const u32x4_t*>(p)[i / 4];
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + i / 4);
       out[i] = v[0]; out[i + 1] = v[1]; out[i + 2] = v[2]; out[i + 3] = v[3];
     }
   } else if constexpr (N == 2) {
@@ -227,15 +231,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   __shared__ float4 s_kp0[4][2][2 * D / 4], s_kp1[4][2][2 * D / 4];   // [wave][group][delta | zero]
   __shared__ float s_vp0[4][2][64], s_vp1[4][2][64];                  // [wave][delta | zero][token]
 
-  // chunk range of this split and wave (empty for splits that only take
-  // exact tokens)
+  // this wave's chunks: gw, gw + nw_row, ... (none for waves past the
+  // chunk count, whose splits only take exact tokens)
   const int64_t nch = (a.Q + 63) >> 6;
-  const int64_t c0_raw = int64_t(split) * a.blocks_per_split;
-  const int64_t c0 = c0_raw < nch ? c0_raw : nch;
-  const int64_t c1 = c0 + a.blocks_per_split < nch ? c0 + a.blocks_per_split : nch;
-  const int64_t per_wave = (c1 - c0 + 3) >> 2;
-  const int64_t wc0 = c0 + wave * per_wave;
-  const int64_t wc1 = wc0 + per_wave < c1 ? wc0 + per_wave : c1;
+  const int64_t nw_row = int64_t(a.n_split) * 4;
+  const int64_t gw = int64_t(split) * 4 + wave;
+  const int64_t wn = gw < nch ? (nch - gw + nw_row - 1) / nw_row : 0;
   const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRB;
   const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRB;
   const float* vs_head = a.v_scale + bh * a.qcap;
@@ -292,9 +293,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     qv[j] = load1<DT>(a.q, b * a.q_sb + (h * GQA + qh) * a.q_sh + d);
   }
   CR ra, rb;
-  if (wc0 < wc1) {
-    issue_batch(wc0, ra, std::integral_constant<int, 0>{});
-    issue_batch(wc0 + 1 < wc1 ? wc0 + 1 : 0, rb, std::integral_constant<int, 1>{});
+  if (wn > 0) {
+    issue_batch(gw, ra, std::integral_constant<int, 0>{});
+    issue_batch(wn > 1 ? gw + nw_row : 0, rb, std::integral_constant<int, 1>{});
   }
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
@@ -519,21 +520,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // only the last chunk of the quantized range can be a half chunk
     const int64_t full_end = (a.Q & 63) ? nch - 1 : nch;
     // After a chunk, its registers and parameter buffer are free: start
-    // the batch of the chunk after next.  Past the wave's range the batch
-    // re-reads chunk 0 of this (b, h), which every wave shares and which
-    // stays in the L2, so that a batch always follows each chunk (the
-    // counter waits assume it).  The copies into the buffer are ordered
-    // after this wave's reads of it by the wait on the LDS counter.
-    auto run_chunk = [&](int64_t ch, CR& r, auto buf_tag) {
+    // the batch of the wave's chunk after next.  Past the wave's last chunk
+    // the batch re-reads chunk 0 of this (b, h), which every wave shares and
+    // which is mostly served by the L2, so that a batch always follows each
+    // chunk (the counter waits assume it).  The copies into the buffer are
+    // ordered after this wave's reads of it by the wait on the LDS counter.
+    auto run_chunk = [&](int64_t k, CR& r, auto buf_tag) {
+      const int64_t ch = gw + k * nw_row;
       process_chunk(ch, r, ch >= full_end, buf_tag);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      issue_batch(ch + 2 < wc1 ? ch + 2 : 0, r, buf_tag);
+      issue_batch(k + 2 < wn ? gw + (k + 2) * nw_row : 0, r, buf_tag);
     };
-    // ra holds chunk ch, rb chunk ch + 1 (both in flight or landed)
-    for (int64_t ch = wc0; ch < wc1; ch += 2) {
-      run_chunk(ch, ra, std::integral_constant<int, 0>{});
-      if (ch + 1 >= wc1) break;
-      run_chunk(ch + 1, rb, std::integral_constant<int, 1>{});
+    // ra holds the wave's chunk k, rb its chunk k + 1 (in flight or landed)
+    for (int64_t k = 0; k < wn; k += 2) {
+      run_chunk(k, ra, std::integral_constant<int, 0>{});
+      if (k + 1 >= wn) break;
+      run_chunk(k + 1, rb, std::integral_constant<int, 1>{});
     }
     // let every copy land before the buffers are left behind
     wait_vmcnt<0>();

@@ -312,6 +312,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   float m = -__builtin_inff(), l = 0.f, z = 0.f;
   int kexp = kNoScale;                               // P'' = p * delta * 2^kexp
   const float neg_lo = is_lo ? -1.0f : 0.0f;
+  // byte selector of v_perm: identity on high lanes, 16-bit halves swapped
+  // on low lanes
+  const uint32_t swap_sel = is_lo ? 0x01000302u : 0x03020100u;
 
   // Running-max update shared by both token kinds: the max moves only when
   // a score exceeds it by more than the slack, so p <= 2^8 in between.
@@ -475,34 +478,39 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       cm = max_xor32(cm);
       raise_max(cm);
       const float km0 = kap[0] - m, km1 = kap[1] - m;
-      // ---- P.V per 32-token step (tiles 2ps, 2ps+1)
+      // ---- P.V per 32-token step (tiles 2ps, 2ps+1).  A high column and
+      // its low partner (GQA lanes apart in the row) hold the same scores:
+      // the high one weighs tile 2ps, the low one tile 2ps+1, and each takes
+      // the other tile's weights from its partner; both then pack the pair
+      // in tile order (high or low parts).  l and z gather per tile parity
+      // and meet at the end.
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps) {
         if (ps * 32 >= nv) break;
         const int t0 = 2 * ps, t1 = 2 * ps + 1;
         const float kmp = (t0 / kSegTiles) == 0 ? km0 : km1;
-        const float4 d0v = *reinterpret_cast<const float4*>(&vpb[wave][0][16 * t0 + 4 * lg]);
-        const float4 d1v = *reinterpret_cast<const float4*>(&vpb[wave][0][16 * t1 + 4 * lg]);
-        const float4 z0v = *reinterpret_cast<const float4*>(&vpb[wave][1][16 * t0 + 4 * lg]);
-        const float4 z1v = *reinterpret_cast<const float4*>(&vpb[wave][1][16 * t1 + 4 * lg]);
-        const float d0s[4] = {d0v.x * vfk[0], d0v.y * vfk[1], d0v.z * vfk[2], d0v.w * vfk[3]};
-        const float d1s[4] = {d1v.x * vfk[0], d1v.y * vfk[1], d1v.z * vfk[2], d1v.w * vfk[3]};
-        const float z0s[4] = {z0v.x, z0v.y, z0v.z, z0v.w}, z1s[4] = {z1v.x, z1v.y, z1v.z, z1v.w};
-        float p0[4], p1[4];
+        const int tok = 16 * (is_lo ? t1 : t0) + 4 * lg;
+        const float4 dv = *reinterpret_cast<const float4*>(&vpb[wave][0][tok]);
+        const float4 zv = *reinterpret_cast<const float4*>(&vpb[wave][1][tok]);
+        const float ds[4] = {dv.x * vfk[0], dv.y * vfk[1], dv.z * vfk[2], dv.w * vfk[3]};
+        const float zs[4] = {zv.x, zv.y, zv.z, zv.w};
+        float pm[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t0][i], kS, kmp));
-          p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t1][i], kS, kmp));
-          l += p0[i] + p1[i];                 // every lane; owners are kept at the end
-          z = __builtin_fmaf(p0[i], z0s[i], z);
-          z = __builtin_fmaf(p1[i], z1s[i], z);
+          const float sm = is_lo ? sc[t1][i] : sc[t0][i];
+          pm[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm, kS, kmp));
+          l += pm[i];                         // every lane; owners and partners meet at the end
+          z = __builtin_fmaf(pm[i], zs[i], z);
         }
-        float w0[4], w1[4];
-        field_weights<BITS>(p0, d0s, w0);
-        field_weights<BITS>(p1, d1s, w1);
+        float wm[4];
+        field_weights<BITS>(pm, ds, wm);
         u32x4_t ap;
 #pragma unroll
-        for (int r2 = 0; r2 < 4; ++r2) ap[r2] = split_pack(w0[r2], w1[r2], neg_lo);
+        for (int r2 = 0; r2 < 4; ++r2) {
+          const float wo = dpp_rot<kJoin>(wm[r2]);
+          // (own, other) -> (tile 2ps, tile 2ps+1): halves swapped on low lanes
+          ap[r2] = __builtin_amdgcn_perm(0u, split_pack(wm[r2], wo, neg_lo), swap_sel);
+        }
 #pragma unroll
         for (int n = 0; n < kNB; ++n) {
           u32x4_t bv;
@@ -582,7 +590,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const float sc = sum_xor32(part);             // score of head hh
       raise_max(sc);
       const float p = __builtin_amdgcn_exp2f(sc - m);
-      if (lg == 0) l += p;                          // one lane group per column
+      if (lg == 0 && !is_lo) l += p;                // one lane group of the high columns
       float pr[4];
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2) {
@@ -601,6 +609,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   // ---- wave result: join high and low rows (in real units), reduce l and
   // z over the lane groups of the owner columns
   {
+    l += dpp_rot<kJoin>(l);            // owner (even tiles, exact tokens) + partner (odd tiles)
+    z += dpp_rot<kJoin>(z);
     if (!owner) {
       l = 0.f;
       z = 0.f;

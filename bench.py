@@ -116,8 +116,15 @@ def cpu_baseline(w, data, sample_seconds: float):
             times.append(time.perf_counter() - t0)
     per_kv_head = sum(times) / len(times)
     step_s = per_kv_head * w.n_kv_heads * w.batch
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": w.batch / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
         "sample": (f"oracle decode attention (fp64, dequantize then attend) for the {g} q heads "
                    f"of one KV head at T={T}, {len(times)} runs, mean {per_kv_head:.3f}s, "
                    f"scaled x{w.n_kv_heads * w.batch} to one step; append not timed"),

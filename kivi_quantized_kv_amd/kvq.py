@@ -77,7 +77,7 @@ def load_library(path: str | None = None):
     return lib
 
 
-@dataclasses.dataclass
+@dataclasses.dataclass(frozen=True)
 class Config:
     batch: int
     n_kv_heads: int
@@ -90,8 +90,19 @@ class Config:
     dtype: str = "bf16"
 
     def c(self) -> c_config:
+        """A new kvq_config struct of these fields."""
         return c_config(self.batch, self.n_kv_heads, self.head_dim, self.bits, self.group,
                         self.sink, self.residual, DTYPE_CODE[self.dtype], self.capacity)
+
+    def _cref(self):
+        """Pointer to this config's struct, built once (the dataclass is frozen)."""
+        r = self.__dict__.get("_ref")
+        if r is None:
+            c = self.c()
+            r = ctypes.byref(c)
+            object.__setattr__(self, "_keep", c)
+            object.__setattr__(self, "_ref", r)
+        return r
 
     # closed-form sizes, as in include/kvq.h
     @property
@@ -132,8 +143,26 @@ class Cache:
     BUFFERS = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
                "k_sink", "v_sink", "k_resid", "v_resid")
 
+    def __setattr__(self, name, value):
+        # a replaced buffer invalidates the cached kvq_cache struct
+        super().__setattr__(name, value)
+        if name in self.BUFFERS:
+            super().__setattr__("_ref", None)
+
     def c(self) -> c_cache:
+        """A new kvq_cache struct of the current buffers."""
         return c_cache(*[_ptr(getattr(self, n)) for n in self.BUFFERS])
+
+    def _cref(self):
+        """Pointer to the struct of the current buffers, rebuilt after a
+        buffer is replaced."""
+        r = self.__dict__.get("_ref")
+        if r is None:
+            c = self.c()
+            r = ctypes.byref(c)
+            super().__setattr__("_keep", c)
+            super().__setattr__("_ref", r)
+        return r
 
     def nbytes(self) -> int:
         return sum(getattr(self, n).numel() * getattr(self, n).element_size() for n in self.BUFFERS)
@@ -156,8 +185,13 @@ def tensor(t: torch.Tensor) -> c_tensor:
     raise ValueError("expected a 3-d or 4-d tensor")
 
 
-def _stream(stream):
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device: torch.device | None = None):
     if stream is None:
+        if _raw_stream is not None and device is not None and device.index is not None:
+            return _raw_stream(device.index)        # torch's current stream on that device
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
@@ -171,25 +205,25 @@ def _check(fn: str, status: int):
 
 def kvq_quantize_keys(cfg: Config, cache: Cache, k: torch.Tensor, n_tokens: int, stream=None):
     lib = load_library()
-    c, cc = cfg.c(), cache.c()
+    c, cc = cfg._cref(), cache._cref()
     _check("kvq_quantize_keys",
-           lib.kvq_quantize_keys(ctypes.byref(c), ctypes.byref(cc), tensor(k), n_tokens, _stream(stream)))
+           lib.kvq_quantize_keys(c, cc, tensor(k), n_tokens, _stream(stream, k.device)))
 
 
 def kvq_quantize_values(cfg: Config, cache: Cache, v: torch.Tensor, n_tokens: int, stream=None):
     lib = load_library()
-    c, cc = cfg.c(), cache.c()
+    c, cc = cfg._cref(), cache._cref()
     _check("kvq_quantize_values",
-           lib.kvq_quantize_values(ctypes.byref(c), ctypes.byref(cc), tensor(v), n_tokens, _stream(stream)))
+           lib.kvq_quantize_values(c, cc, tensor(v), n_tokens, _stream(stream, v.device)))
 
 
 def kvq_append_token(cfg: Config, cache: Cache, n_before: int, k_new: torch.Tensor,
                      v_new: torch.Tensor, stream=None):
     lib = load_library()
-    c, cc = cfg.c(), cache.c()
+    c, cc = cfg._cref(), cache._cref()
     _check("kvq_append_token",
-           lib.kvq_append_token(ctypes.byref(c), ctypes.byref(cc), n_before, tensor(k_new),
-                                tensor(v_new), _stream(stream)))
+           lib.kvq_append_token(c, cc, n_before, tensor(k_new),
+                                tensor(v_new), _stream(stream, k_new.device)))
 
 
 def kvq_decode_attention(cfg: Config, cache: Cache, n_tokens: int, q: torch.Tensor,
@@ -201,11 +235,11 @@ def kvq_decode_attention(cfg: Config, cache: Cache, n_tokens: int, q: torch.Tens
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = torch.empty(cfg.workspace_bytes(Hq), dtype=torch.uint8, device=q.device)
-    c, cc = cfg.c(), cache.c()
+    c, cc = cfg._cref(), cache._cref()
     _check("kvq_decode_attention",
-           lib.kvq_decode_attention(ctypes.byref(c), ctypes.byref(cc), n_tokens, Hq, tensor(q),
+           lib.kvq_decode_attention(c, cc, n_tokens, Hq, tensor(q),
                                     float(softmax_scale), out.data_ptr(), workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+                                    workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
     return out
 
 

@@ -349,16 +349,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const int vtok = (lane & 31) * 2;                // value deltas this lane checks
 
     u32x4_t qB[kKS];
-    float kap[2] = {0.f, 0.f};                       // kappa of each segment's group
-    int64_t cur_grp = -1;
 
     auto process_chunk = [&](int64_t ch, const CR& r, bool half, auto buf_tag) {
       constexpr int BUF = decltype(buf_tag)::value;
       const auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
       const auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
-      const int64_t base = ch << 6;
+      (void)ch;
       const int nv = half ? 32 : 64;           // a half chunk (only ever the last) holds 32 tokens
-      const int64_t g0 = base >> gsh;
       constexpr int kSegTiles = G32 ? 2 : 4;
       // this chunk's batch is complete once at most the next one is in flight
       wait_vmcnt<kBatch>();
@@ -382,14 +379,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       }
       // ---- q.K^T: per key-group segment, K-steps outer, tiles inner
       f32x4_t sc[4];
+      float kap[2] = {0.f, 0.f};               // kappa of each segment's group
 #pragma unroll
       for (int seg = 0; seg < 2; ++seg) {
         const int t_begin = seg * kSegTiles;
         const int t_end = t_begin + kSegTiles;
-        if (t_begin >= 4 || (seg == 1 && half)) break;
-        const int64_t grp = g0 + (G32 ? seg : 0);
-        if (grp != cur_grp) {
-          cur_grp = grp;
+        if (t_begin >= 4) break;
+        // (a half chunk's second segment may read parameters of a group not
+        // yet written: its scores are replaced by -inf below)
+        {
           const float* kpd = reinterpret_cast<const float*>(&kpb[wave][G32 ? seg : 0][0]);
 #pragma unroll
           for (int kk = 0; kk < kKS; ++kk) {
@@ -436,8 +434,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           kpart += dpp_rot<kJoin>(kpart);
           kpart = sum_xor16(kpart);
           kap[seg] = sum_xor32(kpart);
-        } else if (seg == 1) {
-          kap[1] = kap[0];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -486,19 +482,26 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       // and meet at the end.
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps) {
-        if (ps * 32 >= nv) break;
+        // the second step of a half chunk weighs nothing (its parameters may
+        // never have been written: cleared by a bit mask, which the compiler
+        // keeps as arithmetic, so both steps stay in one block)
+        const uint32_t live = (ps == 1 && half) ? 0u : ~0u;
+        auto keep = [live](float x) {
+          return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & live);
+        };
         const int t0 = 2 * ps, t1 = 2 * ps + 1;
         const float kmp = (t0 / kSegTiles) == 0 ? km0 : km1;
         const int tok = 16 * (is_lo ? t1 : t0) + 4 * lg;
         const float4 dv = *reinterpret_cast<const float4*>(&vpb[wave][0][tok]);
         const float4 zv = *reinterpret_cast<const float4*>(&vpb[wave][1][tok]);
-        const float ds[4] = {dv.x * vfk[0], dv.y * vfk[1], dv.z * vfk[2], dv.w * vfk[3]};
-        const float zs[4] = {zv.x, zv.y, zv.z, zv.w};
+        const float ds[4] = {keep(dv.x * vfk[0]), keep(dv.y * vfk[1]), keep(dv.z * vfk[2]),
+                             keep(dv.w * vfk[3])};
+        const float zs[4] = {keep(zv.x), keep(zv.y), keep(zv.z), keep(zv.w)};
         float pm[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float sm = is_lo ? sc[t1][i] : sc[t0][i];
-          pm[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm, kS, kmp));
+          pm[i] = keep(__builtin_amdgcn_exp2f(__builtin_fmaf(sm, kS, kmp)));
           l += pm[i];                         // every lane; owners and partners meet at the end
           z = __builtin_fmaf(pm[i], zs[i], z);
         }

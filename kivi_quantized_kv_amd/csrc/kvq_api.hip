@@ -15,6 +15,15 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+int device_cu_count();
+
+// One workgroup per (batch, q head) row fills the GPU when the rows come in
+// whole rounds of CUs (or so many rounds that a partial last one is cheap).
+bool direct_rows(int64_t rows) {
+  const int64_t cu = device_cu_count();
+  return rows >= cu && (rows % cu == 0 || rows >= 4 * cu);
+}
+
 // Compute units of the current device (cached per device id; a host query,
 // no allocation).  Falls back to 256 if the query fails.
 int device_cu_count() {
@@ -126,6 +135,9 @@ template <int DT, int D, int BITS> struct AttnValuFn {
 };
 template <int DT, int D, int BITS> struct AttnValuOccFn {
   static int run() { return attn_valu_blocks_per_cu<DT, D, BITS>(); }
+};
+template <int DT, int D, int BITS> struct AttnValuDirectOkFn {
+  static bool run() { return attn_valu_direct_ok<DT, D, BITS>(); }
 };
 
 // Prefill of one half: fp copies of sinks and residual tokens, then the
@@ -260,6 +272,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     int64_t fp_per_split = 32;
     int64_t bps = 1;
     int64_t n_split = 0;
+    bool direct = false;
     if (mfma) {
       const int64_t slots = 2 * int64_t(device_cu_count());
       const int64_t rows = int64_t(B) * H;
@@ -275,6 +288,13 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
       if (n_split < want_fp) n_split = want_fp;
       if (n_split < 1) n_split = 1;
       fp_per_split = (n_fp + n_split - 1) / n_split;
+    } else if (direct_rows(int64_t(B) * n_q_heads) && dispatch3<AttnValuDirectOkFn>(cfg)) {
+      // the rows alone fill the GPU: one 16-wave workgroup per row takes
+      // all of its tokens, merges in LDS and writes the output
+      direct = true;
+      n_split = 1;
+      bps = nblk > 0 ? nblk : 1;
+      fp_per_split = n_fp > 0 ? n_fp : 1;
     } else {
       // one round of resident workgroups, at least one block per wave
       const int64_t slots = int64_t(dispatch3<AttnValuOccFn>(cfg)) * device_cu_count();
@@ -308,6 +328,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     a.H = H; a.Hq = n_q_heads; a.gqa = n_q_heads / H; a.G = int(G);
     a.g_shift = G == 32 ? 5 : (G == 64 ? 6 : 7);
     a.n_split = int(n_split);
+    a.direct = direct ? 1 : 0;
     a.blocks_per_split = int(bps);
     a.fp_per_split = int(fp_per_split);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -320,6 +341,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
       else ea = dispatch3<AttnValuFn>(cfg, a, B, s);
     }
     if (ea != hipSuccess) return KVQ_EHIP;
+    if (direct) return KVQ_OK;
     hipError_t e;
     if (cfg->dtype == KVQ_F32) e = D == 64 ? launch_merge<DT_F32, 64>(a, B, s) : launch_merge<DT_F32, 128>(a, B, s);
     else if (cfg->dtype == KVQ_F16) e = D == 64 ? launch_merge<DT_F16, 64>(a, B, s) : launch_merge<DT_F16, 128>(a, B, s);

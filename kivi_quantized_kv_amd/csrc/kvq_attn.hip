@@ -180,10 +180,13 @@ __device__ __forceinline__ void load_small(const void* base, int64_t i, float* o
 }
 
 // ---------------------------------------------------------------------------
-// VALU kernel: one workgroup of 4 waves per (split, q head, batch).  A split
-// owns a run of value-code blocks of L tokens (32 at 4/8 bits, 64 at 2
-// bits) and a run of the full-precision tokens; its four waves share both
-// evenly and fold them into one softmax state each.
+// VALU kernel: one workgroup of NW waves per (split, q head, batch).  A
+// split owns a run of value-code blocks of L tokens (32 at 4/8 bits, 64 at 2
+// bits) and a run of the full-precision tokens; its waves share both evenly
+// and fold them into one softmax state each.  With NW = 4 the workgroup
+// writes its split's partial for the log-sum-exp merge; with NW = 16 it is
+// the only split of its row (the rows alone fill the GPU), merges its waves
+// in LDS and writes the output row itself.
 //
 // Full-precision tokens go first, in tiles of 16: lane (qt, tl) scores
 // token tl over channel quarter qt, and lane l then adds channels
@@ -206,8 +209,9 @@ __device__ __forceinline__ void load_small(const void* base, int64_t i, float* o
 template <int DT, int D, int BITS>
 constexpr int valu_waves_per_simd() { return (D == 64 || (BITS == 4 && DT == DT_F16)) ? 4 : 3; }
 
-template <int DT, int D, int BITS>
-__global__ __launch_bounds__(256, (valu_waves_per_simd<DT, D, BITS>())) void k_attn_valu(AttnArgs a) {
+template <int DT, int D, int BITS, int NW>
+__global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D, BITS>())) void k_attn_valu(
+    AttnArgs a) {
   using VL = VLayout<BITS>;
   using WS = WordShape<BITS>;
   constexpr float kS = 16777216.0f;              // 2^24: unit of a subnormal field
@@ -231,10 +235,11 @@ __global__ __launch_bounds__(256, (valu_waves_per_simd<DT, D, BITS>())) void k_a
   const int vj = lane & 15;         // P.V: channel within 16
 
   __shared__ __attribute__((aligned(16))) float s_q[D];
-  __shared__ __attribute__((aligned(16))) float s_x[4][kHalves][D];
-  __shared__ float s_out[4][D + 2];
+  constexpr int kThreads = 64 * NW;
+  __shared__ __attribute__((aligned(16))) float s_x[NW][kHalves][D];
+  __shared__ float s_out[NW][D + 2];
 
-  for (int d = threadIdx.x; d < D; d += 256)
+  for (int d = threadIdx.x; d < D; d += kThreads)
     s_q[d] = load1<DT>(a.q, b * a.q_sb + hq * a.q_sh + d) * a.sm_scale_log2;
   __syncthreads();
 
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(256, (valu_waves_per_simd<DT, D, BITS>())) void k_a
   const int64_t nblk = (a.Q + VL::L - 1) / VL::L;
   const int64_t blk0 = int64_t(split) * a.blocks_per_split;
   const int64_t blk1 = blk0 + a.blocks_per_split < nblk ? blk0 + a.blocks_per_split : nblk;
-  const int64_t per_wave = blk1 > blk0 ? (blk1 - blk0 + 3) / 4 : 0;
+  const int64_t per_wave = blk1 > blk0 ? (blk1 - blk0 + NW - 1) / NW : 0;
   const int64_t wb0 = blk0 + wave * per_wave;
   const int64_t wb1 = wb0 + per_wave < blk1 ? wb0 + per_wave : blk1;
 
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(256, (valu_waves_per_simd<DT, D, BITS>())) void k_a
   {
     const int64_t f0 = int64_t(split) * a.fp_per_split;
     const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
-    const int64_t fpw = f1 > f0 ? (f1 - f0 + 3) / 4 : 0;
+    const int64_t fpw = f1 > f0 ? (f1 - f0 + NW - 1) / NW : 0;
     const int64_t fw0 = f0 + wave * fpw;
     const int64_t fw1 = fw0 + fpw < f1 ? fw0 + fpw : f1;
     // element offset of exact token i's row and the store holding it
@@ -495,28 +500,39 @@ __global__ __launch_bounds__(256, (valu_waves_per_simd<DT, D, BITS>())) void k_a
     s_out[wave][D + 1] = l;
   }
   __syncthreads();
-  // merge the four waves and write this split's partial; a wave with no
-  // tokens left m = -inf, l = 0 and a zero row
-  float* dst = a.ws + ((int64_t(b) * a.Hq + hq) * a.n_split + split) * (D + 2);
+  // merge the waves; a wave with no tokens left m = -inf, l = 0 and a zero
+  // row.  NW = 4: this split's partial; NW = 16: the output row.
   float M = s_out[0][D];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, s_out[w][D]);
+  for (int w = 1; w < NW; ++w) M = __builtin_fmaxf(M, s_out[w][D]);
   const float Mref = M == -__builtin_inff() ? 0.f : M;
-  float f[4];
+  float f[NW];
+  float L = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) f[w] = __builtin_amdgcn_exp2f(s_out[w][D] - Mref);
-  for (int d = threadIdx.x; d < D; d += 256) {
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o = __builtin_fmaf(f[w], s_out[w][d], o);
-    dst[d] = o;
+  for (int w = 0; w < NW; ++w) {
+    f[w] = __builtin_amdgcn_exp2f(s_out[w][D] - Mref);
+    L = __builtin_fmaf(f[w], s_out[w][D + 1], L);
   }
-  if (threadIdx.x == 0) {
-    float L = 0.f;
+  if constexpr (NW == 16) {
+    float* dst = a.out + (int64_t(b) * a.Hq + hq) * D;
+    for (int d = threadIdx.x; d < D; d += kThreads) {
+      float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) L = __builtin_fmaf(f[w], s_out[w][D + 1], L);
-    dst[D] = M;
-    dst[D + 1] = L;
+      for (int w = 0; w < NW; ++w) o = __builtin_fmaf(f[w], s_out[w][d], o);
+      dst[d] = o / L;
+    }
+  } else {
+    float* dst = a.ws + ((int64_t(b) * a.Hq + hq) * a.n_split + split) * (D + 2);
+    for (int d = threadIdx.x; d < D; d += kThreads) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) o = __builtin_fmaf(f[w], s_out[w][d], o);
+      dst[d] = o;
+    }
+    if (threadIdx.x == 0) {
+      dst[D] = M;
+      dst[D + 1] = L;
+    }
   }
 }
 
@@ -593,17 +609,31 @@ template <int DT, int D, int BITS>
 int attn_valu_blocks_per_cu() {
   static const int n = [] {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_valu<DT, D, BITS>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_valu<DT, D, BITS, 4>, 256, 0) != hipSuccess ||
         v < 1)
       v = 1;
     return v;
   }();
   return n;
 }
+// Whether the one-split form (16 waves, output written directly) exists for
+// this instantiation: it needs the kernel to fit four waves per SIMD.
+template <int DT, int D, int BITS>
+bool attn_valu_direct_ok() {
+  return valu_waves_per_simd<DT, D, BITS>() == 4;
+}
 
 template <int DT, int D, int BITS>
 hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn_valu<DT, D, BITS>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
+  if (a.n_split == 1 && a.direct) {
+    if constexpr (valu_waves_per_simd<DT, D, BITS>() == 4) {
+      hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 16>), dim3(1, a.Hq, B), dim3(1024), 0, s, a);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 4>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <int DT, int D>
@@ -618,7 +648,10 @@ hipError_t launch_merge(const AttnArgs& a, int B, hipStream_t s) {
   template hipError_t launch_attn_valu<DT, D, 8>(const AttnArgs&, int, hipStream_t); \
   template int attn_valu_blocks_per_cu<DT, D, 2>();                                  \
   template int attn_valu_blocks_per_cu<DT, D, 4>();                                  \
-  template int attn_valu_blocks_per_cu<DT, D, 8>();
+  template int attn_valu_blocks_per_cu<DT, D, 8>();                                  \
+  template bool attn_valu_direct_ok<DT, D, 2>();                                     \
+  template bool attn_valu_direct_ok<DT, D, 4>();                                     \
+  template bool attn_valu_direct_ok<DT, D, 8>();
 KVQ_INST_VALU(DT_F32, 64)
 KVQ_INST_VALU(DT_F32, 128)
 KVQ_INST_VALU(DT_F16, 64)

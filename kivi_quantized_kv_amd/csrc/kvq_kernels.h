@@ -58,6 +58,7 @@ struct AttnArgs {
   int64_t resid_slot0;      // ring slot of the first residual token, Q mod ring
   int H, Hq, gqa, G, g_shift;
   int n_split;              // splits per (batch, q head)
+  int direct;               // VALU kernel, one split per row: write out, no merge
   int blocks_per_split;     // value-code blocks per quantized split
   int fp_per_split;         // full-precision tokens per split that takes them
 };
@@ -74,6 +75,8 @@ template <int DT, int D, int BITS>
 hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s);
 template <int DT, int D, int BITS>
 int attn_valu_blocks_per_cu();
+template <int DT, int D, int BITS>
+bool attn_valu_direct_ok();
 template <int DT, int D, int BITS, int GQA>
 hipError_t launch_attn_mfma(const AttnArgs& a, int B, hipStream_t s);
 template <int DT, int D>

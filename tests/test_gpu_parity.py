@@ -61,6 +61,13 @@ SMALL = [
     (3, 24, 3, 128, 4, 64, 4, 128, 4100, "bf16"),
     (1, 32, 4, 128, 2, 32, 4, 32, 548, "bf16"),     # Q % 64 == 32
     (1, 64, 8, 128, 4, 64, 4, 128, 70000, "bf16"),
+    # VALU kernel, one 16-wave workgroup per (batch, q head) row when the
+    # rows fill a 256-CU part: D 64 (every width), D 128 4-bit fp16, and a
+    # cache with no quantized tokens yet
+    (16, 16, 16, 64, 2, 32, 4, 32, 300, "f32"),
+    (8, 32, 32, 128, 4, 32, 4, 128, 700, "f16"),
+    (4, 64, 32, 64, 8, 64, 3, 64, 260, "bf16"),
+    (16, 16, 16, 64, 4, 32, 4, 32, 40, "f16"),
 ]
 
 

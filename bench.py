@@ -186,7 +186,7 @@ def main():
     torch.cuda.synchronize()
     log(f"{n_layers} layer caches of {layers[0].nbytes() / 2**20:.1f} MiB prefilled")
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
-    ws = cfg.workspace(w.n_q_heads)
+    ws = torch.empty(cfg.workspace_bytes(w.n_q_heads), dtype=torch.uint8, device="cuda")
     n_tok = [w.n_tokens] * n_layers
 
     def step(i):

@@ -162,22 +162,16 @@ static inline int64_t kvq_resid_bytes(const kvq_config *c) {
          kvq_dtype_bytes(c->dtype);
 }
 
-/* Decode-attention workspace: KVQ_WORKSPACE_COUNTER_BYTES of arrival
- * counters, then per (batch, query head) up to KVQ_MAX_SPLITS partial
- * results of D + 2 floats, then one merged partial per 8 of them.  The
- * counter bytes must be zero before the workspace is first used (for
- * instance allocated zero-filled); every completed call leaves them zero.
- * The rest needs no initialization.  Any size of at least
+/* Decode-attention workspace: per (batch, query head) up to
+ * KVQ_MAX_SPLITS partial results of D + 2 floats.  Any size of at least
  * kvq_workspace_bytes_min works; the kernel uses fewer splits when given
  * less room.  Results agree across split counts to fp32 rounding. */
 #define KVQ_MAX_SPLITS 1024
-#define KVQ_WORKSPACE_COUNTER_BYTES 65536
 static inline int64_t kvq_workspace_bytes(const kvq_config *c, int32_t n_q_heads) {
-  return KVQ_WORKSPACE_COUNTER_BYTES +
-         (int64_t)c->batch * n_q_heads * (KVQ_MAX_SPLITS + KVQ_MAX_SPLITS / 8) * (c->head_dim + 2) * 4;
+  return (int64_t)c->batch * n_q_heads * KVQ_MAX_SPLITS * (c->head_dim + 2) * 4;
 }
 static inline int64_t kvq_workspace_bytes_min(const kvq_config *c, int32_t n_q_heads) {
-  return KVQ_WORKSPACE_COUNTER_BYTES + (int64_t)c->batch * n_q_heads * (64 + 8) * (c->head_dim + 2) * 4;
+  return (int64_t)c->batch * n_q_heads * 64 * (c->head_dim + 2) * 4;
 }
 
 /* ---- entry points -------------------------------------------------- */
@@ -235,10 +229,8 @@ kvq_status kvq_append_token(const kvq_config *cfg, const kvq_cache *cache, int64
  *   q:   [B][n_q_heads][D] in cfg->dtype; n_q_heads a multiple of Hkv.
  *   out: f32 [B][n_q_heads][D], written densely.
  *   softmax_scale: <= 0 selects 1/sqrt(D).
- *   workspace: device scratch of workspace_bytes bytes (see above): its
- *   counter bytes zero before the first call (calls keep them zero), the
- *   rest needing no initialization and garbage afterwards.  Calls that
- *   overlap in time must use different workspaces.
+ *   workspace: device scratch of workspace_bytes bytes (see above); its
+ *   contents need no initialization and are garbage afterwards.
  * Errors: KVQ_EINVAL (null pointers, n_tokens < 1, bad n_q_heads),
  * KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EUNSUPPORTED, KVQ_EHIP.
  */

@@ -253,15 +253,11 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     const int64_t n_sink = T < S ? T : S;
     const int64_t n_res = T > S ? T - S - Q : 0;
     const int64_t n_fp = n_sink + n_res;
-    // Workspace: arrival counters, then the split partials, then the merged
-    // partials of split groups (at most one per 8 splits).
     const int64_t per_split_bytes = int64_t(B) * n_q_heads * (D + 2) * 4;
-    if (int64_t(workspace_bytes) < kvq_workspace_bytes_min(cfg, n_q_heads)) return KVQ_EWORKSPACE;
-    const int64_t usable = int64_t(workspace_bytes) - KVQ_WORKSPACE_COUNTER_BYTES;
-    int64_t cap_splits = usable * 8 / (per_split_bytes * 9);
+    int64_t cap_splits = int64_t(workspace_bytes) / per_split_bytes;
     if (cap_splits > KVQ_MAX_SPLITS) cap_splits = KVQ_MAX_SPLITS;
-    while (cap_splits > 0 && (cap_splits + (cap_splits + 7) / 8) * per_split_bytes > usable) --cap_splits;
-    if (cap_splits < 2) return KVQ_EWORKSPACE;
+    if (int64_t(workspace_bytes) < kvq_workspace_bytes_min(cfg, n_q_heads) || cap_splits < 2)
+      return KVQ_EWORKSPACE;
 
     // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit
     // codes.  It works per KV head on 64-token chunks, with the grid sized
@@ -321,9 +317,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     a.k_sink = cache->k_sink; a.v_sink = cache->v_sink;
     a.k_resid = cache->k_resid; a.v_resid = cache->v_resid;
     a.q = q.ptr; a.q_sb = q.stride_b; a.q_sh = q.stride_h;
-    a.counters = reinterpret_cast<uint32_t*>(workspace);
-    a.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + KVQ_WORKSPACE_COUNTER_BYTES);
-    a.ws2 = a.ws + int64_t(B) * n_q_heads * n_split * (D + 2);
+    a.ws = reinterpret_cast<float*>(workspace);
     a.out = out;
     const double scale = softmax_scale > 0 ? double(softmax_scale) : 1.0 / std::sqrt(double(D));
     a.sm_scale_log2 = float(scale * 1.4426950408889634);
@@ -335,18 +329,6 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     a.g_shift = G == 32 ? 5 : (G == 64 ? 6 : 7);
     a.n_split = int(n_split);
     a.direct = direct ? 1 : 0;
-    // Splits merge inside the attention kernel when the arrival counters
-    // fit: groups of 8 splits (about sqrt(n_split) past 64 splits), then the
-    // groups of each row.
-    {
-      const int64_t rows = mfma ? int64_t(B) * H : int64_t(B) * n_q_heads;
-      int64_t grp = 8;
-      while (n_split > 64 && grp * grp < n_split) ++grp;
-      const int64_t n_groups = (n_split + grp - 1) / grp;
-      a.merge_group = int(grp);
-      a.n_groups = int(n_groups);
-      a.fused = !direct && rows * (n_groups + 1) <= KVQ_WORKSPACE_COUNTER_BYTES / 4 ? 1 : 0;
-    }
     a.blocks_per_split = int(bps);
     a.fp_per_split = int(fp_per_split);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -359,7 +341,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
       else ea = dispatch3<AttnValuFn>(cfg, a, B, s);
     }
     if (ea != hipSuccess) return KVQ_EHIP;
-    if (direct || a.fused) return KVQ_OK;
+    if (direct) return KVQ_OK;
     hipError_t e;
     if (cfg->dtype == KVQ_F32) e = D == 64 ? launch_merge<DT_F32, 64>(a, B, s) : launch_merge<DT_F32, 128>(a, B, s);
     else if (cfg->dtype == KVQ_F16) e = D == 64 ? launch_merge<DT_F16, 64>(a, B, s) : launch_merge<DT_F16, 128>(a, B, s);

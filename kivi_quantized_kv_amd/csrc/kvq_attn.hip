@@ -527,19 +527,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
       float o = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) o = __builtin_fmaf(f[w], s_out[w][d], o);
-      if (a.fused) st_dev(dst + d, o);
-      else dst[d] = o;
+      dst[d] = o;
     }
     if (threadIdx.x == 0) {
-      if (a.fused) {
-        st_dev(dst + D, M);
-        st_dev(dst + D + 1, L);
-      } else {
-        dst[D] = M;
-        dst[D + 1] = L;
-      }
+      dst[D] = M;
+      dst[D + 1] = L;
     }
-    if (a.fused) merge_split<1, D>(a, b, hq, split);
   }
 }
 

@@ -193,101 +193,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ---------------------------------------------------------------- split merge
-// Device-scope coherent stores and loads of merge data.  On gfx950 the
-// stores write through to the device's coherence point (sc1) and the loads
-// read from it, so partials written by one workgroup are seen by another on
-// any XCD once the writer's stores have completed, without a whole-L2
-// write-back.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until this wave's stores have completed (vector memory counter at
-// zero; stores count there on this target).
-__device__ __forceinline__ void wait_stores_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Arrival of this workgroup at a counter of `expected` arrivals (called by
-// every thread after its merge-data stores): returns to every thread
-// whether this workgroup arrived last, in which case the counter is back
-// at zero for the next call.  `flag` is a workgroup-shared int.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* flag) {
-  wait_stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = ticket == expected - 1;
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = last ? 1 : 0;
-  }
-  __syncthreads();
-  return *flag != 0;
-}
-
-// Log-sum-exp merge of `count` partials of H heads x D channels by one
-// 256-thread workgroup: partial j of head qh is (o[D], m, l) at
-// src + (qh * head_stride + j) * (D + 2).  Result: M = max m_j,
-// L = sum 2^(m_j - M) l_j, o = sum 2^(m_j - M) o_j; written as the output
-// row o / L (final) or as a partial at dst + qh * dst_head_stride.
-template <int H, int D>
-__device__ __forceinline__ void merge_partials(const float* src, int64_t head_stride, int count, bool final,
-                                               float* dst, int64_t dst_head_stride) {
-  constexpr int kOut = H * D;
-  constexpr int kE = kOut >= 256 ? kOut / 256 : 1;   // channels per thread
-  constexpr int kR = 8;                               // partials per load round
-  const int x = threadIdx.x * kE;
-  if (x >= kOut) return;
-  const int qh = x / D, d0 = x % D;
-  const float* base = src + qh * head_stride * (D + 2);
-  float M = -__builtin_inff(), L = 0.f, o[kE];
-#pragma unroll
-  for (int e = 0; e < kE; ++e) o[e] = 0.f;
-  for (int j0 = 0; j0 < count; j0 += kR) {
-    float mj[kR], lj[kR], oj[kR][kE];
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const int j = j0 + r < count ? j0 + r : count - 1;   // in range; weight 0 below
-      const float* pj = base + int64_t(j) * (D + 2);
-      mj[r] = j0 + r < count ? ld_dev(pj + D) : -__builtin_inff();
-      lj[r] = ld_dev(pj + D + 1);
-#pragma unroll
-      for (int e = 0; e < kE; ++e) oj[r][e] = ld_dev(pj + d0 + e);
-    }
-    float cm = mj[0];
-#pragma unroll
-    for (int r = 1; r < kR; ++r) cm = __builtin_fmaxf(cm, mj[r]);
-    if (cm > M) {
-      const float f = __builtin_amdgcn_exp2f(M - cm);   // 0 while M = -inf
-      L *= f;
-#pragma unroll
-      for (int e = 0; e < kE; ++e) o[e] *= f;
-      M = cm;
-    }
-    const float Mref = M == -__builtin_inff() ? 0.f : M;
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const float w = __builtin_amdgcn_exp2f(mj[r] - Mref);   // 0 for empty partials
-      L = __builtin_fmaf(w, lj[r], L);
-#pragma unroll
-      for (int e = 0; e < kE; ++e) o[e] = __builtin_fmaf(w, oj[r][e], o[e]);
-    }
-  }
-  float* out = dst + qh * dst_head_stride;
-  if (final) {
-#pragma unroll
-    for (int e = 0; e < kE; ++e) out[d0 + e] = o[e] / L;
-  } else {
-#pragma unroll
-    for (int e = 0; e < kE; ++e) st_dev(out + d0 + e, o[e]);
-    if (d0 == 0) {
-      st_dev(out + D, M);
-      st_dev(out + D + 1, L);
-    }
-  }
-}
-
 // ---------------------------------------------------------------- partition
 // With n = max(0, T - S): Q = G * floor((n - R) / G) if n >= R, else 0.
 __host__ __device__ __forceinline__ int64_t quantized_count(int64_t T, int64_t S, int64_t R,

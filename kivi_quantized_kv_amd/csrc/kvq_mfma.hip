@@ -655,21 +655,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       L = __builtin_fmaf(f, s_l[w][qh], L);
     }
     float* dst = a.ws + ((int64_t(b) * a.Hq + h * GQA + qh) * a.n_split + split) * (D + 2);
-    if (a.fused) {
-      st_dev(dst + d, o);
-      if (d == 0) {
-        st_dev(dst + D, M);
-        st_dev(dst + D + 1, L);
-      }
-    } else {
-      dst[d] = o;
-      if (d == 0) {
-        dst[D] = M;
-        dst[D + 1] = L;
-      }
+    dst[d] = o;
+    if (d == 0) {
+      dst[D] = M;
+      dst[D + 1] = L;
     }
   }
-  if (a.fused) merge_split<GQA, D>(a, b, h * GQA, split);
 }
 
 template <int DT, int D, int BITS, int GQA>

@@ -20,7 +20,6 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
 STATUS = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_EUNSUPPORTED", 3: "KVQ_ECAPACITY",
           4: "KVQ_EWORKSPACE", 5: "KVQ_EHIP"}
 MAX_SPLITS = 1024
-WORKSPACE_COUNTER_BYTES = 65536
 EXPORTS = ("kvq_quantize_keys", "kvq_quantize_values", "kvq_append_token",
            "kvq_decode_attention")
 
@@ -117,14 +116,8 @@ class Config:
         return self.head_dim * self.bits // 8
 
     def workspace_bytes(self, n_q_heads: int, splits: int = MAX_SPLITS) -> int:
-        """Room for `splits` partials per (batch, q head), their group merges
-        and the arrival counters (kvq.h)."""
-        return WORKSPACE_COUNTER_BYTES + self.batch * n_q_heads * (splits + -(-splits // 8)) * (
-            self.head_dim + 2) * 4
-
-    def workspace(self, n_q_heads: int, splits: int = MAX_SPLITS, device="cuda") -> torch.Tensor:
-        """A decode-attention workspace, zero-filled as its counters require."""
-        return torch.zeros(self.workspace_bytes(n_q_heads, splits), dtype=torch.uint8, device=device)
+        """Room for `splits` partials per (batch, q head)."""
+        return self.batch * n_q_heads * splits * (self.head_dim + 2) * 4
 
 
 class Cache:
@@ -241,7 +234,7 @@ def kvq_decode_attention(cfg: Config, cache: Cache, n_tokens: int, q: torch.Tens
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = cfg.workspace(Hq, device=q.device)
+        workspace = torch.empty(cfg.workspace_bytes(Hq), dtype=torch.uint8, device=q.device)
     c, cc = cfg._cref(), cache._cref()
     _check("kvq_decode_attention",
            lib.kvq_decode_attention(c, cc, n_tokens, Hq, tensor(q),

@@ -59,8 +59,9 @@ struct AttnArgs {
   int H, Hq, gqa, G, g_shift;
   int n_split;              // splits per (batch, q head)
   int direct;               // VALU kernel, one split per row: write out, no merge
-  int blocks_per_split;     // value-code blocks per quantized split
-  int fp_per_split;         // full-precision tokens per split that takes them
+  int blocks_per_split;     // value-code blocks per split (VALU kernel; the matrix-core
+                            // kernel deals chunks to its waves in turn instead)
+  int fp_per_split;         // full-precision tokens per split
 };
 
 template <int DT, int D, int BITS>

@@ -260,13 +260,14 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
       return KVQ_EWORKSPACE;
 
     // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit
-    // codes.  It works per KV head on 64-token chunks, with the grid sized
+    // codes, once at least one token is quantized (its chunk loads assume a
+    // chunk 0).  It works per KV head on 64-token chunks, with the grid sized
     // to one round of two workgroups per CU, and spreads the full-precision
     // tokens evenly over its splits.  Everything else runs the VALU kernel
     // per query head on value-code blocks, again with the full-precision
     // tokens spread evenly over the splits.
     const int gqa = n_q_heads / H;
-    const bool mfma = (gqa == 4 || gqa == 8) && cfg->bits != 8;
+    const bool mfma = (gqa == 4 || gqa == 8) && cfg->bits != 8 && Q > 0;
     const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
     const int64_t nblk = (Q + L - 1) / L;
     int64_t fp_per_split = 32;
@@ -332,8 +333,6 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     a.blocks_per_split = int(bps);
     a.fp_per_split = int(fp_per_split);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // With nothing quantized yet the matrix-core path has no splits: the
-    // merge kernel alone attends the full-precision tokens.
     hipError_t ea = hipSuccess;
     if (a.n_split > 0) {
       if (mfma && gqa == 8) ea = dispatch3<AttnMfma8Fn>(cfg, a, B, s);

@@ -61,6 +61,9 @@ SMALL = [
     (3, 24, 3, 128, 4, 64, 4, 128, 4100, "bf16"),
     (1, 32, 4, 128, 2, 32, 4, 32, 548, "bf16"),     # Q % 64 == 32
     (1, 64, 8, 128, 4, 64, 4, 128, 70000, "bf16"),
+    # GQA 4 / 8 with nothing quantized yet (the VALU kernel takes these)
+    (1, 8, 1, 128, 4, 64, 4, 128, 150, "bf16"),
+    (2, 8, 2, 64, 2, 32, 2, 32, 50, "f16"),
     # VALU kernel, one 16-wave workgroup per (batch, q head) row when the
     # rows fill a 256-CU part: D 64 (every width), D 128 4-bit fp16, and a
     # cache with no quantized tokens yet

@@ -316,10 +316,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 
     u32x4_t qB[kKS];
 
-    auto process_chunk = [&](const CR& r, bool half) {
+    // A half chunk (only ever the last of the quantized range) holds 32
+    // tokens: tiles 0 and 1, the first 32-token step of P.V.
+    auto process_chunk = [&](const CR& r, auto half_tag) {
+      constexpr bool HALF = decltype(half_tag)::value;
+      constexpr int kTiles = HALF ? 2 : 4;
       const auto& kpb = s_kp;
       const auto& vpb = s_vp;
-      const int nv = half ? 32 : 64;           // a half chunk (only ever the last) holds 32 tokens
+      constexpr int nv = HALF ? 32 : 64;
       constexpr int kSegTiles = G32 ? 2 : 4;
       // the chunk's parameters into the wave's LDS buffer (the wave's reads
       // of the previous chunk's were issued before, and LDS keeps a wave's
@@ -358,10 +362,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int seg = 0; seg < 2; ++seg) {
         const int t_begin = seg * kSegTiles;
-        const int t_end = t_begin + kSegTiles;
-        if (t_begin >= 4) break;
-        // (a half chunk's second segment may read parameters of a group not
-        // yet written: its scores are replaced by -inf below)
+        const int t_end = t_begin + kSegTiles < kTiles ? t_begin + kSegTiles : kTiles;
+        if (t_begin >= kTiles) break;
         {
           const float* kpd = reinterpret_cast<const float*>(&kpb[wave][G32 ? seg : 0][0]);
 #pragma unroll
@@ -427,24 +429,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         }
       }
       // join the high and low columns of each head (scores - kappa, times
-      // 2^-24); the second half of a half chunk (codes past the quantized
-      // range, still finite subnormal fields) is masked out
+      // 2^-24)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[t][i] += dpp_rot<kJoin>(sc[t][i]);
-          if (t >= 2) sc[t][i] = half ? -__builtin_inff() : sc[t][i];
-        }
+        for (int i = 0; i < 4; ++i) sc[t][i] += dpp_rot<kJoin>(sc[t][i]);
       }
       // ---- online softmax (log2 domain); m is per head, uniform over lanes
       float cm_seg[2] = {-__builtin_inff(), -__builtin_inff()};
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < kTiles; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cm_seg[t / kSegTiles] = __builtin_fmaxf(cm_seg[t / kSegTiles], sc[t][i]);
       float cm = __builtin_fmaf(cm_seg[0], kS, kap[0]);
-      if constexpr (G32) cm = __builtin_fmaxf(cm, __builtin_fmaf(cm_seg[1], kS, kap[1]));
+      if constexpr (G32 && !HALF) cm = __builtin_fmaxf(cm, __builtin_fmaf(cm_seg[1], kS, kap[1]));
       cm = max_xor16(cm);
       cm = max_xor32(cm);
       raise_max(cm);
@@ -456,27 +454,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       // in tile order (high or low parts).  l and z gather per tile parity
       // and meet at the end.
 #pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-        // the second step of a half chunk weighs nothing (its parameters may
-        // never have been written: cleared by a bit mask, which the compiler
-        // keeps as arithmetic, so both steps stay in one block)
-        const uint32_t live = (ps == 1 && half) ? 0u : ~0u;
-        auto keep = [live](float x) {
-          return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & live);
-        };
+      for (int ps = 0; ps < kTiles / 2; ++ps) {
         const int t0 = 2 * ps, t1 = 2 * ps + 1;
         const float kmp = (t0 / kSegTiles) == 0 ? km0 : km1;
         const int tok = 16 * (is_lo ? t1 : t0) + 4 * lg;
         const float4 dv = *reinterpret_cast<const float4*>(&vpb[wave][0][tok]);
         const float4 zv = *reinterpret_cast<const float4*>(&vpb[wave][1][tok]);
-        const float ds[4] = {keep(dv.x * vfk[0]), keep(dv.y * vfk[1]), keep(dv.z * vfk[2]),
-                             keep(dv.w * vfk[3])};
-        const float zs[4] = {keep(zv.x), keep(zv.y), keep(zv.z), keep(zv.w)};
+        const float ds[4] = {dv.x * vfk[0], dv.y * vfk[1], dv.z * vfk[2], dv.w * vfk[3]};
+        const float zs[4] = {zv.x, zv.y, zv.z, zv.w};
         float pm[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float sm = is_lo ? sc[t1][i] : sc[t0][i];
-          pm[i] = keep(__builtin_amdgcn_exp2f(__builtin_fmaf(sm, kS, kmp)));
+          pm[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm, kS, kmp));
           l += pm[i];                         // every lane; owners and partners meet at the end
           z = __builtin_fmaf(pm[i], zs[i], z);
         }
@@ -503,8 +493,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       }
     };
 
-    // only the last chunk of the quantized range can be a half chunk
-    const int64_t full_end = (a.Q & 63) ? nch - 1 : nch;
+    // only the last chunk of the quantized range can be a half chunk, and
+    // only the wave whose run ends on it has one
+    const bool last_half = (a.Q & 63) != 0 && gw + (wn - 1) * nw_row == nch - 1;
+    const int64_t n_full = wn - (last_half ? 1 : 0);
     // After a chunk its registers are free: start the loads of the wave's
     // chunk after next.  Past the wave's last chunk the loads re-read chunk
     // 0 of this (b, h) (valid: the wave has a chunk, so Q > 0), which every
@@ -512,20 +504,27 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // never under a branch: the compiler counts outstanding loads along
     // the control flow, and a path that skipped a batch would make it wait
     // for all of them.
-    auto run_chunk = [&](int64_t k, CR& r) {
-      const int64_t ch = gw + k * nw_row;
-      process_chunk(r, ch >= full_end);
+    auto run_chunk = [&](int64_t k, CR& r, auto half_tag) {
+      process_chunk(r, half_tag);
       issue_batch(k + 2 < wn ? gw + (k + 2) * nw_row : 0, r);
     };
+    using Full = std::false_type;
+    using Half = std::true_type;
     // ra holds the wave's chunk k, rb its chunk k + 1 (in flight or
     // landed).  The loop is entered only with rb's loads the newest, so the
-    // compiler's waits for ra never cover rb; an odd last chunk is peeled.
+    // compiler's waits for ra never cover rb.  An odd last full chunk and
+    // the half chunk are peeled.
     int64_t k = 0;
-    for (; k + 1 < wn; k += 2) {
-      run_chunk(k, ra);
-      run_chunk(k + 1, rb);
+    for (; k + 1 < n_full; k += 2) {
+      run_chunk(k, ra, Full{});
+      run_chunk(k + 1, rb, Full{});
     }
-    if (k < wn) run_chunk(k, ra);
+    if (k < n_full) {
+      run_chunk(k, ra, Full{});
+      if (last_half) run_chunk(k + 1, rb, Half{});
+    } else if (last_half) {
+      run_chunk(k, ra, Half{});
+    }
   }
   // ---- full-precision tokens of this split (sinks and the residual
   // window), one per wave in turn, folded into the same softmax state and

@@ -59,7 +59,12 @@ SMALL = [
     (1, 8, 2, 128, 4, 128, 0, 0, 1000, "f32"),
     (1, 4, 1, 128, 2, 128, 3, 128, 2999, "f16"),
     (3, 24, 3, 128, 4, 64, 4, 128, 4100, "bf16"),
-    (1, 32, 4, 128, 2, 32, 4, 32, 548, "bf16"),     # Q % 64 == 32
+    (1, 32, 4, 128, 2, 32, 4, 32, 580, "bf16"),     # Q % 64 == 32: a half chunk
+    (2, 16, 2, 64, 4, 32, 4, 32, 644, "f16"),       # half chunk, GQA 8
+    (1, 8, 1, 128, 2, 32, 0, 64, 480, "bf16"),      # half chunk, GQA 8, 2-bit
+    # 64 waves per KV head on a 256-CU part, 129 chunks: the wave with the
+    # half chunk has three chunks (the half one on the first register set)
+    (4, 32, 8, 128, 4, 32, 4, 32, 8260, "bf16"),
     (1, 64, 8, 128, 4, 64, 4, 128, 70000, "bf16"),
     # GQA 4 / 8 with nothing quantized yet (the VALU kernel takes these)
     (1, 8, 1, 128, 4, 64, 4, 128, 150, "bf16"),

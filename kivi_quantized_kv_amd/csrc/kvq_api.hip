@@ -332,6 +332,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     a.direct = direct ? 1 : 0;
     a.blocks_per_split = int(bps);
     a.fp_per_split = int(fp_per_split);
+    a.ml_offset = int64_t(B) * n_q_heads * n_split * D;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t ea = hipSuccess;
     if (a.n_split > 0) {

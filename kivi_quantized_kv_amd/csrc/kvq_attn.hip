@@ -522,84 +522,94 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
       dst[d] = o / L;
     }
   } else {
-    float* dst = a.ws + ((int64_t(b) * a.Hq + hq) * a.n_split + split) * (D + 2);
+    const int64_t row = int64_t(b) * a.Hq + hq;
+    float* dst = partial_o(a, row, split, D);
     for (int d = threadIdx.x; d < D; d += kThreads) {
       float o = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) o = __builtin_fmaf(f[w], s_out[w][d], o);
       dst[d] = o;
     }
-    if (threadIdx.x == 0) {
-      dst[D] = M;
-      dst[D + 1] = L;
-    }
+    if (threadIdx.x == 0) *reinterpret_cast<float2*>(partial_ml(a, row, split)) = float2{M, L};
   }
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials: one workgroup per (q head, batch).
-// M = max_j m_j, L = sum_j 2^(m_j - M) l_j, out = sum_j 2^(m_j - M) o_j / L.
-// Thread (sub, d) folds channel d of splits sub, sub + kSub, ... into its
-// own running (max, sums), loading up to kCh splits in one round; the kSub
-// subsets then meet through LDS.
+// Log-sum-exp merge of the split partials: M = max_j m_j,
+// L = sum_j 2^(m_j - M) l_j, out = sum_j 2^(m_j - M) o_j / L.
+// One workgroup per (32-channel block, q head, batch), one round of loads:
+// thread (slot, c4) folds channels [4 c4, 4 c4 + 4) of the block for
+// splits slot, slot + 32, ... (float4 loads) into a running state of its
+// own (local max, sums); the 32 slot states then meet through LDS by the
+// same rule.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_merge(AttnArgs a) {
-  constexpr int kSub = 256 / D;             // split subsets per channel
-  constexpr int kCh = 32;                   // splits per thread per load round
-  __shared__ float s_m[kSub], s_o[kSub][D], s_l[kSub];
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const int t = threadIdx.x, d = t % D, sub = t / D;
+  constexpr int kCW = 32;                   // channels per workgroup
+  constexpr int kQ = kCW / 4;               // float4 columns per split row
+  constexpr int kSlots = 256 / kQ;          // 32 split slots
+  constexpr int kPer = 4;                   // splits per slot per load round
+  __shared__ float s_m[kSlots], s_l[kSlots];
+  __shared__ float4 s_acc[kSlots][kQ];
+  const int cb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, c4 = t % kQ, slot = t / kQ;
   const int ns = a.n_split;
-  const float* src = a.ws + (int64_t(b) * a.Hq + hq) * ns * (D + 2);
-  float M = -__builtin_inff(), o = 0.f, L = 0.f;
-  for (int j0 = sub; j0 < ns; j0 += kSub * kCh) {
-    float mj[kCh], oj[kCh], lj[kCh];
+  const int64_t row = int64_t(b) * a.Hq + hq;
+  const float2* ml = reinterpret_cast<const float2*>(partial_ml(a, row, 0));
+  const float* ob = partial_o(a, row, 0, D) + cb * kCW + 4 * c4;
+  float M = -__builtin_inff(), L = 0.f;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = slot; j0 < ns; j0 += kSlots * kPer) {
+    float2 p[kPer];
+    float4 o[kPer];
 #pragma unroll
-    for (int i = 0; i < kCh; ++i) {
-      const int j = j0 + kSub * i;
+    for (int i = 0; i < kPer; ++i) {
+      const int j = j0 + kSlots * i;
       const int jj = j < ns ? j : ns - 1;   // in bounds; weight 0 below
-      const float* pj = src + int64_t(jj) * (D + 2);
-      mj[i] = j < ns ? pj[D] : -__builtin_inff();
-      oj[i] = pj[d];
-      lj[i] = pj[D + 1];
+      p[i] = ml[jj];
+      o[i] = *reinterpret_cast<const float4*>(ob + int64_t(jj) * D);
+      if (j >= ns) p[i].x = -__builtin_inff();
     }
-    float cm = mj[0];
+    float cm = p[0].x;
 #pragma unroll
-    for (int i = 1; i < kCh; ++i) cm = __builtin_fmaxf(cm, mj[i]);
+    for (int i = 1; i < kPer; ++i) cm = __builtin_fmaxf(cm, p[i].x);
     if (cm > M) {
       const float f = __builtin_amdgcn_exp2f(M - cm);   // 0 while M = -inf
-      o *= f;
+      acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
       L *= f;
       M = cm;
     }
     const float Mref = M == -__builtin_inff() ? 0.f : M;
 #pragma unroll
-    for (int i = 0; i < kCh; ++i) {
-      const float w = __builtin_amdgcn_exp2f(mj[i] - Mref);   // 0 for empty splits
-      o = __builtin_fmaf(w, oj[i], o);
-      L = __builtin_fmaf(w, lj[i], L);
+    for (int i = 0; i < kPer; ++i) {
+      const float w = __builtin_amdgcn_exp2f(p[i].x - Mref);   // 0 for empty splits
+      acc.x = __builtin_fmaf(w, o[i].x, acc.x);
+      acc.y = __builtin_fmaf(w, o[i].y, acc.y);
+      acc.z = __builtin_fmaf(w, o[i].z, acc.z);
+      acc.w = __builtin_fmaf(w, o[i].w, acc.w);
+      L = __builtin_fmaf(w, p[i].y, L);
     }
   }
-  s_o[sub][d] = o;
-  if (d == 0) {
-    s_m[sub] = M;
-    s_l[sub] = L;
+  s_acc[slot][c4] = acc;
+  if (c4 == 0) {
+    s_m[slot] = M;
+    s_l[slot] = L;
   }
   __syncthreads();
-  if (t < D) {
+  if (t < kCW) {
     float Mt = s_m[0];
 #pragma unroll
-    for (int k = 1; k < kSub; ++k) Mt = __builtin_fmaxf(Mt, s_m[k]);
+    for (int k = 1; k < kSlots; ++k) Mt = __builtin_fmaxf(Mt, s_m[k]);
     const float Mref = Mt == -__builtin_inff() ? 0.f : Mt;
-    float acc = 0.f, Lt = 0.f;
-#pragma unroll
-    for (int k = 0; k < kSub; ++k) {
+    float sum = 0.f, Lt = 0.f;
+    const int q = t / 4, e = t % 4;
+#pragma unroll 8
+    for (int k = 0; k < kSlots; ++k) {
       const float f = __builtin_amdgcn_exp2f(s_m[k] - Mref);
-      acc = __builtin_fmaf(f, s_o[k][t], acc);
+      sum = __builtin_fmaf(f, reinterpret_cast<const float*>(&s_acc[k][q])[e], sum);
       Lt = __builtin_fmaf(f, s_l[k], Lt);
     }
-    a.out[(int64_t(b) * a.Hq + hq) * D + t] = acc / Lt;
+    a.out[row * D + cb * kCW + t] = sum / Lt;
   }
 }
 
@@ -638,7 +648,7 @@ hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s) {
 }
 template <int DT, int D>
 hipError_t launch_merge(const AttnArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((k_merge<DT, D>), dim3(a.Hq, B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_merge<DT, D>), dim3(D / 32, a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

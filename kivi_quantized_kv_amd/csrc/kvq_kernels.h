@@ -41,8 +41,10 @@ struct AppendArgs {
   int H, G, flush;
 };
 
-// Decode attention.  Partials: ws[((b*Hq + hq)*n_split + split)*(D+2) + ...]
-// holds o (D floats, unnormalized), then m (log2 domain), then l.
+// Decode attention.  Split partials of row r = b*Hq + hq: o (D floats,
+// unnormalized) at ws[(r*n_split + split)*D], and the pair (m, l) (m in the
+// log2 domain) at ws[ml_offset + 2*(r*n_split + split)], with ml_offset =
+// B*Hq*n_split*D: the o rows stay 16-byte aligned for vector loads.
 struct AttnArgs {
   const uint8_t* k_codes;
   const uint8_t* v_codes;
@@ -62,7 +64,15 @@ struct AttnArgs {
   int blocks_per_split;     // value-code blocks per split (VALU kernel; the matrix-core
                             // kernel deals chunks to its waves in turn instead)
   int fp_per_split;         // full-precision tokens per split
+  int64_t ml_offset;        // floats before the (m, l) pairs in ws
 };
+
+__device__ __forceinline__ float* partial_o(const AttnArgs& a, int64_t row, int split, int D) {
+  return a.ws + (row * a.n_split + split) * D;
+}
+__device__ __forceinline__ float* partial_ml(const AttnArgs& a, int64_t row, int split) {
+  return a.ws + a.ml_offset + (row * a.n_split + split) * 2;
+}
 
 template <int DT, int D, int BITS>
 hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_groups, int B, int H, hipStream_t s);

@@ -312,7 +312,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       for (int i = 0; i < 4; ++i) vfk[i] = __builtin_amdgcn_ldexpf(field_scale<BITS>(i), kexp);
     };
     set_vfk();
-    const int vtok = (lane & 31) * 2;                // value deltas this lane checks
 
     u32x4_t qB[kKS];
 
@@ -342,8 +341,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       // that the largest delta seen sits in [2^6, 2^7); with p <= 2^8 the
       // value weights stay below 2^15
       {
-        const float2 dv = *reinterpret_cast<const float2*>(&vpb[wave][0][vtok]);
-        const float vmax = vtok < nv ? __builtin_fmaxf(dv.x, dv.y) : 0.0f;
+        // (lane t holds the delta of token t in a register)
+        const float vmax = lane < nv ? r.vd : 0.0f;
         const float vthr = __builtin_amdgcn_ldexpf(1.0f, 7 - kexp);
         if (__builtin_amdgcn_ballot_w64(vmax >= vthr) != 0) {
           const int knew = 7 - __builtin_amdgcn_frexp_expf(wave_max(vmax));
@@ -629,12 +628,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       o = __builtin_fmaf(f, s_o[w][qh][d] + s_z[w][qh], o);
       L = __builtin_fmaf(f, s_l[w][qh], L);
     }
-    float* dst = a.ws + ((int64_t(b) * a.Hq + h * GQA + qh) * a.n_split + split) * (D + 2);
-    dst[d] = o;
-    if (d == 0) {
-      dst[D] = M;
-      dst[D + 1] = L;
-    }
+    const int64_t row = int64_t(b) * a.Hq + h * GQA + qh;
+    partial_o(a, row, split, D)[d] = o;
+    if (d == 0) *reinterpret_cast<float2*>(partial_ml(a, row, split)) = float2{M, L};
   }
 }
 

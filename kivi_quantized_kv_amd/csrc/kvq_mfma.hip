@@ -149,28 +149,46 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* out) {
   }
 }
 
-// Registers of one 64-token chunk in flight: its code words, and its key
-// and value parameters, which go to wave-private LDS when the chunk comes
-// up (the weights read them as broadcasts).  Key parameters: per group,
-// lanes 0..31 hold delta and lanes 32..63 zero, D / 32 consecutive
-// channels each.  Value parameters: delta and zero of token lane.
-template <int D, int BITS, int NG>
+// Code registers of one 64-token chunk in flight.
+template <int D, int BITS>
 struct ChunkRegs {
   static constexpr int kQW = (D / 4) * BITS / 32;    // key words per lane per tile
   static constexpr int kNB = D / 16;                 // value words per lane per block
   static constexpr int kVB = 64 / VLayout<BITS>::L;  // value blocks per chunk
-  static constexpr int kPW = D / 32;                 // key parameter words per lane per group
   uint32_t kw[4][kQW];
   uint32_t vw[kVB][kNB];
-  uint32_t kp[NG][kPW];
-  float vd, vz;
 };
+
+// Asynchronous copy of 4 or 16 bytes per lane from global memory into LDS
+// (lane l's bytes land at lds + l * bytes, lds wave-uniform), counted by
+// vmcnt like a load.  Written as assembly so that the compiler, which
+// would otherwise hold every later LDS read behind the newest copy in
+// flight, leaves the ordering to the explicit waits of the caller; the
+// memory clobber keeps the copy in place relative to the wave's other
+// memory instructions.  M0 carries the LDS address, as the instruction
+// requires.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(const void* src, const void* lds) {
+  static_assert(BYTES == 4 || BYTES == 16, "copy size");
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(l) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(l) : "memory", "m0");
+}
+
+// s_waitcnt for the vector-memory counter only (expcnt and lgkmcnt left
+// at their maxima), N < 16.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 template <int DT, int D, int BITS, int GQA, bool G32>
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   using VLy = VLayout<BITS>;
-  constexpr int kNG = G32 ? 2 : 1;         // key groups per chunk
-  using CR = ChunkRegs<D, BITS, kNG>;
+  using CR = ChunkRegs<D, BITS>;
   constexpr int kRB = D * BITS / 8;        // bytes per key row
   constexpr int kQCH = D / 4;              // channels of a lane's quarter row
   constexpr int kCPW = 32 / BITS;          // codes per 32-bit word
@@ -178,16 +196,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int kKS = D / 32;              // K-steps of q.K^T
   constexpr int kNB = CR::kNB;
   constexpr int kVB = CR::kVB;
+  constexpr int kNG = G32 ? 2 : 1;         // key groups per chunk
   constexpr int kStepsPerWord = kCPW / 8;  // K-steps covered by one code word
   constexpr int kJoin = GQA == 8 ? kRowRor8 : kRowRor4;   // high <-> low column
   constexpr float kS = 16777216.0f;        // 2^24: unit of a subnormal code field
   constexpr float kSlack = 8.0f;           // running max kept within 2^8 of the true one
   constexpr int kNoScale = 100;            // value exponent before any scale is seen
-  constexpr int kPW = CR::kPW;
+  // vector-memory instructions per chunk batch: code loads, then the
+  // parameter copies (key groups: one 16-byte copy per group at D = 128,
+  // two 4-byte copies at D = 64; values: delta and zero, 4 bytes each)
+  constexpr int kCodeLoads = 4 * ((kQW * 4 + 15) / 16) + kVB * ((kNB * 4 + 15) / 16);
+  constexpr int kBatch = kCodeLoads + kNG * (D == 128 ? 1 : 2) + 2;
+  static_assert(kBatch < 16, "batch must fit the vmcnt field");
   static_assert(D == 64 || D == 128, "head_dim");
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = int64_t(b) * a.H + h;
+  // the wave index is uniform: kept in a scalar register, it makes the LDS
+  // copy destinations scalar as the copy instructions require
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, lg = lane >> 4;
   const int hh = col % GQA;                          // head of this column
@@ -198,9 +224,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   __shared__ float s_qf[GQA][D + 4];   // the same times each channel's field scale
   __shared__ float s_o[4][GQA][D];
   __shared__ float s_m[4][GQA], s_l[4][GQA], s_z[4][GQA];
-  // wave-private parameters of the chunk being processed
-  __shared__ float4 s_kp[4][kNG][2 * D / 4];   // [wave][group][delta | zero]
-  __shared__ float s_vp[4][2][64];             // [wave][delta | zero][token]
+  // wave-private parameter buffers of the chunks at even / odd positions
+  // of the wave's run, filled by LDS copies.  Two separate arrays, so that
+  // the compiler, which orders reads of an array after the copies in flight
+  // into it, does not hold the reads of one buffer behind the other's copies.
+  __shared__ float4 s_kp0[4][2][2 * D / 4], s_kp1[4][2][2 * D / 4];   // [wave][group][delta | zero]
+  __shared__ float s_vp0[4][2][64], s_vp1[4][2][64];                  // [wave][delta | zero][token]
 
   // this wave's chunks: gw, gw + nw_row, ... (none for waves past the
   // chunk count, whose splits only take exact tokens)
@@ -216,13 +245,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const float* kz_head = a.k_zero + bh * a.kgroups * D;
   const int gsh = a.g_shift;
 
-  // Issue the loads of chunk ch into r: its code words, then its key and
-  // value parameters.  Every address lies inside the allocation (qcap >=
-  // 64 * ceil(Q / 64) tokens, qcap / G key groups); whatever lies past the
-  // quantized range is masked later.  All of them are ordinary loads, so
-  // the compiler's own waits before each use hold the wave only for the
-  // loads of the chunk it is processing, never for the next one's.
-  auto issue_batch = [&](int64_t ch, CR& r) {
+  // Issue the batch of chunk ch: its code words into r, then its key and
+  // value parameters into parameter buffer ch & 1.  Every address lies
+  // inside the allocation (qcap >= 64 * ceil(Q / 64) tokens, qcap / G key
+  // groups); whatever lies past the quantized range is skipped or masked
+  // later.  The instruction count is fixed (kBatch), so waiting for
+  // vmcnt <= kBatch completes every batch but the last one issued.
+  auto issue_batch = [&](int64_t ch, CR& r, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
+    auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
     const int64_t base = ch << 6;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -232,41 +264,43 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     for (int vb = 0; vb < kVB; ++vb)
       load_words<kNB>(vc_head + (base / VLy::L + vb) * (VLy::L * kRB) + (lg * 16 + col) * kNB * 4,
                       r.vw[vb]);
+    __builtin_amdgcn_sched_barrier(0);
     const int64_t g0 = base >> gsh;
 #pragma unroll
     for (int gi = 0; gi < kNG; ++gi) {
-      const float* src = (lane < 32 ? ks_head : kz_head) + (g0 + gi) * D + (lane & 31) * kPW;
-      load_words<kPW>(reinterpret_cast<const uint8_t*>(src), r.kp[gi]);
+      float* dst = reinterpret_cast<float*>(&kpb[wave][gi][0]);
+      if constexpr (D == 128) {
+        // lanes 0..31: delta[4l..4l+3], lanes 32..63: zero[4(l-32)..]
+        const float* src = (lane < 32 ? ks_head : kz_head) + (g0 + gi) * D + (lane & 31) * 4;
+        copy_to_lds<16>(src, dst);
+      } else {
+        copy_to_lds<4>(ks_head + (g0 + gi) * D + lane, dst);
+        copy_to_lds<4>(kz_head + (g0 + gi) * D + lane, dst + D);
+      }
     }
-    r.vd = vs_head[base + lane];
-    r.vz = vz_head[base + lane];
+    copy_to_lds<4>(vs_head + base + lane, &vpb[wave][0][0]);
+    copy_to_lds<4>(vz_head + base + lane, &vpb[wave][1][0]);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // q first (its loads complete before the chunk loads), then the first
-  // two chunks' loads, then q into LDS
+  // q first (its loads complete before the chunk batches), then the first
+  // two batches, then q into LDS
   constexpr int kQPer = GQA * D / 256;
-  using QE = typename Elem<DT>::T;
-  QE qraw[kQPer];                                  // widened after the chunk loads are issued
+  float qv[kQPer];
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
     const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
-    qraw[j] = reinterpret_cast<const QE*>(a.q)[b * a.q_sb + (h * GQA + qh) * a.q_sh + d];
+    qv[j] = load1<DT>(a.q, b * a.q_sb + (h * GQA + qh) * a.q_sh + d);
   }
-  // The first two chunks' loads, on every wave (a wave without chunks
-  // re-reads chunk 0, which exists: the kernel runs only with Q > 0), so
-  // that no branch separates them from their uses.
   CR ra, rb;
-  issue_batch(wn > 0 ? gw : 0, ra);
-  issue_batch(wn > 1 ? gw + nw_row : 0, rb);
+  if (wn > 0) {
+    issue_batch(gw, ra, std::integral_constant<int, 0>{});
+    issue_batch(wn > 1 ? gw + nw_row : 0, rb, std::integral_constant<int, 1>{});
+  }
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
     const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
-    float qf;
-    if constexpr (DT == DT_F32) qf = qraw[j];
-    else if constexpr (DT == DT_F16) qf = f16_bits_to_f32(qraw[j]);
-    else qf = bf16_bits_to_f32(qraw[j]);
-    const float v = qf * a.sm_scale_log2;
+    const float v = qv[j] * a.sm_scale_log2;
     s_q[qh][d] = v;
     s_qf[qh][d] = v * field_scale<BITS>(d);
   }
@@ -303,7 +337,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     }
   };
 
-  if (wn > 0) {
+  {
     // ------------------------------------------------------------ quantized
     // value field scales of rows i (token 4g + i of a tile) times 2^kexp
     float vfk[4];
@@ -312,37 +346,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       for (int i = 0; i < 4; ++i) vfk[i] = __builtin_amdgcn_ldexpf(field_scale<BITS>(i), kexp);
     };
     set_vfk();
+    const int vtok = (lane & 31) * 2;                // value deltas this lane checks
 
     u32x4_t qB[kKS];
 
     // A half chunk (only ever the last of the quantized range) holds 32
     // tokens: tiles 0 and 1, the first 32-token step of P.V.
-    auto process_chunk = [&](const CR& r, auto half_tag) {
+    auto process_chunk = [&](const CR& r, auto half_tag, auto buf_tag) {
       constexpr bool HALF = decltype(half_tag)::value;
       constexpr int kTiles = HALF ? 2 : 4;
-      const auto& kpb = s_kp;
-      const auto& vpb = s_vp;
+      constexpr int BUF = decltype(buf_tag)::value;
+      const auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
+      const auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
       constexpr int nv = HALF ? 32 : 64;
       constexpr int kSegTiles = G32 ? 2 : 4;
-      // the chunk's parameters into the wave's LDS buffer (the wave's reads
-      // of the previous chunk's were issued before, and LDS keeps a wave's
-      // accesses in order)
-#pragma unroll
-      for (int gi = 0; gi < kNG; ++gi) {
-        uint8_t* dst = reinterpret_cast<uint8_t*>(&s_kp[wave][gi][0]) + lane * (kPW * 4);
-        if constexpr (kPW == 4)
-          *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{r.kp[gi][0], r.kp[gi][1], r.kp[gi][2], r.kp[gi][3]};
-        else
-          *reinterpret_cast<uint2*>(dst) = uint2{r.kp[gi][0], r.kp[gi][1]};
-      }
-      s_vp[wave][0][lane] = r.vd;
-      s_vp[wave][1][lane] = r.vz;
+      // this chunk's batch is complete once at most the next one is in flight
+      wait_vmcnt<kBatch>();
       // ---- value scale: a delta at or above 2^(7-kexp) lowers kexp so
       // that the largest delta seen sits in [2^6, 2^7); with p <= 2^8 the
       // value weights stay below 2^15
       {
-        // (lane t holds the delta of token t in a register)
-        const float vmax = lane < nv ? r.vd : 0.0f;
+        const float2 dv = *reinterpret_cast<const float2*>(&vpb[wave][0][vtok]);
+        const float vmax = vtok < nv ? __builtin_fmaxf(dv.x, dv.y) : 0.0f;
         const float vthr = __builtin_amdgcn_ldexpf(1.0f, 7 - kexp);
         if (__builtin_amdgcn_ballot_w64(vmax >= vthr) != 0) {
           const int knew = 7 - __builtin_amdgcn_frexp_expf(wave_max(vmax));
@@ -442,9 +467,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         for (int i = 0; i < 4; ++i) cm_seg[t / kSegTiles] = __builtin_fmaxf(cm_seg[t / kSegTiles], sc[t][i]);
       float cm = __builtin_fmaf(cm_seg[0], kS, kap[0]);
       if constexpr (G32 && !HALF) cm = __builtin_fmaxf(cm, __builtin_fmaf(cm_seg[1], kS, kap[1]));
-      cm = max_xor16(cm);
-      cm = max_xor32(cm);
-      raise_max(cm);
+      // the head's max over lanes is only needed when the running max
+      // moves: any lane over m + slack means its head's max is
+      if (__builtin_amdgcn_ballot_w64(cm > m + kSlack) != 0) {
+        cm = max_xor16(cm);
+        cm = max_xor32(cm);
+        raise_max(cm);
+      }
       const float km0 = kap[0] - m, km1 = kap[1] - m;
       // ---- P.V per 32-token step (tiles 2ps, 2ps+1).  A high column and
       // its low partner (GQA lanes apart in the row) hold the same scores:
@@ -496,34 +525,38 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // only the wave whose run ends on it has one
     const bool last_half = (a.Q & 63) != 0 && gw + (wn - 1) * nw_row == nch - 1;
     const int64_t n_full = wn - (last_half ? 1 : 0);
-    // After a chunk its registers are free: start the loads of the wave's
-    // chunk after next.  Past the wave's last chunk the loads re-read chunk
-    // 0 of this (b, h) (valid: the wave has a chunk, so Q > 0), which every
-    // wave shares and the L2 mostly serves.  Loads are issued on every path,
-    // never under a branch: the compiler counts outstanding loads along
-    // the control flow, and a path that skipped a batch would make it wait
-    // for all of them.
-    auto run_chunk = [&](int64_t k, CR& r, auto half_tag) {
-      process_chunk(r, half_tag);
-      issue_batch(k + 2 < wn ? gw + (k + 2) * nw_row : 0, r);
+    // After a chunk, its registers and parameter buffer are free: start
+    // the batch of the wave's chunk after next.  Past the wave's last chunk
+    // the batch re-reads chunk 0 of this (b, h), which every wave shares and
+    // which is mostly served by the L2, so that a batch always follows each
+    // chunk (the counter waits assume it).  The copies into the buffer are
+    // ordered after this wave's reads of it by the wait on the LDS counter.
+    auto run_chunk = [&](int64_t k, CR& r, auto half_tag, auto buf_tag) {
+      process_chunk(r, half_tag, buf_tag);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      issue_batch(k + 2 < wn ? gw + (k + 2) * nw_row : 0, r, buf_tag);
     };
     using Full = std::false_type;
     using Half = std::true_type;
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
     // ra holds the wave's chunk k, rb its chunk k + 1 (in flight or
-    // landed).  The loop is entered only with rb's loads the newest, so the
-    // compiler's waits for ra never cover rb.  An odd last full chunk and
-    // the half chunk are peeled.
+    // landed).  The loop is entered only with rb's batch the newest, so the
+    // compiler's own waits for ra's registers never reach far into rb's;
+    // an odd last full chunk and the half chunk are peeled.
     int64_t k = 0;
     for (; k + 1 < n_full; k += 2) {
-      run_chunk(k, ra, Full{});
-      run_chunk(k + 1, rb, Full{});
+      run_chunk(k, ra, Full{}, B0{});
+      run_chunk(k + 1, rb, Full{}, B1{});
     }
     if (k < n_full) {
-      run_chunk(k, ra, Full{});
-      if (last_half) run_chunk(k + 1, rb, Half{});
+      run_chunk(k, ra, Full{}, B0{});
+      if (last_half) run_chunk(k + 1, rb, Half{}, B1{});
     } else if (last_half) {
-      run_chunk(k, ra, Half{});
+      run_chunk(k, ra, Half{}, B0{});
     }
+    // let every copy land before the buffers are left behind
+    wait_vmcnt<0>();
   }
   // ---- full-precision tokens of this split (sinks and the residual
   // window), one per wave in turn, folded into the same softmax state and

@@ -42,7 +42,11 @@
 // of its chunks the codes of its next one are already in flight into
 // registers (non-temporal loads: read once, not kept in the caches), and so
 // are its key/value parameters, which are staged through wave-private LDS
-// (broadcast reads) when the chunk comes up.
+// (broadcast reads) when the chunk comes up.  The sink and residual tokens
+// of a split are spread over its waves; each wave loads its first one
+// before the chunk batches and folds it in, in a softmax state of its own,
+// while the batches are in flight.  The workgroup merge joins the four
+// waves' quantized states and their exact-token states.
 //
 // MFMA operand layout (16x16x32, 64 lanes): lane l holds A[row l%16][k in
 // group l/16] and B[k in group l/16][col l%16] (8 values each, the same
@@ -224,6 +228,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   __shared__ float s_qf[GQA][D + 4];   // the same times each channel's field scale
   __shared__ float s_o[4][GQA][D];
   __shared__ float s_m[4][GQA], s_l[4][GQA], s_z[4][GQA];
+  __shared__ float s_of[4][GQA][D];                  // each wave's exact-token partial
+  __shared__ float s_mf[4][GQA], s_lf[4][GQA];
   // wave-private parameter buffers of the chunks at even / odd positions
   // of the wave's run, filled by LDS copies.  Two separate arrays, so that
   // the compiler, which orders reads of an array after the copies in flight
@@ -286,21 +292,62 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   // q first (its loads complete before the chunk batches), then the first
   // two batches, then q into LDS
   constexpr int kQPer = GQA * D / 256;
-  float qv[kQPer];
+  using QE = typename Elem<DT>::T;
+  QE qraw[kQPer];                                  // widened after the batches are issued
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
     const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
-    qv[j] = load1<DT>(a.q, b * a.q_sb + (h * GQA + qh) * a.q_sh + d);
+    qraw[j] = reinterpret_cast<const QE*>(a.q)[b * a.q_sb + (h * GQA + qh) * a.q_sh + d];
+  }
+  // The first two batches, on every wave: a wave without chunks re-reads
+  // chunk 0, which exists (the kernel runs only with Q > 0).  Under a branch
+  // they would make the compiler's wait for q below cover both batches.
+  // This wave's exact tokens (sinks and the residual window): f0 + wave,
+  // f0 + wave + 4, ... below f1.  The first one's rows are loaded before
+  // the chunk batches, so that they land first and are folded in while the
+  // batches are in flight.
+  const int64_t f0 = int64_t(split) * a.fp_per_split;
+  const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
+  auto fp_row = [&](int64_t i, const void*& kb, const void*& vb, int64_t& off) {
+    if (i < a.n_sink) {
+      kb = a.k_sink; vb = a.v_sink; off = (bh * a.S + i) * D;
+    } else {
+      int64_t slot = a.resid_slot0 + (i - a.n_sink);   // < 2 * ring
+      if (slot >= a.ring) slot -= a.ring;
+      kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + slot) * D;
+    }
+  };
+  // first exact token, raw bits (widened after the batches are issued):
+  // key quarter row, values
+  using KR = std::conditional_t<DT == DT_F32, float4, uint2>;
+  KR fkr[kQCH / 4];
+  uint32_t fvr[kNB];                                 // one 32-bit register per value (no packing)
+  const bool has_fp = f0 + wave < f1;
+  if (has_fp) {
+    const void* kb;
+    const void* vb;
+    int64_t off;
+    fp_row(f0 + wave, kb, vb, off);
+#pragma unroll
+    for (int c = 0; c < kQCH; c += 4)
+      fkr[c / 4] = *reinterpret_cast<const KR*>(reinterpret_cast<const QE*>(kb) + off + lg * kQCH + c);
+#pragma unroll
+    for (int n = 0; n < kNB; ++n) {
+      if constexpr (DT == DT_F32) fvr[n] = reinterpret_cast<const uint32_t*>(vb)[off + 16 * n + col];
+      else fvr[n] = reinterpret_cast<const QE*>(vb)[off + 16 * n + col];
+    }
   }
   CR ra, rb;
-  if (wn > 0) {
-    issue_batch(gw, ra, std::integral_constant<int, 0>{});
-    issue_batch(wn > 1 ? gw + nw_row : 0, rb, std::integral_constant<int, 1>{});
-  }
+  issue_batch(wn > 0 ? gw : 0, ra, std::integral_constant<int, 0>{});
+  issue_batch(wn > 1 ? gw + nw_row : 0, rb, std::integral_constant<int, 1>{});
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
     const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
-    const float v = qv[j] * a.sm_scale_log2;
+    float qf;
+    if constexpr (DT == DT_F32) qf = qraw[j];
+    else if constexpr (DT == DT_F16) qf = f16_bits_to_f32(qraw[j]);
+    else qf = bf16_bits_to_f32(qraw[j]);
+    const float v = qf * a.sm_scale_log2;
     s_q[qh][d] = v;
     s_qf[qh][d] = v * field_scale<BITS>(d);
   }
@@ -336,6 +383,119 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       m = new_m;
     }
   };
+
+  // Wave state into LDS: l and z reduced over the owner columns' lane
+  // groups, the high and low rows joined, o in real units (acc times unit).
+  auto stash = [&](float (*so)[D], float* sm, float* sl, float* sz, float unit) {
+    float lr = l + dpp_rot<kJoin>(l);     // owner (even tiles or exact tokens) + partner (odd tiles)
+    float zr = z + dpp_rot<kJoin>(z);
+    if (!owner) {
+      lr = 0.f;
+      zr = 0.f;
+    }
+    lr = sum_xor32(sum_xor16(lr));
+    zr = sum_xor32(sum_xor16(zr));
+    if (lane < GQA) {
+      sm[lane] = m;
+      sl[lane] = lr;
+      if (sz) sz[lane] = zr;
+    }
+#pragma unroll
+    for (int n = 0; n < kNB; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[n][i];
+        if constexpr (GQA == 8) v = sum_xor32(v);    // rows r and r + 8
+        else v = sum_xor16(v);                       // rows r and r + 4
+        const int row = 4 * lg + i;
+        if (row < GQA) so[row][n * 16 + col] = v * unit;
+      }
+    }
+  };
+
+  // ---- exact tokens first, in a softmax state of their own (scores as
+  // fp32 dot products, values added to the high rows in real units); it
+  // goes to LDS and meets the quantized state in the workgroup merge.
+  {
+    auto fold_fp = [&](const float* kq, const float* vv) {
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < kQCH; c += 4) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&s_q[hh][lg * kQCH + c]);
+        part = __builtin_fmaf(kq[c], q4.x, part);
+        part = __builtin_fmaf(kq[c + 1], q4.y, part);
+        part = __builtin_fmaf(kq[c + 2], q4.z, part);
+        part = __builtin_fmaf(kq[c + 3], q4.w, part);
+      }
+      part = sum_xor16(part);
+      const float sc = sum_xor32(part);             // score of head hh
+      raise_max(sc);
+      const float p = __builtin_amdgcn_exp2f(sc - m);
+      if (lg == 0 && !is_lo) l += p;                // one lane group of the high columns
+      float pr[4];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                      ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, p)));
+        pr[i2] = (4 * lg + i2) < GQA ? v : 0.f;     // high rows only
+      }
+#pragma unroll
+      for (int n = 0; n < kNB; ++n)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] = __builtin_fmaf(pr[i2], vv[n], acc[n][i2]);
+    };
+    if (has_fp) {
+      // keep the widening here, after the batches were issued
+#pragma unroll
+      for (int n = 0; n < kNB; ++n) asm volatile("" : "+v"(fvr[n]));
+#pragma unroll
+      for (int c = 0; c < kQCH / 4; ++c) {
+        if constexpr (DT == DT_F32) {
+          asm volatile("" : "+v"(fkr[c].x), "+v"(fkr[c].y), "+v"(fkr[c].z), "+v"(fkr[c].w));
+        } else {
+          asm volatile("" : "+v"(fkr[c].x), "+v"(fkr[c].y));
+        }
+      }
+      float fk[kQCH], fv[kNB];
+      auto widen1 = [](uint32_t r) -> float {
+        if constexpr (DT == DT_F16) return f16_bits_to_f32(r);
+        else return bf16_bits_to_f32(r);
+      };
+#pragma unroll
+      for (int c = 0; c < kQCH; c += 4) {
+        if constexpr (DT == DT_F32) {
+          fk[c] = fkr[c / 4].x; fk[c + 1] = fkr[c / 4].y; fk[c + 2] = fkr[c / 4].z; fk[c + 3] = fkr[c / 4].w;
+        } else {
+          fk[c] = widen1(fkr[c / 4].x & 0xFFFFu); fk[c + 1] = widen1(fkr[c / 4].x >> 16);
+          fk[c + 2] = widen1(fkr[c / 4].y & 0xFFFFu); fk[c + 3] = widen1(fkr[c / 4].y >> 16);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < kNB; ++n) {
+        if constexpr (DT == DT_F32) fv[n] = __builtin_bit_cast(float, fvr[n]);
+        else fv[n] = widen1(fvr[n]);
+      }
+      fold_fp(fk, fv);
+      for (int64_t i = f0 + wave + 4; i < f1; i += 4) {
+        const void* kb;
+        const void* vb;
+        int64_t off;
+        fp_row(i, kb, vb, off);
+        float kq[kQCH], vv[kNB];
+#pragma unroll
+        for (int c = 0; c < kQCH; c += 4) load4<DT>(kb, off + lg * kQCH + c, &kq[c]);
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) vv[n] = load1<DT>(vb, off + 16 * n + col);
+        fold_fp(kq, vv);
+      }
+    }
+    stash(s_of[wave], s_mf[wave], s_lf[wave], nullptr, 1.0f);
+#pragma unroll
+    for (int n = 0; n < kNB; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = -__builtin_inff();
+    l = 0.f;
+    z = 0.f;
+  }
 
   {
     // ------------------------------------------------------------ quantized
@@ -558,93 +718,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // let every copy land before the buffers are left behind
     wait_vmcnt<0>();
   }
-  // ---- full-precision tokens of this split (sinks and the residual
-  // window), one per wave in turn, folded into the same softmax state and
-  // accumulator rows: scores as fp32 dot products, values added to the
-  // high rows in the accumulator's unit 2^(kexp-24).
-  {
-    if (kexp > 24) {
-      const float f = __builtin_amdgcn_ldexpf(1.0f, 24 - kexp);
-#pragma unroll
-      for (int n = 0; n < kNB; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[n][i] *= f;
-      kexp = 24;
-    }
-    const float fp_unit = __builtin_amdgcn_ldexpf(1.0f, kexp - 24);
-    const int64_t f0 = int64_t(split) * a.fp_per_split;
-    const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
-    for (int64_t i = f0 + wave; i < f1; i += 4) {
-      const void* kb;
-      const void* vb;
-      int64_t off;
-      if (i < a.n_sink) {
-        kb = a.k_sink; vb = a.v_sink; off = (bh * a.S + i) * D;
-      } else {
-        int64_t slot = a.resid_slot0 + (i - a.n_sink);   // < 2 * ring
-        if (slot >= a.ring) slot -= a.ring;
-        kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + slot) * D;
-      }
-      float part = 0.f;
-#pragma unroll
-      for (int c = 0; c < kQCH; c += 4) {
-        float k4[4];
-        load4<DT>(kb, off + lg * kQCH + c, k4);
-        const float4 q4 = *reinterpret_cast<const float4*>(&s_q[hh][lg * kQCH + c]);
-        part = __builtin_fmaf(k4[0], q4.x, part);
-        part = __builtin_fmaf(k4[1], q4.y, part);
-        part = __builtin_fmaf(k4[2], q4.z, part);
-        part = __builtin_fmaf(k4[3], q4.w, part);
-      }
-      part = sum_xor16(part);
-      const float sc = sum_xor32(part);             // score of head hh
-      raise_max(sc);
-      const float p = __builtin_amdgcn_exp2f(sc - m);
-      if (lg == 0 && !is_lo) l += p;                // one lane group of the high columns
-      float pr[4];
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                      ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, p)));
-        pr[i2] = (4 * lg + i2) < GQA ? v * fp_unit : 0.f;   // high rows only
-      }
-#pragma unroll
-      for (int n = 0; n < kNB; ++n) {
-        const float v = load1<DT>(vb, off + 16 * n + col);
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] = __builtin_fmaf(pr[i2], v, acc[n][i2]);
-      }
-    }
-  }
-  // ---- wave result: join high and low rows (in real units), reduce l and
-  // z over the lane groups of the owner columns
-  {
-    l += dpp_rot<kJoin>(l);            // owner (even tiles, exact tokens) + partner (odd tiles)
-    z += dpp_rot<kJoin>(z);
-    if (!owner) {
-      l = 0.f;
-      z = 0.f;
-    }
-    l = sum_xor32(sum_xor16(l));
-    z = sum_xor32(sum_xor16(z));
-    if (lane < GQA) {
-      s_m[wave][lane] = m;
-      s_l[wave][lane] = l;
-      s_z[wave][lane] = z;
-    }
-    const float unit = __builtin_amdgcn_ldexpf(1.0f, 24 - kexp);
-#pragma unroll
-    for (int n = 0; n < kNB; ++n) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = acc[n][i];
-        if constexpr (GQA == 8) v = sum_xor32(v);    // rows r and r + 8
-        else v = sum_xor16(v);                       // rows r and r + 4
-        const int row = 4 * lg + i;
-        if (row < GQA) s_o[wave][row][n * 16 + col] = v * unit;
-      }
-    }
-  }
+  // ---- wave result
+  stash(s_o[wave], s_m[wave], s_l[wave], s_z[wave], __builtin_amdgcn_ldexpf(1.0f, 24 - kexp));
   __syncthreads();
   // ---- merge the four waves; write this split's partial for each head
   for (int x = threadIdx.x; x < GQA * D; x += 256) {
@@ -652,6 +727,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     float M = s_m[0][qh];
 #pragma unroll
     for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, s_m[w][qh]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, s_mf[w][qh]);
     // a split with no tokens at all leaves m = -inf, l = 0, o = 0
     const float Mref = M == -__builtin_inff() ? 0.f : M;
     float o = 0.f, L = 0.f;
@@ -660,6 +737,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const float f = __builtin_amdgcn_exp2f(s_m[w][qh] - Mref);
       o = __builtin_fmaf(f, s_o[w][qh][d] + s_z[w][qh], o);
       L = __builtin_fmaf(f, s_l[w][qh], L);
+      const float g = __builtin_amdgcn_exp2f(s_mf[w][qh] - Mref);
+      o = __builtin_fmaf(g, s_of[w][qh][d], o);
+      L = __builtin_fmaf(g, s_lf[w][qh], L);
     }
     const int64_t row = int64_t(b) * a.Hq + h * GQA + qh;
     partial_o(a, row, split, D)[d] = o;

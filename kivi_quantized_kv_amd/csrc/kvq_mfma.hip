@@ -257,18 +257,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   // groups); whatever lies past the quantized range is skipped or masked
   // later.  The instruction count is fixed (kBatch), so waiting for
   // vmcnt <= kBatch completes every batch but the last one issued.
-  auto issue_batch = [&](int64_t ch, CR& r, auto buf_tag) {
+  // A batch that is not live (past the wave's last chunk) keeps the same
+  // instructions, with every lane of each on the same 16 bytes of chunk 0:
+  // one cache line per instruction.
+  auto issue_batch = [&](int64_t ch, bool live, CR& r, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
     auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
-    const int64_t base = ch << 6;
+    const int64_t base = live ? ch << 6 : 0;
+    const int cl = live ? col : 0, lgl = live ? lg : 0, ll = live ? lane : 0;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      load_words<kQW>(kc_head + (base + 16 * t + col) * kRB + lg * (kQW * 4), r.kw[t]);
+      load_words<kQW>(kc_head + (base + 16 * t + cl) * kRB + lgl * (kQW * 4), r.kw[t]);
 #pragma unroll
     for (int vb = 0; vb < kVB; ++vb)
-      load_words<kNB>(vc_head + (base / VLy::L + vb) * (VLy::L * kRB) + (lg * 16 + col) * kNB * 4,
+      load_words<kNB>(vc_head + (base / VLy::L + vb) * (VLy::L * kRB) + (lgl * 16 + cl) * kNB * 4,
                       r.vw[vb]);
     __builtin_amdgcn_sched_barrier(0);
     const int64_t g0 = base >> gsh;
@@ -277,15 +281,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       float* dst = reinterpret_cast<float*>(&kpb[wave][gi][0]);
       if constexpr (D == 128) {
         // lanes 0..31: delta[4l..4l+3], lanes 32..63: zero[4(l-32)..]
-        const float* src = (lane < 32 ? ks_head : kz_head) + (g0 + gi) * D + (lane & 31) * 4;
+        const float* src = (lane < 32 ? ks_head : kz_head) + (g0 + gi) * D + (ll & 31) * 4;
         copy_to_lds<16>(src, dst);
       } else {
-        copy_to_lds<4>(ks_head + (g0 + gi) * D + lane, dst);
-        copy_to_lds<4>(kz_head + (g0 + gi) * D + lane, dst + D);
+        copy_to_lds<4>(ks_head + (g0 + gi) * D + ll, dst);
+        copy_to_lds<4>(kz_head + (g0 + gi) * D + ll, dst + D);
       }
     }
-    copy_to_lds<4>(vs_head + base + lane, &vpb[wave][0][0]);
-    copy_to_lds<4>(vz_head + base + lane, &vpb[wave][1][0]);
+    copy_to_lds<4>(vs_head + base + ll, &vpb[wave][0][0]);
+    copy_to_lds<4>(vz_head + base + ll, &vpb[wave][1][0]);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -338,8 +342,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     }
   }
   CR ra, rb;
-  issue_batch(wn > 0 ? gw : 0, ra, std::integral_constant<int, 0>{});
-  issue_batch(wn > 1 ? gw + nw_row : 0, rb, std::integral_constant<int, 1>{});
+  issue_batch(gw, wn > 0, ra, std::integral_constant<int, 0>{});
+  issue_batch(gw + nw_row, wn > 1, rb, std::integral_constant<int, 1>{});
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
     const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
@@ -694,7 +698,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     auto run_chunk = [&](int64_t k, CR& r, auto half_tag, auto buf_tag) {
       process_chunk(r, half_tag, buf_tag);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      issue_batch(k + 2 < wn ? gw + (k + 2) * nw_row : 0, r, buf_tag);
+      issue_batch(gw + (k + 2) * nw_row, k + 2 < wn, r, buf_tag);
     };
     using Full = std::false_type;
     using Half = std::true_type;

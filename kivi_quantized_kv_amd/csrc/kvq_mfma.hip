@@ -528,22 +528,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       wait_vmcnt<kBatch>();
       // ---- value scale: a delta at or above 2^(7-kexp) lowers kexp so
       // that the largest delta seen sits in [2^6, 2^7); with p <= 2^8 the
-      // value weights stay below 2^15
-      {
-        const float2 dv = *reinterpret_cast<const float2*>(&vpb[wave][0][vtok]);
-        const float vmax = vtok < nv ? __builtin_fmaxf(dv.x, dv.y) : 0.0f;
-        const float vthr = __builtin_amdgcn_ldexpf(1.0f, 7 - kexp);
-        if (__builtin_amdgcn_ballot_w64(vmax >= vthr) != 0) {
-          const int knew = 7 - __builtin_amdgcn_frexp_expf(wave_max(vmax));
-          const float f = __builtin_amdgcn_ldexpf(1.0f, knew - kexp);
-#pragma unroll
-          for (int n = 0; n < kNB; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[n][i] *= f;
-          kexp = knew;
-          set_vfk();
-        }
-      }
+      // value weights stay below 2^15.  Checked here, acted on (rarely)
+      // together with the running max before P.V, so that one branch per
+      // chunk splits its instruction stream.
+      const float2 dv = *reinterpret_cast<const float2*>(&vpb[wave][0][vtok]);
+      const float vmax = vtok < nv ? __builtin_fmaxf(dv.x, dv.y) : 0.0f;
+      const bool v_over = vmax >= __builtin_amdgcn_ldexpf(1.0f, 7 - kexp);
       // ---- q.K^T: per key-group segment, K-steps outer, tiles inner
       f32x4_t sc[4];
       float kap[2] = {0.f, 0.f};               // kappa of each segment's group
@@ -633,10 +623,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       if constexpr (G32 && !HALF) cm = __builtin_fmaxf(cm, __builtin_fmaf(cm_seg[1], kS, kap[1]));
       // the head's max over lanes is only needed when the running max
       // moves: any lane over m + slack means its head's max is
-      if (__builtin_amdgcn_ballot_w64(cm > m + kSlack) != 0) {
-        cm = max_xor16(cm);
-        cm = max_xor32(cm);
-        raise_max(cm);
+      const uint64_t need_v = __builtin_amdgcn_ballot_w64(v_over);
+      const uint64_t need_m = __builtin_amdgcn_ballot_w64(cm > m + kSlack);
+      if ((need_v | need_m) != 0) {
+        if (need_v != 0) {
+          const int knew = 7 - __builtin_amdgcn_frexp_expf(wave_max(vmax));
+          const float f = __builtin_amdgcn_ldexpf(1.0f, knew - kexp);
+#pragma unroll
+          for (int n = 0; n < kNB; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[n][i] *= f;
+          kexp = knew;
+          set_vfk();
+        }
+        if (need_m != 0) {
+          cm = max_xor16(cm);
+          cm = max_xor32(cm);
+          raise_max(cm);
+        }
       }
       const float km0 = kap[0] - m, km1 = kap[1] - m;
       // ---- P.V per 32-token step (tiles 2ps, 2ps+1).  A high column and

@@ -729,9 +729,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   // ---- wave result
   stash(s_o[wave], s_m[wave], s_l[wave], s_z[wave], __builtin_amdgcn_ldexpf(1.0f, 24 - kexp));
   __syncthreads();
-  // ---- merge the four waves; write this split's partial for each head
-  for (int x = threadIdx.x; x < GQA * D; x += 256) {
-    const int qh = x / D, d = x % D;
+  // ---- merge the four waves' quantized and exact-token states: the
+  // weights 2^(m_j - M) of the eight states of each head once, then the
+  // rows; write this split's partial for each head
+  __shared__ float s_fac[GQA][8], s_M[GQA];
+  if (threadIdx.x < 8 * GQA) {
+    const int qh = threadIdx.x / 8, j = threadIdx.x % 8;
     float M = s_m[0][qh];
 #pragma unroll
     for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, s_m[w][qh]);
@@ -739,19 +742,30 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, s_mf[w][qh]);
     // a split with no tokens at all leaves m = -inf, l = 0, o = 0
     const float Mref = M == -__builtin_inff() ? 0.f : M;
-    float o = 0.f, L = 0.f;
+    const float mj = j < 4 ? s_m[j][qh] : s_mf[j - 4][qh];
+    s_fac[qh][j] = __builtin_amdgcn_exp2f(mj - Mref);
+    if (j == 0) s_M[qh] = M;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < GQA * D; x += 256) {
+    const int qh = x / D, d = x % D;
+    float o = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = __builtin_amdgcn_exp2f(s_m[w][qh] - Mref);
-      o = __builtin_fmaf(f, s_o[w][qh][d] + s_z[w][qh], o);
-      L = __builtin_fmaf(f, s_l[w][qh], L);
-      const float g = __builtin_amdgcn_exp2f(s_mf[w][qh] - Mref);
-      o = __builtin_fmaf(g, s_of[w][qh][d], o);
-      L = __builtin_fmaf(g, s_lf[w][qh], L);
+      o = __builtin_fmaf(s_fac[qh][w], s_o[w][qh][d] + s_z[w][qh], o);
+      o = __builtin_fmaf(s_fac[qh][4 + w], s_of[w][qh][d], o);
     }
     const int64_t row = int64_t(b) * a.Hq + h * GQA + qh;
     partial_o(a, row, split, D)[d] = o;
-    if (d == 0) *reinterpret_cast<float2*>(partial_ml(a, row, split)) = float2{M, L};
+    if (d == 0) {
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        L = __builtin_fmaf(s_fac[qh][w], s_l[w][qh], L);
+        L = __builtin_fmaf(s_fac[qh][4 + w], s_lf[w][qh], L);
+      }
+      *reinterpret_cast<float2*>(partial_ml(a, row, split)) = float2{s_M[qh], L};
+    }
   }
 }
 

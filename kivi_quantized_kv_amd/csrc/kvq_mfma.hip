@@ -202,7 +202,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int kVB = CR::kVB;
   constexpr int kNG = G32 ? 2 : 1;         // key groups per chunk
   constexpr int kStepsPerWord = kCPW / 8;  // K-steps covered by one code word
-  constexpr int kJoin = GQA == 8 ? kRowRor8 : kRowRor4;   // high <-> low column
+  // GQA 4 with 32-token key groups: the 8 matrix columns a GQA-4 group
+  // leaves free take the chunk's second key group (columns 0-3 / 8-11:
+  // group 0 high / low parts, 4-7 / 12-15: group 1), so one weight pass
+  // serves both groups; the high and low columns of a head are then 8
+  // apart, as with GQA 8.
+  constexpr bool DUAL = GQA == 4 && G32;
+  constexpr int kJoin = (GQA == 8 || DUAL) ? kRowRor8 : kRowRor4;   // high <-> low column
   constexpr float kS = 16777216.0f;        // 2^24: unit of a subnormal code field
   constexpr float kSlack = 8.0f;           // running max kept within 2^8 of the true one
   constexpr int kNoScale = 100;            // value exponent before any scale is seen
@@ -221,8 +227,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, lg = lane >> 4;
   const int hh = col % GQA;                          // head of this column
-  const bool is_lo = ((col / GQA) & 1) != 0;         // low part column
+  const bool is_lo = DUAL ? col >= 8 : ((col / GQA) & 1) != 0;   // low part column
   const bool owner = col < GQA;                      // counts l and z once
+  const int grp = DUAL ? (col >> 2) & 1 : 0;         // key group of this column (dual form)
+  // v from lane l ^ 4: the other key group's column of the same head
+  auto other_group = [&](float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 4) << 2, __builtin_bit_cast(int, v)));
+  };
 
   __shared__ float s_q[GQA][D + 4];    // scale*log2e * q; rows padded against bank conflicts
   __shared__ float s_qf[GQA][D + 4];   // the same times each channel's field scale
@@ -393,6 +404,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   auto stash = [&](float (*so)[D], float* sm, float* sl, float* sz, float unit) {
     float lr = l + dpp_rot<kJoin>(l);     // owner (even tiles or exact tokens) + partner (odd tiles)
     float zr = z + dpp_rot<kJoin>(z);
+    if constexpr (DUAL) {
+      lr += other_group(lr);
+      zr += other_group(zr);
+    }
     if (!owner) {
       lr = 0.f;
       zr = 0.f;
@@ -409,8 +424,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = acc[n][i];
-        if constexpr (GQA == 8) v = sum_xor32(v);    // rows r and r + 8
-        else v = sum_xor16(v);                       // rows r and r + 4
+        if constexpr (DUAL) v = sum_xor32(sum_xor16(v));   // rows r, r + 4, r + 8, r + 12
+        else if constexpr (GQA == 8) v = sum_xor32(v);     // rows r and r + 8
+        else v = sum_xor16(v);                             // rows r and r + 4
         const int row = 4 * lg + i;
         if (row < GQA) so[row][n * 16 + col] = v * unit;
       }
@@ -435,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const float sc = sum_xor32(part);             // score of head hh
       raise_max(sc);
       const float p = __builtin_amdgcn_exp2f(sc - m);
-      if (lg == 0 && !is_lo) l += p;                // one lane group of the high columns
+      if (lg == 0 && owner) l += p;                 // one lane group of the owner columns
       float pr[4];
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2) {
@@ -537,13 +553,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       // ---- q.K^T: per key-group segment, K-steps outer, tiles inner
       f32x4_t sc[4];
       float kap[2] = {0.f, 0.f};               // kappa of each segment's group
+      constexpr int kPasses = (G32 && !DUAL) ? 2 : 1;
 #pragma unroll
-      for (int seg = 0; seg < 2; ++seg) {
-        const int t_begin = seg * kSegTiles;
-        const int t_end = t_begin + kSegTiles < kTiles ? t_begin + kSegTiles : kTiles;
+      for (int seg = 0; seg < kPasses; ++seg) {
+        const int t_begin = DUAL ? 0 : seg * kSegTiles;
+        const int t_end = DUAL ? kTiles : (t_begin + kSegTiles < kTiles ? t_begin + kSegTiles : kTiles);
         if (t_begin >= kTiles) break;
         {
-          const float* kpd = reinterpret_cast<const float*>(&kpb[wave][G32 ? seg : 0][0]);
+          const float* kpd = reinterpret_cast<const float*>(&kpb[wave][DUAL ? grp : (G32 ? seg : 0)][0]);
 #pragma unroll
           for (int kk = 0; kk < kKS; ++kk) {
             const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
@@ -619,8 +636,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       for (int t = 0; t < kTiles; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cm_seg[t / kSegTiles] = __builtin_fmaxf(cm_seg[t / kSegTiles], sc[t][i]);
-      float cm = __builtin_fmaf(cm_seg[0], kS, kap[0]);
-      if constexpr (G32 && !HALF) cm = __builtin_fmaxf(cm, __builtin_fmaf(cm_seg[1], kS, kap[1]));
+      float cm;
+      if constexpr (DUAL) {
+        cm = __builtin_fmaf(grp ? cm_seg[1] : cm_seg[0], kS, kap[0]);   // this column's group's tiles
+      } else {
+        cm = __builtin_fmaf(cm_seg[0], kS, kap[0]);
+        if constexpr (G32 && !HALF) cm = __builtin_fmaxf(cm, __builtin_fmaf(cm_seg[1], kS, kap[1]));
+      }
       // the head's max over lanes is only needed when the running max
       // moves: any lane over m + slack means its head's max is
       const uint64_t need_v = __builtin_amdgcn_ballot_w64(v_over);
@@ -639,6 +661,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         if (need_m != 0) {
           cm = max_xor16(cm);
           cm = max_xor32(cm);
+          if constexpr (DUAL) cm = __builtin_fmaxf(cm, other_group(cm));
           raise_max(cm);
         }
       }
@@ -652,7 +675,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int ps = 0; ps < kTiles / 2; ++ps) {
         const int t0 = 2 * ps, t1 = 2 * ps + 1;
-        const float kmp = (t0 / kSegTiles) == 0 ? km0 : km1;
+        const float kmp = DUAL ? km0 : ((t0 / kSegTiles) == 0 ? km0 : km1);
         const int tok = 16 * (is_lo ? t1 : t0) + 4 * lg;
         const float4 dv = *reinterpret_cast<const float4*>(&vpb[wave][0][tok]);
         const float4 zv = *reinterpret_cast<const float4*>(&vpb[wave][1][tok]);
@@ -663,6 +686,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           const float sm = is_lo ? sc[t1][i] : sc[t0][i];
           pm[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm, kS, kmp));
+          if constexpr (DUAL) pm[i] = ps == grp ? pm[i] : 0.f;   // the other group's columns weigh nothing
           l += pm[i];                         // every lane; owners and partners meet at the end
           z = __builtin_fmaf(pm[i], zs[i], z);
         }

@@ -537,19 +537,19 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the split partials: M = max_j m_j,
 // L = sum_j 2^(m_j - M) l_j, out = sum_j 2^(m_j - M) o_j / L.
-// One workgroup per (32-channel block, q head, batch), one round of loads:
-// thread (slot, c4) folds channels [4 c4, 4 c4 + 4) of the block for
-// splits slot, slot + 32, ... (float4 loads) into a running state of its
-// own (local max, sums); the 32 slot states then meet through LDS by the
-// same rule.
+// One workgroup per (32-channel block, q head, batch), one round of loads
+// up to 64 splits: thread (slot, c4) folds channels [4 c4, 4 c4 + 4) of the
+// block for splits slot, slot + 32, ... (float4 loads) into a running
+// state of its own (local max, sums); the 32 slot states then meet through
+// LDS by the same rule, with each slot's weight 2^(M_slot - M) computed once.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_merge(AttnArgs a) {
   constexpr int kCW = 32;                   // channels per workgroup
   constexpr int kQ = kCW / 4;               // float4 columns per split row
   constexpr int kSlots = 256 / kQ;          // 32 split slots
-  constexpr int kPer = 4;                   // splits per slot per load round
-  __shared__ float s_m[kSlots], s_l[kSlots];
+  constexpr int kPer = 2;                   // splits per slot per load round
+  __shared__ float s_m[kSlots], s_l[kSlots], s_w[kSlots];
   __shared__ float4 s_acc[kSlots][kQ];
   const int cb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, c4 = t % kQ, slot = t / kQ;
@@ -596,16 +596,21 @@ __global__ __launch_bounds__(256) void k_merge(AttnArgs a) {
     s_l[slot] = L;
   }
   __syncthreads();
-  if (t < kCW) {
-    float Mt = s_m[0];
+  // the slot weights 2^(M_k - M), once per slot
+  if (t < kSlots) {
+    float Mt = s_m[t];
 #pragma unroll
-    for (int k = 1; k < kSlots; ++k) Mt = __builtin_fmaxf(Mt, s_m[k]);
+    for (int o = 16; o > 0; o >>= 1) Mt = __builtin_fmaxf(Mt, __shfl_xor(Mt, o, 32));
     const float Mref = Mt == -__builtin_inff() ? 0.f : Mt;
+    s_w[t] = __builtin_amdgcn_exp2f(s_m[t] - Mref);
+  }
+  __syncthreads();
+  if (t < kCW) {
     float sum = 0.f, Lt = 0.f;
     const int q = t / 4, e = t % 4;
 #pragma unroll 8
     for (int k = 0; k < kSlots; ++k) {
-      const float f = __builtin_amdgcn_exp2f(s_m[k] - Mref);
+      const float f = s_w[k];
       sum = __builtin_fmaf(f, reinterpret_cast<const float*>(&s_acc[k][q])[e], sum);
       Lt = __builtin_fmaf(f, s_l[k], Lt);
     }

@@ -304,8 +304,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // q first (its loads complete before the chunk batches), then the first
-  // two batches, then q into LDS
+  // q first, then the first exact token, then the first two batches (q and
+  // that token complete before them), then q into LDS
   constexpr int kQPer = GQA * D / 256;
   using QE = typename Elem<DT>::T;
   QE qraw[kQPer];                                  // widened after the batches are issued
@@ -314,9 +314,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
     qraw[j] = reinterpret_cast<const QE*>(a.q)[b * a.q_sb + (h * GQA + qh) * a.q_sh + d];
   }
-  // The first two batches, on every wave: a wave without chunks re-reads
-  // chunk 0, which exists (the kernel runs only with Q > 0).  Under a branch
-  // they would make the compiler's wait for q below cover both batches.
   // This wave's exact tokens (sinks and the residual window): f0 + wave,
   // f0 + wave + 4, ... below f1.  The first one's rows are loaded before
   // the chunk batches, so that they land first and are folded in while the
@@ -352,6 +349,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       else fvr[n] = reinterpret_cast<const QE*>(vb)[off + 16 * n + col];
     }
   }
+  // The first two batches, on every wave (a wave with fewer chunks issues
+  // batches that are not live, on chunk 0, which exists: the kernel runs
+  // only with Q > 0).  Under a branch they would make the compiler's wait
+  // for q below cover both batches.
   CR ra, rb;
   issue_batch(gw, wn > 0, ra, std::integral_constant<int, 0>{});
   issue_batch(gw + nw_row, wn > 1, rb, std::integral_constant<int, 1>{});
@@ -719,10 +720,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const int64_t n_full = wn - (last_half ? 1 : 0);
     // After a chunk, its registers and parameter buffer are free: start
     // the batch of the wave's chunk after next.  Past the wave's last chunk
-    // the batch re-reads chunk 0 of this (b, h), which every wave shares and
-    // which is mostly served by the L2, so that a batch always follows each
-    // chunk (the counter waits assume it).  The copies into the buffer are
-    // ordered after this wave's reads of it by the wait on the LDS counter.
+    // that batch is not live (one cache line of chunk 0 per instruction), so
+    // that a batch always follows each chunk, as the counter waits assume.
+    // The copies into the buffer are ordered after this wave's reads of it
+    // by the wait on the LDS counter.
     auto run_chunk = [&](int64_t k, CR& r, auto half_tag, auto buf_tag) {
       process_chunk(r, half_tag, buf_tag);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)

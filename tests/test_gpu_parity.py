@@ -65,6 +65,9 @@ SMALL = [
     # 64 waves per KV head on a 256-CU part, 129 chunks: the wave with the
     # half chunk has three chunks (the half one on the first register set)
     (4, 32, 8, 128, 4, 32, 4, 32, 8260, "bf16"),
+    # GQA 4 with 32-token key groups at D 64, 4-bit: the dual-group form
+    # (both key groups of a chunk in one weight pass), several chunks per wave
+    (4, 32, 8, 64, 4, 32, 4, 32, 10000, "f16"),
     (1, 64, 8, 128, 4, 64, 4, 128, 70000, "bf16"),
     # GQA 4 / 8 with nothing quantized yet (the VALU kernel takes these)
     (1, 8, 1, 128, 4, 64, 4, 128, 150, "bf16"),
@@ -169,6 +172,7 @@ STREAM = [
     (1, 4, 4, 128, 2, 32, 5, 32, 40, 130, "f16"),
     (1, 16, 4, 128, 2, 32, 4, 128, 100, 140, "bf16"),   # matrix-core path, GQA 4
     (2, 16, 2, 64, 4, 64, 2, 0, 30, 150, "f16"),        # matrix-core path, GQA 8, R 0
+    (2, 8, 2, 64, 4, 32, 2, 32, 60, 130, "f16"),        # dual-group GQA 4, 4-bit, half chunks
 ]
 
 

@@ -673,10 +673,59 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       // the other tile's weights from its partner; both then pack the pair
       // in tile order (high or low parts).  l and z gather per tile parity
       // and meet at the end.
+      if constexpr (DUAL) {
+        // dual-group form: a column weighs only its own group's 32-token
+        // step (tiles 2 grp and 2 grp + 1; none in a half chunk for group
+        // 1), so its weights are computed once and placed in that step's
+        // operand, with zeros in the other step's
+        const int t_own = 2 * grp + (is_lo ? 1 : 0);
+        const int tok = 16 * t_own + 4 * lg;
+        const float4 dv = *reinterpret_cast<const float4*>(&vpb[wave][0][tok]);
+        const float4 zv = *reinterpret_cast<const float4*>(&vpb[wave][1][tok]);
+        const float ds[4] = {dv.x * vfk[0], dv.y * vfk[1], dv.z * vfk[2], dv.w * vfk[3]};
+        const float zs[4] = {zv.x, zv.y, zv.z, zv.w};
+        float pm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float s0 = is_lo ? sc[1][i] : sc[0][i];
+          float sm = s0;
+          if constexpr (!HALF) sm = grp ? (is_lo ? sc[3][i] : sc[2][i]) : s0;
+          pm[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm, kS, km0));
+          if constexpr (HALF) pm[i] = grp ? 0.f : pm[i];
+          l += pm[i];
+          z = __builtin_fmaf(pm[i], zs[i], z);
+        }
+        float wm[4];
+        field_weights<BITS>(pm, ds, wm);
+        u32x4_t ap_own;
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) {
+          const float wo = dpp_rot<kJoin>(wm[r2]);
+          ap_own[r2] = __builtin_amdgcn_perm(0u, split_pack(wm[r2], wo, neg_lo), swap_sel);
+        }
+#pragma unroll
+        for (int ps = 0; ps < kTiles / 2; ++ps) {
+          u32x4_t ap;
+#pragma unroll
+          for (int r2 = 0; r2 < 4; ++r2) ap[r2] = ps == grp ? ap_own[r2] : 0u;
+#pragma unroll
+          for (int n = 0; n < kNB; ++n) {
+            u32x4_t bv;
+            if constexpr (kVB == 2) {
+              bv = code_fields<BITS, 0>(r.vw[ps][n]);
+            } else {
+              if (ps == 0) bv = code_fields<BITS, 0>(r.vw[0][n]);
+              else bv = code_fields<BITS, 1>(r.vw[0][n]);
+            }
+            acc[n] = mfma_f16(ap, bv, acc[n]);
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int ps = 0; ps < kTiles / 2; ++ps) {
         const int t0 = 2 * ps, t1 = 2 * ps + 1;
-        const float kmp = DUAL ? km0 : ((t0 / kSegTiles) == 0 ? km0 : km1);
+        const float kmp = (t0 / kSegTiles) == 0 ? km0 : km1;
         const int tok = 16 * (is_lo ? t1 : t0) + 4 * lg;
         const float4 dv = *reinterpret_cast<const float4*>(&vpb[wave][0][tok]);
         const float4 zv = *reinterpret_cast<const float4*>(&vpb[wave][1][tok]);
@@ -687,7 +736,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           const float sm = is_lo ? sc[t1][i] : sc[t0][i];
           pm[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm, kS, kmp));
-          if constexpr (DUAL) pm[i] = ps == grp ? pm[i] : 0.f;   // the other group's columns weigh nothing
           l += pm[i];                         // every lane; owners and partners meet at the end
           z = __builtin_fmaf(pm[i], zs[i], z);
         }

@@ -646,6 +646,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       }
       // the head's max over lanes is only needed when the running max
       // moves: any lane over m + slack means its head's max is
+      // wave priority: 1 from the chunk's start, 2 from here to the issue
+      // of the next batch, 0 after it; a wave that has reached P.V goes
+      // ahead of its SIMD partner, so its chunk ends and its next loads go
+      // out sooner (same-box A/B: -0.5 to -0.9 us per call)
+      __builtin_amdgcn_s_setprio(2);
       const uint64_t need_v = __builtin_amdgcn_ballot_w64(v_over);
       const uint64_t need_m = __builtin_amdgcn_ballot_w64(cm > m + kSlack);
       if ((need_v | need_m) != 0) {
@@ -773,9 +778,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // The copies into the buffer are ordered after this wave's reads of it
     // by the wait on the LDS counter.
     auto run_chunk = [&](int64_t k, CR& r, auto half_tag, auto buf_tag) {
+      __builtin_amdgcn_s_setprio(1);
       process_chunk(r, half_tag, buf_tag);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       issue_batch(gw + (k + 2) * nw_row, k + 2 < wn, r, buf_tag);
+      __builtin_amdgcn_s_setprio(0);
     };
     using Full = std::false_type;
     using Half = std::true_type;

@@ -27,7 +27,13 @@
  *  - Arithmetic: delta = fl32(fl32(max - min) / (2^b - 1)); zero point =
  *    min + 0.0f (fp32); code = clamp(rint_half_even(fl32(fl32(x - zp) /
  *    delta)), 0, 2^b - 1), a true IEEE division; delta == 0 gives code 0.
- *    Subnormals are kept.  Inputs must be finite.
+ *    Subnormals are kept.  Inputs must be finite with magnitude below
+ *    2^127, so that max - min is finite in fp32.
+ *  - Decode attention accumulates in fp32: every score scale * q . k_hat
+ *    and every partial sum of its terms must be finite in fp32.  Within
+ *    that, any key or value range is handled (the kernels track power-of-
+ *    two exponents for both); outputs inside fp32's subnormal range carry
+ *    its absolute rounding.
  *  - Sink and residual tokens are stored bit-exactly in the input dtype.
  *  - GQA: query head hq reads KV head hq / (Hq / Hkv).
  *  - The decode query attends to all n_tokens cached tokens (no mask);
@@ -164,14 +170,15 @@ static inline int64_t kvq_resid_bytes(const kvq_config *c) {
 
 /* Decode-attention workspace: per (batch, query head) up to
  * KVQ_MAX_SPLITS partial results of D + 2 floats.  Any size of at least
- * kvq_workspace_bytes_min works; the kernel uses fewer splits when given
- * less room.  Results agree across split counts to fp32 rounding. */
+ * kvq_workspace_bytes_min (room for one split) works; the kernels use
+ * fewer splits when given less room, down to one.  Results agree across
+ * split counts to fp32 rounding. */
 #define KVQ_MAX_SPLITS 1024
 static inline int64_t kvq_workspace_bytes(const kvq_config *c, int32_t n_q_heads) {
   return (int64_t)c->batch * n_q_heads * KVQ_MAX_SPLITS * (c->head_dim + 2) * 4;
 }
 static inline int64_t kvq_workspace_bytes_min(const kvq_config *c, int32_t n_q_heads) {
-  return (int64_t)c->batch * n_q_heads * 64 * (c->head_dim + 2) * 4;
+  return (int64_t)c->batch * n_q_heads * (c->head_dim + 2) * 4;
 }
 
 /* ---- entry points -------------------------------------------------- */

@@ -256,7 +256,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cach
     const int64_t per_split_bytes = int64_t(B) * n_q_heads * (D + 2) * 4;
     int64_t cap_splits = int64_t(workspace_bytes) / per_split_bytes;
     if (cap_splits > KVQ_MAX_SPLITS) cap_splits = KVQ_MAX_SPLITS;
-    if (int64_t(workspace_bytes) < kvq_workspace_bytes_min(cfg, n_q_heads) || cap_splits < 2)
+    if (int64_t(workspace_bytes) < kvq_workspace_bytes_min(cfg, n_q_heads) || cap_splits < 1)
       return KVQ_EWORKSPACE;
 
     // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit

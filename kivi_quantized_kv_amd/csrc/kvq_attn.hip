@@ -197,12 +197,18 @@ __device__ __forceinline__ void load_small(const void* base, int64_t i, float* o
 // a block is processed.
 // q . K: lane (qt, tl) takes channel quarter qt of token tl of a 16-token
 //   sub-tile; the quarter sums meet by quad DPP.  The coefficients of a key
-//   group, x_d = q_d delta_d 2^24 2^-(b (d mod codes per byte)), are formed
+//   group, x_d = q_d delta_d 2^-(b (d mod codes per byte)), are formed
 //   once per 32 tokens: each lane scales D/64 channels, the wave trades them
-//   through LDS, and kappa = sum_d q_d z_d is a wave sum.
+//   through LDS, and kappa = sum_d q_d z_d is a wave sum.  The factor 2^24
+//   of the code fields is applied to the finished dot product, so neither
+//   a wide key range nor a subnormal one leaves fp32's range on the way.
 // P . V: lane (vg, vj) holds code units of channels vj + 16n for the tokens
 //   of lane group vg; the probabilities of those tokens come from their
-//   score lanes by row broadcasts.
+//   score lanes by row broadcasts.  Their coefficients p_t delta_t carry
+//   2^(24 + vexp) (2^24 cancels the code fields' 2^-24, so the accumulators
+//   hold sums times 2^vexp), where the wave's exponent vexp puts the
+//   largest value delta seen so far in [2^6, 2^7); it only decreases, with
+//   an exact power-of-two rescale of the accumulators.
 // ---------------------------------------------------------------------------
 // Waves per SIMD the register budget is held to: four (128 VGPRs) where the
 // kernel fits without spilling, else three.
@@ -283,10 +289,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
   for (int c = 0; c < kWC; ++c) {
     const int ch = lane * kWC + c;
     sq_w[c] = s_q[ch];
-    xs_w[c] = s_q[ch] * (kS * code_field_scale<BITS>(ch));
+    xs_w[c] = s_q[ch] * code_field_scale<BITS>(ch);
   }
-  // weight of this lane's score token in its value code field
-  const float pfac = kS * code_field_scale<BITS>(tl);
+  // exponent of this lane's score token's value code field
+  const int fsh = BITS == 8 ? 0 : -BITS * (tl % (8 / BITS));
+  // value exponent; before any delta is seen the threshold 2^(7 - vexp) is
+  // the smallest fp32 subnormal, so the first nonzero delta sets it
+  int vexp = 156;
+  float vthr = __builtin_amdgcn_ldexpf(1.0f, 7 - vexp);
   // Uniform bases and 32-bit lane offsets (loads take the scalar-base form).
   const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRowBytes;
   const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRowBytes;
@@ -428,11 +438,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        // -inf past the quantized count, added rather than selected so the
-        // dot products stay unconditional
+        // -inf past the quantized count (selected: the key parameters of a
+        // group past the count are never written and may hold anything)
         const int st = 2 * k + u;
-        const float mask = st * 16 + tl < nvalid ? 0.f : -__builtin_inff();
-        sc[st] = quad_sum(dot[u]) + (kap[k] + mask);
+        const float v = __builtin_fmaf(quad_sum(dot[u]), kS, kap[k]);
+        sc[st] = st * 16 + tl < nvalid ? v : -__builtin_inff();
       }
     }
     wave_lds_sync();
@@ -440,16 +450,29 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
 #pragma unroll
     for (int st = 1; st < kNST; ++st) lmax = __builtin_fmaxf(lmax, sc[st]);
     raise_max(tile_max(lmax));
-    float pp[kNST];
+    float pp[kNST], dvs[kNST];
+    float vmax = 0.f;
+#pragma unroll
+    for (int st = 0; st < kNST; ++st) {
+      dvs[st] = st * 16 + tl < nvalid ? r.dv[st] : 0.f;
+      vmax = __builtin_fmaxf(vmax, dvs[st]);
+    }
+    if (__builtin_amdgcn_ballot_w64(vmax >= vthr) != 0) {   // rare: a larger value delta
+      const int knew = __builtin_amdgcn_readfirstlane(7 - __builtin_amdgcn_frexp_expf(wave_max(vmax)));
+#pragma unroll
+      for (int n = 0; n < kUnits; ++n) acc[n] = __builtin_amdgcn_ldexpf(acc[n], knew - vexp);
+      vexp = knew;
+      vthr = __builtin_amdgcn_ldexpf(1.0f, 7 - vexp);
+    }
+    const int vke = vexp + 24 + fsh;
 #pragma unroll
     for (int st = 0; st < kNST; ++st) {
       const bool ok = st * 16 + tl < nvalid;
       const float p = __builtin_amdgcn_exp2f(sc[st] - m);   // 0 past the range
-      const float dv = ok ? r.dv[st] : 0.f;
       const float zv = ok ? r.zv[st] : 0.f;
       l += p;
       z = __builtin_fmaf(p, zv, z);
-      pp[st] = p * dv * pfac;
+      pp[st] = p * __builtin_amdgcn_ldexpf(dvs[st], vke);
     }
     // P . V: code slot i of lane group vg is token vslot_token(vg, i), whose
     // p sits in lane 4 * (i & 3) of this row, sub-tile o / 16
@@ -490,7 +513,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
   z = 0.25f * wave_sum_valu(z);
   if (lane < 16) {
 #pragma unroll
-    for (int n = 0; n < kUnits; ++n) s_out[wave][n * 16 + lane] = acc[n] + z;
+    for (int n = 0; n < kUnits; ++n) s_out[wave][n * 16 + lane] = __builtin_amdgcn_ldexpf(acc[n], -vexp) + z;
   }
   wave_lds_sync();
 #pragma unroll

@@ -211,7 +211,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int kJoin = (GQA == 8 || DUAL) ? kRowRor8 : kRowRor4;   // high <-> low column
   constexpr float kS = 16777216.0f;        // 2^24: unit of a subnormal code field
   constexpr float kSlack = 8.0f;           // running max kept within 2^8 of the true one
-  constexpr int kNoScale = 100;            // value exponent before any scale is seen
+  // value exponent before any scale is seen: the threshold 2^(7 - kNoScale)
+  // is the smallest fp32 subnormal, so the first nonzero delta sets it
+  constexpr int kNoScale = 156;
   // vector-memory instructions per chunk batch: code loads, then the
   // parameter copies (key groups: one 16-byte copy per group at D = 128,
   // two 4-byte copies at D = 64; values: delta and zero, 4 bytes each)
@@ -356,6 +358,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   CR ra, rb;
   issue_batch(gw, wn > 0, ra, std::integral_constant<int, 0>{});
   issue_batch(gw + nw_row, wn > 1, rb, std::integral_constant<int, 1>{});
+  __shared__ float s_qmx[4];
+  float qmx = 0.f;                                 // max |scale*log2e * q| of the workgroup
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
     const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
@@ -366,8 +370,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const float v = qf * a.sm_scale_log2;
     s_q[qh][d] = v;
     s_qf[qh][d] = v * field_scale<BITS>(d);
+    qmx = __builtin_fmaxf(qmx, __builtin_fabsf(v));
   }
+  qmx = wave_max(qmx);
+  if (lane == 0) s_qmx[wave] = qmx;
   __syncthreads();
+  const float qmax = __builtin_fmaxf(__builtin_fmaxf(s_qmx[0], s_qmx[1]), __builtin_fmaxf(s_qmx[2], s_qmx[3]));
+  // Key weights w = x * delta with |x| <= qmax: every field weight is at
+  // most 1.25 qmax delta_max, so the fp16 high parts stay finite while the
+  // chunk's largest key delta is below 2^15 / qmax.  A chunk at or above
+  // 2^12 / qmax takes the rare branch, which scales the weights by 2^-e and
+  // forms its scores in one rounding: below it, kappa - m and the products
+  // stay under ~2^26, so the split sum kappa - m + products keeps the
+  // running-max slack.
+  const float kthr = 4096.0f / qmax;                // +inf when q is zero
 
   f32x4_t acc[kNB];
 #pragma unroll
@@ -401,8 +417,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   };
 
   // Wave state into LDS: l and z reduced over the owner columns' lane
-  // groups, the high and low rows joined, o in real units (acc times unit).
-  auto stash = [&](float (*so)[D], float* sm, float* sl, float* sz, float unit) {
+  // groups, the high and low rows joined, o in real units (acc times
+  // 2^uexp).
+  auto stash = [&](float (*so)[D], float* sm, float* sl, float* sz, int uexp) {
     float lr = l + dpp_rot<kJoin>(l);     // owner (even tiles or exact tokens) + partner (odd tiles)
     float zr = z + dpp_rot<kJoin>(z);
     if constexpr (DUAL) {
@@ -429,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         else if constexpr (GQA == 8) v = sum_xor32(v);     // rows r and r + 8
         else v = sum_xor16(v);                             // rows r and r + 4
         const int row = 4 * lg + i;
-        if (row < GQA) so[row][n * 16 + col] = v * unit;
+        if (row < GQA) so[row][n * 16 + col] = __builtin_amdgcn_ldexpf(v, uexp);
       }
     }
   };
@@ -510,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         fold_fp(kq, vv);
       }
     }
-    stash(s_of[wave], s_mf[wave], s_lf[wave], nullptr, 1.0f);
+    stash(s_of[wave], s_mf[wave], s_lf[wave], nullptr, 0);
 #pragma unroll
     for (int n = 0; n < kNB; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m = -__builtin_inff();
@@ -520,20 +537,65 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 
   {
     // ------------------------------------------------------------ quantized
-    // value field scales of rows i (token 4g + i of a tile) times 2^kexp
-    float vfk[4];
-    auto set_vfk = [&]() {
+    // exponents of the value field scales of rows i (token 4g + i of a
+    // tile) plus kexp: P''_t = p_t * ldexp(delta_t, vke[i]).  ldexp keeps
+    // exponents outside fp32's range of powers of two (kexp up to 156 for
+    // subnormal deltas) exact.
+    int vke[4];
+    auto set_vke = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vfk[i] = __builtin_amdgcn_ldexpf(field_scale<BITS>(i), kexp);
+      for (int i = 0; i < 4; ++i) vke[i] = kexp - BITS * (i % (8 / BITS));
     };
-    set_vfk();
+    set_vke();
     const int vtok = (lane & 31) * 2;                // value deltas this lane checks
 
     u32x4_t qB[kKS];
 
+    // Field weights of one key group into qB (high or low parts): x_d
+    // (field-scaled q) times delta_d.
+    auto group_weights = [&](const float* kpd) {
+#pragma unroll
+      for (int kk = 0; kk < kKS; ++kk) {
+        const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
+        // the 8 channels of this K-step: runs [cA, cA+4) (low halves of
+        // the fields) and [cB, cB+4) (high halves) of word wk
+        const int cA = lg * kQCH + wk * kCPW + 4 * sp;
+        const int cB = cA + kCPW / 2;
+        const float4 qa = *reinterpret_cast<const float4*>(&s_qf[hh][cA]);
+        const float4 qb = *reinterpret_cast<const float4*>(&s_qf[hh][cB]);
+        const float4 da = *reinterpret_cast<const float4*>(kpd + cA);
+        const float4 db = *reinterpret_cast<const float4*>(kpd + cB);
+        const float xa[4] = {qa.x, qa.y, qa.z, qa.w}, xb[4] = {qb.x, qb.y, qb.z, qb.w};
+        const float fa[4] = {da.x, da.y, da.z, da.w}, fb[4] = {db.x, db.y, db.z, db.w};
+        float wa[4], wb[4];
+        field_weights<BITS>(xa, fa, wa);
+        field_weights<BITS>(xb, fb, wb);
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) qB[kk][r2] = split_pack(wa[r2], wb[r2], neg_lo);
+      }
+    };
+    // S^T tiles [t_begin, t_end) of chunk r from the weights in qB.
+    auto tile_products = [&](const CR& r, f32x4_t* sc, int t_begin, int t_end) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t >= t_begin && t < t_end) sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kKS; ++kk) {
+        const int wk = kk / kStepsPerWord;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < t_begin || t >= t_end) continue;
+          u32x4_t av;
+          if (kk % kStepsPerWord == 0) av = code_fields<BITS, 0>(r.kw[t][wk]);
+          else av = code_fields<BITS, 1>(r.kw[t][wk]);
+          sc[t] = mfma_f16(av, qB[kk], sc[t]);
+        }
+      }
+    };
+
     // A half chunk (only ever the last of the quantized range) holds 32
     // tokens: tiles 0 and 1, the first 32-token step of P.V.
-    auto process_chunk = [&](const CR& r, auto half_tag, auto buf_tag) {
+    auto process_chunk = [&](const CR& r, int64_t ch, auto half_tag, auto buf_tag) {
       constexpr bool HALF = decltype(half_tag)::value;
       constexpr int kTiles = HALF ? 2 : 4;
       constexpr int BUF = decltype(buf_tag)::value;
@@ -541,6 +603,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
       constexpr int nv = HALF ? 32 : 64;
       constexpr int kSegTiles = G32 ? 2 : 4;
+      constexpr int kPasses = (G32 && !DUAL) ? 2 : 1;
+      // key groups of this chunk that hold quantized tokens (a half chunk
+      // with 32-token groups has one)
+      constexpr int kLiveGroups = (G32 && !HALF) ? 2 : 1;
       // this chunk's batch is complete once at most the next one is in flight
       wait_vmcnt<kBatch>();
       // ---- value scale: a delta at or above 2^(7-kexp) lowers kexp so
@@ -551,36 +617,44 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const float2 dv = *reinterpret_cast<const float2*>(&vpb[wave][0][vtok]);
       const float vmax = vtok < nv ? __builtin_fmaxf(dv.x, dv.y) : 0.0f;
       const bool v_over = vmax >= __builtin_amdgcn_ldexpf(1.0f, 7 - kexp);
+      // ---- key range: the lanes share the chunk's key deltas, a disjoint
+      // few each; any at or above kthr sends the chunk to the rare branch
+      float kdm;
+      {
+        // lanes [64/kLiveGroups * g, ...) cover group g, kPer deltas each
+        constexpr int kPer = kLiveGroups * D / 64;
+        constexpr int kLanesPerGroup = 64 / kLiveGroups;
+        const float* kp = reinterpret_cast<const float*>(&kpb[wave][lane / kLanesPerGroup][0]) +
+                          (lane % kLanesPerGroup) * kPer;
+        if constexpr (kPer == 4) {
+          const float4 x = *reinterpret_cast<const float4*>(kp);
+          kdm = __builtin_fmaxf(__builtin_fmaxf(x.x, x.y), __builtin_fmaxf(x.z, x.w));
+        } else if constexpr (kPer == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(kp);
+          kdm = __builtin_fmaxf(x.x, x.y);
+        } else {
+          kdm = kp[0];
+        }
+      }
+      const bool k_over = kdm >= kthr;
+      auto seg_range = [&](int seg, int& t_begin, int& t_end) {
+        t_begin = DUAL ? 0 : seg * kSegTiles;
+        t_end = DUAL ? kTiles : (t_begin + kSegTiles < kTiles ? t_begin + kSegTiles : kTiles);
+      };
+      auto seg_params = [&](int seg) {
+        return reinterpret_cast<const float*>(&kpb[wave][DUAL ? grp : (G32 ? seg : 0)][0]);
+      };
       // ---- q.K^T: per key-group segment, K-steps outer, tiles inner
       f32x4_t sc[4];
       float kap[2] = {0.f, 0.f};               // kappa of each segment's group
-      constexpr int kPasses = (G32 && !DUAL) ? 2 : 1;
 #pragma unroll
       for (int seg = 0; seg < kPasses; ++seg) {
-        const int t_begin = DUAL ? 0 : seg * kSegTiles;
-        const int t_end = DUAL ? kTiles : (t_begin + kSegTiles < kTiles ? t_begin + kSegTiles : kTiles);
+        int t_begin, t_end;
+        seg_range(seg, t_begin, t_end);
         if (t_begin >= kTiles) break;
         {
-          const float* kpd = reinterpret_cast<const float*>(&kpb[wave][DUAL ? grp : (G32 ? seg : 0)][0]);
-#pragma unroll
-          for (int kk = 0; kk < kKS; ++kk) {
-            const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
-            // the 8 channels of this K-step: runs [cA, cA+4) (low halves of
-            // the fields) and [cB, cB+4) (high halves) of word wk
-            const int cA = lg * kQCH + wk * kCPW + 4 * sp;
-            const int cB = cA + kCPW / 2;
-            const float4 qa = *reinterpret_cast<const float4*>(&s_qf[hh][cA]);
-            const float4 qb = *reinterpret_cast<const float4*>(&s_qf[hh][cB]);
-            const float4 da = *reinterpret_cast<const float4*>(kpd + cA);
-            const float4 db = *reinterpret_cast<const float4*>(kpd + cB);
-            const float xa[4] = {qa.x, qa.y, qa.z, qa.w}, xb[4] = {qb.x, qb.y, qb.z, qb.w};
-            const float fa[4] = {da.x, da.y, da.z, da.w}, fb[4] = {db.x, db.y, db.z, db.w};
-            float wa[4], wb[4];
-            field_weights<BITS>(xa, fa, wa);
-            field_weights<BITS>(xb, fb, wb);
-#pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) qB[kk][r2] = split_pack(wa[r2], wb[r2], neg_lo);
-          }
+          const float* kpd = seg_params(seg);
+          group_weights(kpd);
           // kappa = sum_d q_d zero_d: high columns take the first half of
           // the K-steps, low columns the second, joined by the rotate-add;
           // it is added to the scores after the matrix products
@@ -608,42 +682,35 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           kpart = sum_xor16(kpart);
           kap[seg] = sum_xor32(kpart);
         }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (t >= t_begin && t < t_end) sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < kKS; ++kk) {
-          const int wk = kk / kStepsPerWord;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if (t < t_begin || t >= t_end) continue;
-            u32x4_t av;
-            if (kk % kStepsPerWord == 0) av = code_fields<BITS, 0>(r.kw[t][wk]);
-            else av = code_fields<BITS, 1>(r.kw[t][wk]);
-            sc[t] = mfma_f16(av, qB[kk], sc[t]);
-          }
-        }
+        tile_products(r, sc, t_begin, t_end);
       }
       // join the high and low columns of each head (scores - kappa, times
       // 2^-24)
+      auto join_tiles = [&]() {
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
+        for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[t][i] += dpp_rot<kJoin>(sc[t][i]);
-      }
+          for (int i = 0; i < 4; ++i) sc[t][i] += dpp_rot<kJoin>(sc[t][i]);
+        }
+      };
+      join_tiles();
       // ---- online softmax (log2 domain); m is per head, uniform over lanes
-      float cm_seg[2] = {-__builtin_inff(), -__builtin_inff()};
+      auto chunk_max = [&]() {
+        float cm_seg[2] = {-__builtin_inff(), -__builtin_inff()};
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t)
+        for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cm_seg[t / kSegTiles] = __builtin_fmaxf(cm_seg[t / kSegTiles], sc[t][i]);
-      float cm;
-      if constexpr (DUAL) {
-        cm = __builtin_fmaf(grp ? cm_seg[1] : cm_seg[0], kS, kap[0]);   // this column's group's tiles
-      } else {
-        cm = __builtin_fmaf(cm_seg[0], kS, kap[0]);
-        if constexpr (G32 && !HALF) cm = __builtin_fmaxf(cm, __builtin_fmaf(cm_seg[1], kS, kap[1]));
-      }
+          for (int i = 0; i < 4; ++i) cm_seg[t / kSegTiles] = __builtin_fmaxf(cm_seg[t / kSegTiles], sc[t][i]);
+        float c;
+        if constexpr (DUAL) {
+          c = __builtin_fmaf(grp ? cm_seg[1] : cm_seg[0], kS, kap[0]);   // this column's group's tiles
+        } else {
+          c = __builtin_fmaf(cm_seg[0], kS, kap[0]);
+          if constexpr (G32 && !HALF) c = __builtin_fmaxf(c, __builtin_fmaf(cm_seg[1], kS, kap[1]));
+        }
+        return c;
+      };
+      float cm = chunk_max();
       // the head's max over lanes is only needed when the running max
       // moves: any lane over m + slack means its head's max is
       // wave priority: 1 from the chunk's start, 2 from here to the issue
@@ -651,18 +718,87 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       // ahead of its SIMD partner, so its chunk ends and its next loads go
       // out sooner (same-box A/B: -0.5 to -0.9 us per call)
       __builtin_amdgcn_s_setprio(2);
+      const uint64_t need_k = __builtin_amdgcn_ballot_w64(k_over);
       const uint64_t need_v = __builtin_amdgcn_ballot_w64(v_over);
-      const uint64_t need_m = __builtin_amdgcn_ballot_w64(cm > m + kSlack);
-      if ((need_v | need_m) != 0) {
+      uint64_t need_m = __builtin_amdgcn_ballot_w64(cm > m + kSlack);
+      if ((need_k | need_v | need_m) != 0) {
+        if (need_k != 0) {
+          // a wide key range: the weights of this chunk again with x scaled
+          // by 2^-e, e = exponent of qmax * (largest delta) less 14, so
+          // every field weight is below 1.25 * 2^14; the products are
+          // scaled back by 2^e (exact) before the scores are formed
+          const float big = qmax * wave_max(kdm);
+          const int e = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(big) - 14);
+          const float xs = __builtin_amdgcn_ldexpf(1.0f, -e);
+          // One K-step at a time, with the chunk's key codes loaded again
+          // (ordinary loads), so that the branch needs few registers beyond
+          // those live across it.
+#pragma unroll
+          for (int seg = 0; seg < kPasses; ++seg) {
+            int t_begin, t_end;
+            seg_range(seg, t_begin, t_end);
+            if (t_begin >= kTiles) break;
+            const float* kpd = seg_params(seg);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (t >= t_begin && t < t_end) sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < kKS; ++kk) {
+              __builtin_amdgcn_sched_barrier(0);
+              const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
+              const int cA = lg * kQCH + wk * kCPW + 4 * sp;
+              const int cB = cA + kCPW / 2;
+              const float4 qa = *reinterpret_cast<const float4*>(&s_qf[hh][cA]);
+              const float4 qb = *reinterpret_cast<const float4*>(&s_qf[hh][cB]);
+              const float4 da = *reinterpret_cast<const float4*>(kpd + cA);
+              const float4 db = *reinterpret_cast<const float4*>(kpd + cB);
+              const float xa[4] = {qa.x * xs, qa.y * xs, qa.z * xs, qa.w * xs};
+              const float xb[4] = {qb.x * xs, qb.y * xs, qb.z * xs, qb.w * xs};
+              const float fa[4] = {da.x, da.y, da.z, da.w}, fb[4] = {db.x, db.y, db.z, db.w};
+              float wa[4], wb[4];
+              field_weights<BITS>(xa, fa, wa);
+              field_weights<BITS>(xb, fb, wb);
+              u32x4_t wq;
+#pragma unroll
+              for (int r2 = 0; r2 < 4; ++r2) wq[r2] = split_pack(wa[r2], wb[r2], neg_lo);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                if (t < t_begin || t >= t_end) continue;
+                const uint32_t w = reinterpret_cast<const uint32_t*>(
+                    kc_head + ((ch << 6) + 16 * t + col) * kRB + lg * (kQW * 4))[wk];
+                u32x4_t av;
+                if (kk % kStepsPerWord == 0) av = code_fields<BITS, 0>(w);
+                else av = code_fields<BITS, 1>(w);
+                sc[t] = mfma_f16(av, wq, sc[t]);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          join_tiles();
+          // whole scores, rounded once, back in units of 2^24 (kappa folded
+          // in and then zero): with scores this large, kappa - m rounded on
+          // its own would leave an error of ulp(kappa) in the largest score
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t) {
+            const float kp = DUAL ? kap[0] : kap[t / kSegTiles];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sc[t][i] = __builtin_amdgcn_ldexpf(
+                  __builtin_fmaf(__builtin_amdgcn_ldexpf(sc[t][i], e), kS, kp), -24);
+          }
+          kap[0] = 0.f;
+          kap[1] = 0.f;
+          cm = chunk_max();
+          need_m = __builtin_amdgcn_ballot_w64(cm > m + kSlack);
+        }
         if (need_v != 0) {
-          const int knew = 7 - __builtin_amdgcn_frexp_expf(wave_max(vmax));
-          const float f = __builtin_amdgcn_ldexpf(1.0f, knew - kexp);
+          const int knew = __builtin_amdgcn_readfirstlane(7 - __builtin_amdgcn_frexp_expf(wave_max(vmax)));
 #pragma unroll
           for (int n = 0; n < kNB; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[n][i] *= f;
+            for (int i = 0; i < 4; ++i) acc[n][i] = __builtin_amdgcn_ldexpf(acc[n][i], knew - kexp);
           kexp = knew;
-          set_vfk();
+          set_vke();
         }
         if (need_m != 0) {
           cm = max_xor16(cm);
@@ -687,8 +823,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         const int tok = 16 * t_own + 4 * lg;
         const float4 dv = *reinterpret_cast<const float4*>(&vpb[wave][0][tok]);
         const float4 zv = *reinterpret_cast<const float4*>(&vpb[wave][1][tok]);
-        const float ds[4] = {dv.x * vfk[0], dv.y * vfk[1], dv.z * vfk[2], dv.w * vfk[3]};
-        const float zs[4] = {zv.x, zv.y, zv.z, zv.w};
+        const float ds[4] = {__builtin_amdgcn_ldexpf(dv.x, vke[0]), __builtin_amdgcn_ldexpf(dv.y, vke[1]),
+                             __builtin_amdgcn_ldexpf(dv.z, vke[2]), __builtin_amdgcn_ldexpf(dv.w, vke[3])};
+        // group 1 of a half chunk has no tokens: its zero points are never
+        // written, so they are not read into z
+        const float zs[4] = {(HALF && grp) ? 0.f : zv.x, (HALF && grp) ? 0.f : zv.y,
+                             (HALF && grp) ? 0.f : zv.z, (HALF && grp) ? 0.f : zv.w};
         float pm[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -734,7 +874,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         const int tok = 16 * (is_lo ? t1 : t0) + 4 * lg;
         const float4 dv = *reinterpret_cast<const float4*>(&vpb[wave][0][tok]);
         const float4 zv = *reinterpret_cast<const float4*>(&vpb[wave][1][tok]);
-        const float ds[4] = {dv.x * vfk[0], dv.y * vfk[1], dv.z * vfk[2], dv.w * vfk[3]};
+        const float ds[4] = {__builtin_amdgcn_ldexpf(dv.x, vke[0]), __builtin_amdgcn_ldexpf(dv.y, vke[1]),
+                             __builtin_amdgcn_ldexpf(dv.z, vke[2]), __builtin_amdgcn_ldexpf(dv.w, vke[3])};
         const float zs[4] = {zv.x, zv.y, zv.z, zv.w};
         float pm[4];
 #pragma unroll
@@ -779,7 +920,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // by the wait on the LDS counter.
     auto run_chunk = [&](int64_t k, CR& r, auto half_tag, auto buf_tag) {
       __builtin_amdgcn_s_setprio(1);
-      process_chunk(r, half_tag, buf_tag);
+      process_chunk(r, gw + k * nw_row, half_tag, buf_tag);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       issue_batch(gw + (k + 2) * nw_row, k + 2 < wn, r, buf_tag);
       __builtin_amdgcn_s_setprio(0);
@@ -807,7 +948,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     wait_vmcnt<0>();
   }
   // ---- wave result
-  stash(s_o[wave], s_m[wave], s_l[wave], s_z[wave], __builtin_amdgcn_ldexpf(1.0f, 24 - kexp));
+  stash(s_o[wave], s_m[wave], s_l[wave], s_z[wave], 24 - kexp);
   __syncthreads();
   // ---- merge the four waves' quantized and exact-token states: the
   // weights 2^(m_j - M) of the eight states of each head once, then the

@@ -121,9 +121,10 @@ class Config:
 
 
 class Cache:
-    """Device buffers of one cache, zero-filled, in the layout of kvq.h."""
+    """Device buffers of one cache in the layout of kvq.h, zero-filled (or
+    every byte set to `fill`)."""
 
-    def __init__(self, cfg: Config, device="cuda"):
+    def __init__(self, cfg: Config, device="cuda", fill: int | None = None):
         B, H, D, G = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.group
         qc = cfg.qcap
         td = TORCH_DTYPE[cfg.dtype]
@@ -139,6 +140,11 @@ class Cache:
         self.v_sink = torch.zeros((B, H, cfg.sink, D), dtype=td, **z)
         self.k_resid = torch.zeros((B, H, cfg.residual + G, D), dtype=td, **z)
         self.v_resid = torch.zeros((B, H, cfg.residual + G, D), dtype=td, **z)
+        if fill is not None:
+            for n in self.BUFFERS:
+                t = getattr(self, n)
+                if t.numel():
+                    t.view(torch.uint8).fill_(fill)
 
     BUFFERS = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
                "k_sink", "v_sink", "k_resid", "v_resid")

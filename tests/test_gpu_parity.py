@@ -163,6 +163,143 @@ def test_constructed_edge_values(bits):
     compare_state(geo, read_state(cache), ref, T)
 
 
+
+# Attention on caches built from edge values, on both kernels.  Each path is
+# (Hq, Hkv, bits, G, D): the matrix-core kernel for GQA 8 (one and two key
+# groups per chunk) and for the dual-group GQA-4 form, the VALU kernel for
+# GQA 1 / 2 and for 8-bit codes.  T = 524 with S = 2, R = 32 leaves a
+# quantized count with Q % 64 == 32 at G = 32 (a half chunk / half value
+# block at the end).
+EDGE_PATHS = [
+    (8, 1, 4, 64, 128),
+    (8, 1, 2, 32, 64),
+    (4, 1, 2, 32, 128),
+    (4, 1, 4, 32, 64),
+    (1, 1, 4, 32, 128),
+    (2, 1, 2, 32, 64),
+    (8, 1, 8, 32, 128),
+]
+EDGE_KINDS = ["ties", "constant", "negzero", "ksub", "vtiny", "kwide", "kwide30", "vwide30",
+              "outlier300"]
+
+
+def _edge_inputs(kind, B, Hq, Hkv, D, G, S, T, bits, seed):
+    """fp32 K, V, q and the storage dtype of one edge-value case."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    K = rng.standard_normal((B, Hkv, T, D), dtype=f32)
+    V = rng.standard_normal((B, Hkv, T, D), dtype=f32)
+    q = rng.standard_normal((B, Hq, D), dtype=f32)
+    L = 2 ** bits - 1
+    dtype = "f32"
+    if kind == "ties":
+        # every quotient (x - min) / delta a half integer: delta = 1/16 with
+        # both 0 and L/16 present in every key group channel and value token
+        step = f32(2.0 ** -4)
+        K = (rng.integers(0, L, size=K.shape).astype(f32) + f32(0.5)) * step
+        V = (rng.integers(0, L, size=V.shape).astype(f32) + f32(0.5)) * step
+        for g0 in range(S, T, G):
+            K[:, :, g0] = 0
+            if g0 + 1 < T:
+                K[:, :, g0 + 1] = L * step
+        V[..., 0] = 0
+        V[..., 1] = L * step
+        dtype = "f16"
+    elif kind == "constant":
+        # every key group constant per channel, every value token constant
+        for g0 in range(S, T, G):
+            K[:, :, g0:g0 + G] = rng.standard_normal((B, Hkv, 1, D), dtype=f32)
+        V[:] = rng.standard_normal((B, Hkv, T, 1), dtype=f32)
+    elif kind == "negzero":
+        K = rng.uniform(0, 1, size=K.shape).astype(f32)
+        V = rng.uniform(0, 1, size=V.shape).astype(f32)
+        for g0 in range(S, T, G):
+            K[:, :, g0, ::3] = f32(-0.0)
+        V[..., 5] = f32(-0.0)
+    elif kind == "ksub":     # subnormal key range: scores ~ 0, uniform weights
+        K = rng.integers(0, 40, size=K.shape).astype(f32) * f32(2.0 ** -149)
+    elif kind == "vtiny":    # value deltas near 2^-120 (normal fp32)
+        V = V * f32(2.0 ** -118)
+    elif kind == "kwide":    # one key channel wide enough that q * delta > 65504
+        K[..., 7] *= f32(1e6)
+        dtype = "bf16"
+    elif kind == "kwide30":
+        K *= f32(1e30)
+    elif kind == "vwide30":
+        V *= f32(1e30)
+    elif kind == "outlier300":   # ten times the 70B-shaped workload's outliers
+        for h in range(Hkv):
+            K[:, h, :, rng.choice(D, 4, replace=False)] *= f32(300.0)
+        dtype = "bf16"
+    return {"K": synth.cast(K, dtype), "V": synth.cast(V, dtype), "q": synth.cast(q, dtype)}, dtype
+
+
+@pytest.mark.parametrize("kind", EDGE_KINDS)
+@pytest.mark.parametrize("path", EDGE_PATHS, ids=lambda c: "-".join(map(str, c)))
+def test_attention_on_edge_value_caches(kind, path):
+    """Ties, zero ranges, -0, subnormal key ranges, tiny value ranges, key
+    ranges that push q * delta past fp16's range, 1e30 keys and values, and
+    300x outlier channels: state bit-exact, attention within 2e-3 of the
+    oracle on every row, on each kernel path."""
+    kvq = _kvq()
+    Hq, Hkv, bits, G, D = path
+    B, S, R, T = 1, 2, 32, 524
+    log("edge", kind, path)
+    data, dt = _edge_inputs(kind, B, Hq, Hkv, D, G, S, T, bits, seed=11 + bits + D)
+    cfg, geo = make(_cfg_kw(B, Hkv, D, bits, G, S, R, T, dt))
+    cache = _run_prefill(kvq, cfg, data, T)
+    ref = O.prefill(geo, data["K"], data["V"], T)
+    compare_state(geo, read_state(cache), ref, T)
+    out = kvq.kvq_decode_attention(cfg, cache, T, to_dev(data["q"], dt)).cpu().numpy()
+    assert np.isfinite(out).all()
+    err = O.row_rel_error(out, O.decode(geo, ref, T, data["q"], Hq))
+    log("row rel err", err)
+    assert err <= ATOL_ROW_REL
+
+
+# Caches whose buffers start as 0xFF bytes (NaN as fp32): nothing the
+# kernels read outside the cache contents may reach the result.
+FILLED = [
+    # B, Hq, Hkv, D, bits, G, S, R, T, dtype
+    (1, 32, 8, 128, 2, 32, 4, 128, 1193, "bf16"),   # dual-group GQA 4, Q % 64 == 32
+    (1, 8, 1, 128, 4, 32, 4, 32, 580, "bf16"),      # GQA 8, G 32, half chunk
+    (1, 8, 1, 64, 2, 64, 4, 32, 600, "f16"),        # GQA 8, G 64
+    (1, 2, 2, 64, 2, 32, 0, 32, 323, "f16"),        # VALU 2-bit, G 32, half value block
+    (2, 16, 2, 64, 8, 64, 3, 64, 400, "f32"),       # VALU 8-bit
+    (1, 4, 1, 128, 4, 32, 4, 128, 100, "bf16"),     # nothing quantized yet
+]
+
+
+@pytest.mark.parametrize("case", FILLED, ids=lambda c: "-".join(map(str, c)))
+def test_unwritten_cache_bytes_never_reach_the_result(case):
+    kvq = _kvq()
+    B, Hq, Hkv, D, bits, G, S, R, T, dt = case
+    log("filled", case)
+    data = synth.random_case(sum(case[:9]), B, Hq, Hkv, D, T, dt)
+    cfg, geo = make(_cfg_kw(B, Hkv, D, bits, G, S, R, T + 70, dt))
+    cache = kvq.Cache(cfg, fill=0xFF)
+    kvq.prefill(cfg, cache, to_dev(data["K"], dt), to_dev(data["V"], dt), T)
+    ref = O.prefill(geo, data["K"], data["V"], T)
+    compare_state(geo, read_state(cache), ref, T)
+    q = to_dev(data["q"], dt)
+    out = kvq.kvq_decode_attention(cfg, cache, T, q).cpu().numpy()
+    assert O.row_rel_error(out, O.decode(geo, ref, T, data["q"], Hq)) <= ATOL_ROW_REL
+    # appends across the next freeze (the ring slots and the next group's
+    # parameters start as 0xFF too)
+    st = ref
+    Kd, Vd = to_dev(data["K"], dt), to_dev(data["V"], dt)
+    extra = synth.random_case(5 + T, B, Hq, Hkv, D, 70, dt)
+    kn, vn = to_dev(extra["K"], dt), to_dev(extra["V"], dt)
+    for i in range(70):
+        kvq.kvq_append_token(cfg, cache, T + i, kn[:, :, i], vn[:, :, i])
+        st = O.append(geo, st, T + i, extra["K"][:, :, i], extra["V"][:, :, i])
+    del Kd, Vd
+    T2 = T + 70
+    compare_state(geo, read_state(cache), st, T2)
+    out = kvq.kvq_decode_attention(cfg, cache, T2, q).cpu().numpy()
+    assert O.row_rel_error(out, O.decode(geo, st, T2, data["q"], Hq)) <= ATOL_ROW_REL
+
+
 STREAM = [
     # B, Hq, Hkv, D, bits, G, S, R, T0, steps, dtype
     (1, 2, 1, 64, 4, 32, 4, 32, 0, 140, "f32"),
@@ -173,6 +310,8 @@ STREAM = [
     (1, 16, 4, 128, 2, 32, 4, 128, 100, 140, "bf16"),   # matrix-core path, GQA 4
     (2, 16, 2, 64, 4, 64, 2, 0, 30, 150, "f16"),        # matrix-core path, GQA 8, R 0
     (2, 8, 2, 64, 4, 32, 2, 32, 60, 130, "f16"),        # dual-group GQA 4, 4-bit, half chunks
+    (1, 8, 1, 128, 4, 128, 4, 128, 250, 280, "bf16"),   # G 128 freezes at D 128 (largest LDS tile)
+    (2, 4, 2, 64, 2, 128, 0, 0, 100, 300, "f16"),       # G 128 freezes at D 64
 ]
 
 
@@ -204,23 +343,34 @@ def test_streaming_appends_match_oracle_every_step(case):
     compare_state(geo, read_state(fresh), st, Tmax)
 
 
-def test_split_count_invariance():
+@pytest.mark.parametrize("Hq", [8, 4])
+def test_split_count_invariance(Hq):
     """The log-sum-exp merge makes the result independent of the split count
-    up to fp32 rounding."""
+    up to fp32 rounding.  Workspaces with room for 1, 3, 17, 64 and 1024
+    splits per row: Q = 5856 quantized tokens (92 chunks of 64, the last a
+    half chunk; 183 value blocks of 32) with 148 exact tokens.  On a 256-CU
+    part the matrix-core path (Hq 8: GQA 4, dual-group form) then runs 1,
+    3, 16, 46 and 92 splits, the VALU path (Hq 4: GQA 2) 1, 3, 17, 46 and
+    46."""
     kvq = _kvq()
-    B, Hq, Hkv, D, bits, G, S, R, T, dt = (1, 8, 2, 128, 4, 32, 4, 128, 6000, "bf16")
+    B, Hkv, D, bits, G, S, R, T, dt = (1, 2, 128, 4, 32, 4, 128, 6000, "bf16")
     data = synth.random_case(99, B, Hq, Hkv, D, T, dt)
     cfg, geo = make(_cfg_kw(B, Hkv, D, bits, G, S, R, T, dt))
     cache = _run_prefill(kvq, cfg, data, T)
     q = to_dev(data["q"], dt)
     outs = []
-    for splits in (1024, 64, 100):
+    for splits in (1024, 1, 3, 17, 64):
         ws = torch.empty(cfg.workspace_bytes(Hq, splits), dtype=torch.uint8, device="cuda")
         outs.append(kvq.kvq_decode_attention(cfg, cache, T, q, workspace=ws).cpu().numpy())
+    # Split counts change the summation order, the running-max rescales and
+    # (one split) the length of each wave's accumulation chain; with the
+    # matrix-core path's ~22-bit fp16 high/low weights the rows agree to
+    # ~2e-5 (measured), well inside the parity bar checked below.
     for o in outs[1:]:
-        assert O.row_rel_error(o, outs[0]) < 1e-5
+        assert O.row_rel_error(o, outs[0]) < 1e-4
     ref = O.decode(geo, O.prefill(geo, data["K"], data["V"], T), T, data["q"], Hq)
-    assert O.row_rel_error(outs[0], ref) <= ATOL_ROW_REL
+    for o in outs:
+        assert O.row_rel_error(o, ref) <= ATOL_ROW_REL
 
 
 @pytest.mark.parametrize("fill", [0x00, 0xFF, "random"])
@@ -255,12 +405,6 @@ def _workload(name):
     return w, cfg_kw
 
 
-SAMPLE_ROWS = {
-    "mistral": [(0, 0), (1, 5), (2, 17), (3, 31)],
-    "llama70b": [(0, 0), (0, 13), (0, 38), (0, 63)],
-}
-
-
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_prefill_bit_exact_and_attention(name):
     kvq = _kvq()
@@ -275,13 +419,7 @@ def test_workload_prefill_bit_exact_and_attention(name):
     log("state bit-exact")
     q = to_dev(data["q"], w.dtype)
     out = kvq.kvq_decode_attention(cfg, cache, T, q).cpu().numpy()
-    rows = SAMPLE_ROWS.get(name)
-    exp = O.decode(geo, ref, T, data["q"], w.n_q_heads, rows=rows)
-    if rows is not None:
-        idx = tuple(np.array(rows).T)
-        err = O.row_rel_error(out[idx], exp[idx])
-    else:
-        err = O.row_rel_error(out, exp)
+    err = O.row_rel_error(out, O.decode(geo, ref, T, data["q"], w.n_q_heads))   # every row
     log("row rel err", err)
     assert err <= ATOL_ROW_REL
 
@@ -290,7 +428,8 @@ def test_workload_prefill_bit_exact_and_attention(name):
 def test_workload_streaming(name):
     """The streaming workloads: append + attention per step, the state
     checked against the oracle's append path at the steps around both group
-    freezes, attention at those steps (sampled rows for the 70B shape)."""
+    freezes (every step for the GPT-2 shape), attention on every row at
+    those steps."""
     kvq = _kvq()
     w, kw = _workload(name)
     log("workload", name)
@@ -309,7 +448,6 @@ def test_workload_streaming(name):
     check = set([1, w.steps] + flush_steps + [s + 1 for s in flush_steps if s < w.steps])
     if name == "gpt2":
         check = set(range(1, w.steps + 1))
-    rows = SAMPLE_ROWS.get(name)
     for i in range(w.steps):
         n = T0 + i
         kvq.kvq_append_token(cfg, cache, n, kn[i], vn[i])
@@ -319,10 +457,5 @@ def test_workload_streaming(name):
             log("step", i + 1)
             compare_state(geo, read_state(cache), st, n + 1)
             o = out.cpu().numpy()
-            exp = O.decode(geo, st, n + 1, data["q_new"][i], w.n_q_heads, rows=rows)
-            if rows is not None:
-                idx = tuple(np.array(rows).T)
-                err = O.row_rel_error(o[idx], exp[idx])
-            else:
-                err = O.row_rel_error(o, exp)
+            err = O.row_rel_error(o, O.decode(geo, st, n + 1, data["q_new"][i], w.n_q_heads))
             assert err <= ATOL_ROW_REL, (i + 1, err)

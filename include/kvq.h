@@ -245,6 +245,30 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, i
                                 int32_t n_q_heads, kvq_tensor q, float softmax_scale, float *out,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kvq_decode_attention_noalloc: kvq_decode_attention without a workspace
+ * argument, for callers that cannot allocate device memory (code under
+ * stream / graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It allocates nothing and frees nothing.  The split partials
+ * go to a device array inside the library of KVQ_NOALLOC_SCRATCH_BYTES
+ * bytes, one per GPU the library runs on, held until the process ends;
+ * the result equals kvq_decode_attention's with a workspace of that size.
+ *   Limit: one split per (batch, query head) must fit, i.e.
+ *   kvq_workspace_bytes_min(cfg, n_q_heads) <= KVQ_NOALLOC_SCRATCH_BYTES
+ *   (B * n_q_heads * (D + 2) * 4 bytes); larger calls return
+ *   KVQ_EWORKSPACE before any work is enqueued.
+ *   Sharing: every call on one GPU uses that GPU's array and leaves its
+ *   partials there (they need no clearing).  Calls that can overlap in time
+ *   on one GPU (on different streams) race on it and must be ordered by
+ *   the caller.
+ * Arguments and other errors as kvq_decode_attention; KVQ_EHIP also when
+ * the array's device address cannot be obtained.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_config *cfg, const kvq_cache *cache,
+                                        int64_t n_tokens, int32_t n_q_heads, kvq_tensor q,
+                                        float softmax_scale, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

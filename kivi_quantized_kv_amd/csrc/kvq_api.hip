@@ -231,123 +231,194 @@ extern "C" kvq_status kvq_append_token(const kvq_config* cfg, const kvq_cache* c
   }
 }
 
+namespace {
+
+// Argument checks of decode attention that need no workspace.
+kvq_status check_decode_args(const kvq_config* cfg, const kvq_cache* cache, int64_t n_tokens,
+                             int32_t n_q_heads, const kvq_tensor& q, float softmax_scale,
+                             const float* out) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if ((st = check_tensor(q, cfg->dtype, false)) != KVQ_OK) return st;
+  if (!out || !aligned16(out)) return KVQ_EINVAL;
+  if (n_q_heads < 1 || n_q_heads % cfg->n_kv_heads) return KVQ_EINVAL;
+  if (n_tokens < 1) return KVQ_EINVAL;
+  if (n_tokens > cfg->capacity) return KVQ_ECAPACITY;
+  if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale)) return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+// Decode attention after the argument checks, with the split partials in
+// `workspace` (workspace_bytes bytes, 16-byte aligned).
+kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64_t n_tokens,
+                            int32_t n_q_heads, const kvq_tensor& q, float softmax_scale, float* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const int B = cfg->batch, H = cfg->n_kv_heads, D = cfg->head_dim;
+  const int64_t S = cfg->sink, R = cfg->residual, G = cfg->group;
+  const int64_t T = n_tokens;
+  const int64_t Q = quantized_count(T, S, R, G);
+  const int64_t n_sink = T < S ? T : S;
+  const int64_t n_res = T > S ? T - S - Q : 0;
+  const int64_t n_fp = n_sink + n_res;
+  const int64_t per_split_bytes = int64_t(B) * n_q_heads * (D + 2) * 4;
+  int64_t cap_splits = int64_t(workspace_bytes) / per_split_bytes;
+  if (cap_splits > KVQ_MAX_SPLITS) cap_splits = KVQ_MAX_SPLITS;
+  if (int64_t(workspace_bytes) < kvq_workspace_bytes_min(cfg, n_q_heads) || cap_splits < 1)
+    return KVQ_EWORKSPACE;
+
+  // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit
+  // codes, once at least one token is quantized (its chunk loads assume a
+  // chunk 0).  It works per KV head on 64-token chunks, with the grid sized
+  // to one round of two workgroups per CU, and spreads the full-precision
+  // tokens evenly over its splits.  Everything else runs the VALU kernel
+  // per query head on value-code blocks, again with the full-precision
+  // tokens spread evenly over the splits.
+  const int gqa = n_q_heads / H;
+  const bool mfma = (gqa == 4 || gqa == 8) && cfg->bits != 8 && Q > 0;
+  const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
+  const int64_t nblk = (Q + L - 1) / L;
+  int64_t fp_per_split = 32;
+  int64_t bps = 1;
+  int64_t n_split = 0;
+  bool direct = false;
+  if (mfma) {
+    const int64_t slots = 2 * int64_t(device_cu_count());
+    const int64_t rows = int64_t(B) * H;
+    int64_t want = slots / rows > 0 ? slots / rows : 1;
+    if (want > nblk) want = nblk;
+    if (want > cap_splits) want = cap_splits;
+    bps = want > 0 ? (nblk + want - 1) / want : 1;
+    n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
+    // at most ~64 exact tokens per split: splits past the chunks, if any,
+    // take exact tokens only
+    int64_t want_fp = (n_fp + 63) / 64;
+    if (want_fp > cap_splits) want_fp = cap_splits;
+    if (n_split < want_fp) n_split = want_fp;
+    if (n_split < 1) n_split = 1;
+    fp_per_split = (n_fp + n_split - 1) / n_split;
+  } else if (direct_rows(int64_t(B) * n_q_heads) && dispatch3<AttnValuDirectOkFn>(cfg)) {
+    // the rows alone fill the GPU: one 16-wave workgroup per row takes
+    // all of its tokens, merges in LDS and writes the output
+    direct = true;
+    n_split = 1;
+    bps = nblk > 0 ? nblk : 1;
+    fp_per_split = n_fp > 0 ? n_fp : 1;
+  } else {
+    // one round of resident workgroups, at least one block per wave
+    const int64_t slots = int64_t(dispatch3<AttnValuOccFn>(cfg)) * device_cu_count();
+    const int64_t rows = int64_t(B) * n_q_heads;
+    int64_t want = slots / rows > 0 ? slots / rows : 1;
+    if (want > (nblk + 3) / 4) want = (nblk + 3) / 4;
+    if (want > cap_splits) want = cap_splits;
+    bps = want > 0 ? (nblk + want - 1) / want : 1;
+    n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
+    int64_t want_fp = (n_fp + 63) / 64;
+    if (want_fp > cap_splits) want_fp = cap_splits;
+    if (n_split < want_fp) n_split = want_fp;
+    if (n_split < 1) n_split = 1;
+    fp_per_split = (n_fp + n_split - 1) / n_split;
+  }
+  AttnArgs a{};
+  a.k_codes = cache->k_codes; a.v_codes = cache->v_codes;
+  a.k_scale = cache->k_scale; a.k_zero = cache->k_zero;
+  a.v_scale = cache->v_scale; a.v_zero = cache->v_zero;
+  a.k_sink = cache->k_sink; a.v_sink = cache->v_sink;
+  a.k_resid = cache->k_resid; a.v_resid = cache->v_resid;
+  a.q = q.ptr; a.q_sb = q.stride_b; a.q_sh = q.stride_h;
+  a.ws = reinterpret_cast<float*>(workspace);
+  a.out = out;
+  const double scale = softmax_scale > 0 ? double(softmax_scale) : 1.0 / std::sqrt(double(D));
+  a.sm_scale_log2 = float(scale * 1.4426950408889634);
+  a.T = T; a.S = S; a.Q = Q; a.qcap = kvq_qcap(cfg); a.ring = R + G;
+  a.first_resid = S + Q; a.n_sink = n_sink; a.n_fp = n_fp;
+  a.kgroups = kvq_qcap(cfg) / G;
+  a.resid_slot0 = Q % (R + G);
+  a.H = H; a.Hq = n_q_heads; a.gqa = n_q_heads / H; a.G = int(G);
+  a.g_shift = G == 32 ? 5 : (G == 64 ? 6 : 7);
+  a.n_split = int(n_split);
+  a.direct = direct ? 1 : 0;
+  a.blocks_per_split = int(bps);
+  a.fp_per_split = int(fp_per_split);
+  a.ml_offset = int64_t(B) * n_q_heads * n_split * D;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t ea = hipSuccess;
+  if (a.n_split > 0) {
+    if (mfma && gqa == 8) ea = dispatch3<AttnMfma8Fn>(cfg, a, B, s);
+    else if (mfma) ea = dispatch3<AttnMfma4Fn>(cfg, a, B, s);
+    else ea = dispatch3<AttnValuFn>(cfg, a, B, s);
+  }
+  if (ea != hipSuccess) return KVQ_EHIP;
+  if (direct) return KVQ_OK;
+  hipError_t e;
+  if (cfg->dtype == KVQ_F32) e = D == 64 ? launch_merge<DT_F32, 64>(a, B, s) : launch_merge<DT_F32, 128>(a, B, s);
+  else if (cfg->dtype == KVQ_F16) e = D == 64 ? launch_merge<DT_F16, 64>(a, B, s) : launch_merge<DT_F16, 128>(a, B, s);
+  else e = D == 64 ? launch_merge<DT_BF16, 64>(a, B, s) : launch_merge<DT_BF16, 128>(a, B, s);
+  if (e != hipSuccess) return KVQ_EHIP;
+  return KVQ_OK;
+}
+
+}  // namespace
+
 extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                            int64_t n_tokens, int32_t n_q_heads, kvq_tensor q,
                                            float softmax_scale, float* out, void* workspace,
                                            size_t workspace_bytes, void* stream) {
   try {
-    kvq_status st = check_config(cfg);
+    kvq_status st = check_decode_args(cfg, cache, n_tokens, n_q_heads, q, softmax_scale, out);
     if (st != KVQ_OK) return st;
-    if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
-    if ((st = check_tensor(q, cfg->dtype, false)) != KVQ_OK) return st;
-    if (!out || !workspace || !aligned16(out) || !aligned16(workspace)) return KVQ_EINVAL;
-    if (n_q_heads < 1 || n_q_heads % cfg->n_kv_heads) return KVQ_EINVAL;
-    if (n_tokens < 1) return KVQ_EINVAL;
-    if (n_tokens > cfg->capacity) return KVQ_ECAPACITY;
-    if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale)) return KVQ_EINVAL;
+    if (!workspace || !aligned16(workspace)) return KVQ_EINVAL;
+    return decode_attention(cfg, cache, n_tokens, n_q_heads, q, softmax_scale, out, workspace,
+                            workspace_bytes, stream);
+  } catch (...) {
+    return KVQ_EINVAL;
+  }
+}
 
-    const int B = cfg->batch, H = cfg->n_kv_heads, D = cfg->head_dim;
-    const int64_t S = cfg->sink, R = cfg->residual, G = cfg->group;
-    const int64_t T = n_tokens;
-    const int64_t Q = quantized_count(T, S, R, G);
-    const int64_t n_sink = T < S ? T : S;
-    const int64_t n_res = T > S ? T - S - Q : 0;
-    const int64_t n_fp = n_sink + n_res;
-    const int64_t per_split_bytes = int64_t(B) * n_q_heads * (D + 2) * 4;
-    int64_t cap_splits = int64_t(workspace_bytes) / per_split_bytes;
-    if (cap_splits > KVQ_MAX_SPLITS) cap_splits = KVQ_MAX_SPLITS;
-    if (int64_t(workspace_bytes) < kvq_workspace_bytes_min(cfg, n_q_heads) || cap_splits < 1)
+// ---------------------------------------------------------------------------
+// Decode attention without a caller workspace: the split partials live in a
+// file-scope device array of KVQ_NOALLOC_SCRATCH_BYTES, one per GPU the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and cached.  The partials
+// need no clearing (every split writes its own before the merge reads it).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's copy of `scratch`, or null on failure.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);   // same value from any racing thread
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* cache,
+                                                   int64_t n_tokens, int32_t n_q_heads,
+                                                   kvq_tensor q, float softmax_scale, float* out,
+                                                   void* stream) {
+  try {
+    kvq_status st = check_decode_args(cfg, cache, n_tokens, n_q_heads, q, softmax_scale, out);
+    if (st != KVQ_OK) return st;
+    // one split per (batch, q head) must fit the array
+    if (kvq_workspace_bytes_min(cfg, n_q_heads) > int64_t(KVQ_NOALLOC_SCRATCH_BYTES))
       return KVQ_EWORKSPACE;
-
-    // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit
-    // codes, once at least one token is quantized (its chunk loads assume a
-    // chunk 0).  It works per KV head on 64-token chunks, with the grid sized
-    // to one round of two workgroups per CU, and spreads the full-precision
-    // tokens evenly over its splits.  Everything else runs the VALU kernel
-    // per query head on value-code blocks, again with the full-precision
-    // tokens spread evenly over the splits.
-    const int gqa = n_q_heads / H;
-    const bool mfma = (gqa == 4 || gqa == 8) && cfg->bits != 8 && Q > 0;
-    const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
-    const int64_t nblk = (Q + L - 1) / L;
-    int64_t fp_per_split = 32;
-    int64_t bps = 1;
-    int64_t n_split = 0;
-    bool direct = false;
-    if (mfma) {
-      const int64_t slots = 2 * int64_t(device_cu_count());
-      const int64_t rows = int64_t(B) * H;
-      int64_t want = slots / rows > 0 ? slots / rows : 1;
-      if (want > nblk) want = nblk;
-      if (want > cap_splits) want = cap_splits;
-      bps = want > 0 ? (nblk + want - 1) / want : 1;
-      n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
-      // at most ~64 exact tokens per split: splits past the chunks, if any,
-      // take exact tokens only
-      int64_t want_fp = (n_fp + 63) / 64;
-      if (want_fp > cap_splits) want_fp = cap_splits;
-      if (n_split < want_fp) n_split = want_fp;
-      if (n_split < 1) n_split = 1;
-      fp_per_split = (n_fp + n_split - 1) / n_split;
-    } else if (direct_rows(int64_t(B) * n_q_heads) && dispatch3<AttnValuDirectOkFn>(cfg)) {
-      // the rows alone fill the GPU: one 16-wave workgroup per row takes
-      // all of its tokens, merges in LDS and writes the output
-      direct = true;
-      n_split = 1;
-      bps = nblk > 0 ? nblk : 1;
-      fp_per_split = n_fp > 0 ? n_fp : 1;
-    } else {
-      // one round of resident workgroups, at least one block per wave
-      const int64_t slots = int64_t(dispatch3<AttnValuOccFn>(cfg)) * device_cu_count();
-      const int64_t rows = int64_t(B) * n_q_heads;
-      int64_t want = slots / rows > 0 ? slots / rows : 1;
-      if (want > (nblk + 3) / 4) want = (nblk + 3) / 4;
-      if (want > cap_splits) want = cap_splits;
-      bps = want > 0 ? (nblk + want - 1) / want : 1;
-      n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
-      int64_t want_fp = (n_fp + 63) / 64;
-      if (want_fp > cap_splits) want_fp = cap_splits;
-      if (n_split < want_fp) n_split = want_fp;
-      if (n_split < 1) n_split = 1;
-      fp_per_split = (n_fp + n_split - 1) / n_split;
-    }
-    AttnArgs a{};
-    a.k_codes = cache->k_codes; a.v_codes = cache->v_codes;
-    a.k_scale = cache->k_scale; a.k_zero = cache->k_zero;
-    a.v_scale = cache->v_scale; a.v_zero = cache->v_zero;
-    a.k_sink = cache->k_sink; a.v_sink = cache->v_sink;
-    a.k_resid = cache->k_resid; a.v_resid = cache->v_resid;
-    a.q = q.ptr; a.q_sb = q.stride_b; a.q_sh = q.stride_h;
-    a.ws = reinterpret_cast<float*>(workspace);
-    a.out = out;
-    const double scale = softmax_scale > 0 ? double(softmax_scale) : 1.0 / std::sqrt(double(D));
-    a.sm_scale_log2 = float(scale * 1.4426950408889634);
-    a.T = T; a.S = S; a.Q = Q; a.qcap = kvq_qcap(cfg); a.ring = R + G;
-    a.first_resid = S + Q; a.n_sink = n_sink; a.n_fp = n_fp;
-    a.kgroups = kvq_qcap(cfg) / G;
-    a.resid_slot0 = Q % (R + G);
-    a.H = H; a.Hq = n_q_heads; a.gqa = n_q_heads / H; a.G = int(G);
-    a.g_shift = G == 32 ? 5 : (G == 64 ? 6 : 7);
-    a.n_split = int(n_split);
-    a.direct = direct ? 1 : 0;
-    a.blocks_per_split = int(bps);
-    a.fp_per_split = int(fp_per_split);
-    a.ml_offset = int64_t(B) * n_q_heads * n_split * D;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t ea = hipSuccess;
-    if (a.n_split > 0) {
-      if (mfma && gqa == 8) ea = dispatch3<AttnMfma8Fn>(cfg, a, B, s);
-      else if (mfma) ea = dispatch3<AttnMfma4Fn>(cfg, a, B, s);
-      else ea = dispatch3<AttnValuFn>(cfg, a, B, s);
-    }
-    if (ea != hipSuccess) return KVQ_EHIP;
-    if (direct) return KVQ_OK;
-    hipError_t e;
-    if (cfg->dtype == KVQ_F32) e = D == 64 ? launch_merge<DT_F32, 64>(a, B, s) : launch_merge<DT_F32, 128>(a, B, s);
-    else if (cfg->dtype == KVQ_F16) e = D == 64 ? launch_merge<DT_F16, 64>(a, B, s) : launch_merge<DT_F16, 128>(a, B, s);
-    else e = D == 64 ? launch_merge<DT_BF16, 64>(a, B, s) : launch_merge<DT_BF16, 128>(a, B, s);
-    if (e != hipSuccess) return KVQ_EHIP;
-    return KVQ_OK;
+    void* ws = scratch_address();
+    if (!ws) return KVQ_EHIP;
+    return decode_attention(cfg, cache, n_tokens, n_q_heads, q, softmax_scale, out, ws,
+                            KVQ_NOALLOC_SCRATCH_BYTES, stream);
   } catch (...) {
     return KVQ_EINVAL;
   }

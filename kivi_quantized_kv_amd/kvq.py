@@ -20,8 +20,9 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
 STATUS = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_EUNSUPPORTED", 3: "KVQ_ECAPACITY",
           4: "KVQ_EWORKSPACE", 5: "KVQ_EHIP"}
 MAX_SPLITS = 1024
+NOALLOC_SCRATCH_BYTES = 16 << 20
 EXPORTS = ("kvq_quantize_keys", "kvq_quantize_values", "kvq_append_token",
-           "kvq_decode_attention")
+           "kvq_decode_attention", "kvq_decode_attention_noalloc")
 
 
 class KvqError(RuntimeError):
@@ -71,6 +72,9 @@ def load_library(path: str | None = None):
     lib.kvq_decode_attention.argtypes = [P(c_config), P(c_cache), ctypes.c_int64, ctypes.c_int32,
                                          c_tensor, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]
+    lib.kvq_decode_attention_noalloc.argtypes = [P(c_config), P(c_cache), ctypes.c_int64,
+                                                 ctypes.c_int32, c_tensor, ctypes.c_float,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
     for fn in EXPORTS:
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -246,6 +250,20 @@ def kvq_decode_attention(cfg: Config, cache: Cache, n_tokens: int, q: torch.Tens
            lib.kvq_decode_attention(c, cc, n_tokens, Hq, tensor(q),
                                     float(softmax_scale), out.data_ptr(), workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
+    return out
+
+
+def kvq_decode_attention_noalloc(cfg: Config, cache: Cache, n_tokens: int, q: torch.Tensor,
+                                 out: torch.Tensor, softmax_scale: float = 0.0,
+                                 stream=None) -> torch.Tensor:
+    """Decode attention with the library's own split buffer; `out` is
+    caller-provided ([B][Hq][D] fp32), so nothing is allocated here either."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    c, cc = cfg._cref(), cache._cref()
+    _check("kvq_decode_attention_noalloc",
+           lib.kvq_decode_attention_noalloc(c, cc, n_tokens, Hq, tensor(q), float(softmax_scale),
+                                            out.data_ptr(), _stream(stream, q.device)))
     return out
 
 

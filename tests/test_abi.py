@@ -133,3 +133,20 @@ def test_validation_rejects_bad_arguments_without_launching():
     cfg3 = kvq.Config(1, 3, 64, 4, 32, 4, 32, 256, "f16").c()
     assert lib.kvq_decode_attention(ctypes.byref(cfg3), ctypes.byref(cache), 10, 4, t, 0.0,
                                     fake, fake, ws, s) == 1   # 4 q heads over 3 KV heads
+    # decode attention without a workspace: same checks, plus the limit of
+    # the library's own split buffer (one split per row must fit)
+    assert lib.kvq_decode_attention_noalloc(ctypes.byref(good), ctypes.byref(cache), 0, 4, t, 0.0,
+                                            fake, s) == 1
+    assert lib.kvq_decode_attention_noalloc(ctypes.byref(good), ctypes.byref(cache), 10, 4, t, 0.0,
+                                            None, s) == 1
+    big = kvq.Config(1000, 1, 128, 4, 32, 4, 32, 256, "f16")   # 1000 x 64 rows x 520 B > 16 MiB
+    assert big.workspace_bytes(64, 1) > kvq.NOALLOC_SCRATCH_BYTES
+    assert lib.kvq_decode_attention_noalloc(ctypes.byref(big.c()), ctypes.byref(cache), 10, 64,
+                                            kvq.c_tensor(fake, 64 * 128, 128, 0), 0.0, fake, s) == 4
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define KVQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    from kivi_quantized_kv_amd import kvq
+    assert m and int(m.group(1)) << int(m.group(2)) == kvq.NOALLOC_SCRATCH_BYTES

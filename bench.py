@@ -2,14 +2,18 @@
 
 One step = one pass of the whole hot path for one layer: kvq_append_token
 (write the new K/V token, freezing a key group when the residual window
-fills) followed by kvq_decode_attention over the whole packed cache.  The
-default workload is the long-context 70B-shaped layer (B 1, 64 q heads,
+fills) followed by kvq_decode_attention over the whole packed cache; for a
+workload that does not stream (a fixed cache), the attention call alone.
+The default workload is the long-context 70B-shaped layer (B 1, 64 q heads,
 8 KV heads, head_dim 128, 131072 cached tokens, bf16 inputs, int4, G 64,
 R 128, 4 sinks).  Steps rotate over several layer caches whose total size
 exceeds the last-level cache, so every attention call streams its packed
 cache from HBM as in a real multi-layer decode.
 
-Prints one JSON line (metric, value, roofline, cpu_baseline, ...).
+Before the warmup it times the prefill (both quantize entry points) and
+the append on its own (a plain one and one that freezes a group); after the
+timed steps it times the attention call alone.  Prints one JSON line
+(metric, value, roofline, cpu_baseline, detail).
 """
 from __future__ import annotations
 
@@ -92,30 +96,84 @@ def algorithmic_bytes(w, T: int) -> int:
     return per_head * w.batch * w.n_kv_heads
 
 
+def prefill_bytes(w, T: int) -> int:
+    """Bytes a prefill of T tokens moves: K and V read in the input dtype,
+    packed codes, key group and value token (delta, zero) pairs and the
+    exact sink / residual rows written."""
+    ns, Q, nr = partition(T, w.sink, w.residual, w.group)
+    D, b = w.head_dim, w.bits
+    eb = 4 if w.dtype == "f32" else 2
+    per_head = (2 * T * D * eb + 2 * Q * D * b // 8 + (Q // w.group) * D * 8 + Q * 8
+                + 2 * (ns + nr) * D * eb)
+    return per_head * w.batch * w.n_kv_heads
+
+
+def decode_splits(w, T: int, cus: int, ws_splits: int = 1024) -> int:
+    """Split count of one decode call, by the launch rule of the library's
+    host code (matrix-core path: one round of two workgroups per CU over
+    64-token chunks; VALU path: see kvq_api.hip), for the split-partial
+    byte count."""
+    ns, Q, nr = partition(T, w.sink, w.residual, w.group)
+    n_fp = ns + nr
+    if w.gqa in (4, 8) and w.bits != 8 and Q > 0:
+        nblk = -(-Q // 64)
+        want = max(1, 2 * cus // (w.batch * w.n_kv_heads))
+        want = min(want, nblk, ws_splits)
+        bps = -(-nblk // want)
+        n_split = -(-nblk // bps)
+        return max(n_split, min(-(-n_fp // 64), ws_splits), 1)
+    return None
+
+
 def cpu_baseline(w, data, sample_seconds: float):
-    """Time the CPU oracle on a bounded sample of the same step: the decode
-    attention of the q heads of one KV head (append is negligible), scaled
-    to the whole step.  BLAS pools pinned to one thread."""
+    """Time the CPU oracle on a bounded sample of the same work, with BLAS
+    pools pinned to one thread: the prefill and the appends (plain and
+    freezing) of one KV head, and the decode attention of the q heads of
+    one KV head, each scaled to the whole layer.  The reported value is
+    tokens/s of one step (append + attention when the workload streams)."""
     from threadpoolctl import threadpool_limits
     from oracle import kvq_oracle as O
 
     T = w.n_tokens
     geo = O.CacheGeometry(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink,
                           w.residual, w.capacity, w.dtype)
-    t0 = time.time()
-    st = O.prefill(geo, data["K"], data["V"], T)
-    log(f"oracle prefill {time.time() - t0:.1f}s")
+    geo1 = O.CacheGeometry(w.batch, 1, w.head_dim, w.bits, w.group, w.sink, w.residual,
+                           T + max(w.steps, 2 * w.group + w.residual + 1), w.dtype)
     g = w.gqa
     rows = [(0, h) for h in range(g)]          # the q heads of KV head 0
-    times = []
     with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        st1 = O.prefill(geo1, data["K"][:, :1], data["V"][:, :1], T)
+        prefill_s = (time.perf_counter() - t0) * w.n_kv_heads
+        # appends on the one-head state: plain ones up to the next freeze,
+        # then the freezing one
+        n = T
+        plain, freeze = [], []
+        while True:
+            q0 = partition(n, w.sink, w.residual, w.group)[1]
+            q1 = partition(n + 1, w.sink, w.residual, w.group)[1]
+            kn = data["k_new"][(n - T) % len(data["k_new"])][:, :1]
+            vn = data["v_new"][(n - T) % len(data["v_new"])][:, :1]
+            t0 = time.perf_counter()
+            st1 = O.append(geo1, st1, n, kn, vn)
+            (freeze if q1 > q0 else plain).append(time.perf_counter() - t0)
+            n += 1
+            if freeze:
+                break
+        append_plain_s = sum(plain) / max(1, len(plain)) * w.n_kv_heads
+        append_freeze_s = freeze[0] * w.n_kv_heads
+        st = O.prefill(geo, data["K"], data["V"], T)
+        times = []
         t_end = time.time() + sample_seconds
         while time.time() < t_end or not times:
             t0 = time.perf_counter()
             O.decode(geo, st, T, data["q"], w.n_q_heads, rows=rows)
             times.append(time.perf_counter() - t0)
     per_kv_head = sum(times) / len(times)
-    step_s = per_kv_head * w.n_kv_heads * w.batch
+    decode_s = per_kv_head * w.n_kv_heads * w.batch
+    # an append at the natural freeze rate (one freeze per G steps)
+    append_s = (append_plain_s * (w.group - 1) + append_freeze_s) / w.group if w.steps else 0.0
+    step_s = decode_s + append_s
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as fh:
@@ -125,10 +183,20 @@ def cpu_baseline(w, data, sample_seconds: float):
     return {
         "value": w.batch / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
         "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
-        "sample": (f"oracle decode attention (fp64, dequantize then attend) for the {g} q heads "
-                   f"of one KV head at T={T}, {len(times)} runs, mean {per_kv_head:.3f}s, "
-                   f"scaled x{w.n_kv_heads * w.batch} to one step; append not timed"),
+        "prefill_s": round(prefill_s, 3), "append_plain_s": round(append_plain_s, 5),
+        "append_freeze_s": round(append_freeze_s, 4), "decode_s": round(decode_s, 3),
+        "sample": (f"oracle (fp32 quantize, fp64 dequantize then attend), one thread: prefill, "
+                   f"{len(plain)} plain appends and one freezing append of KV head 0, scaled "
+                   f"x{w.n_kv_heads}; decode attention for the {g} q heads of KV head 0 at T={T}, "
+                   f"{len(times)} runs, mean {per_kv_head:.3f}s, scaled x{w.n_kv_heads * w.batch}; "
+                   + ("step = decode + append at one freeze per G steps" if w.steps
+                      else "step = decode (the workload does not stream)")),
     }
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
 def main():
@@ -157,16 +225,18 @@ def main():
 
     kvq.load_library()
     w = synth.WORKLOADS[args.workload]
+    streaming = w.steps > 0
     n_layers = max(1, args.layers)
-    # warmup and the timed steps (the per-call timing appends nothing)
-    per_layer_steps = -(-(args.steps + args.warmup) // n_layers)
+    per_layer_steps = -(-(args.steps + args.warmup) // n_layers) if streaming else 0
     n_gen = max(w.steps, 64)                    # distinct appended tokens / queries
-    steps_cap = max(n_gen, per_layer_steps)
+    # room for the timed steps and for the append timings (up to two freezes ahead)
+    steps_cap = max(n_gen, per_layer_steps, 2 * w.group + w.residual + 2)
     t0 = time.time()
     data = synth.generate(w, steps=n_gen)
     log(f"inputs generated in {time.time() - t0:.1f}s")
     cfg = kvq.Config(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink, w.residual,
                      w.n_tokens + steps_cap, w.dtype)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def dev(a):
         if w.dtype == "bf16":
@@ -175,8 +245,20 @@ def main():
 
     K, V = dev(data["K"]), dev(data["V"])
     kn, vn, qn = dev(data["k_new"]), dev(data["v_new"]), dev(data["q_new"])
+    T0 = w.n_tokens
     layers = [kvq.Cache(cfg)]
-    kvq.prefill(cfg, layers[0], K, V, w.n_tokens)
+    # prefill of the first layer cache, timed (both halves; the first run
+    # also settles the clocks)
+    pre_ms = []
+    for _ in range(4):
+        e0, e1 = _events()
+        torch.cuda.synchronize()
+        e0.record()
+        kvq.prefill(cfg, layers[0], K, V, T0)
+        e1.record()
+        torch.cuda.synchronize()
+        pre_ms.append(e0.elapsed_time(e1))
+    prefill_ms = float(np.median(pre_ms[1:]))
     for _ in range(1, n_layers):
         c = kvq.Cache(cfg)
         for name in kvq.Cache.BUFFERS:
@@ -184,22 +266,53 @@ def main():
         layers.append(c)
     del K, V
     torch.cuda.synchronize()
-    log(f"{n_layers} layer caches of {layers[0].nbytes() / 2**20:.1f} MiB prefilled")
+    log(f"{n_layers} layer caches of {layers[0].nbytes() / 2**20:.1f} MiB prefilled "
+        f"(prefill {prefill_ms * 1e3:.1f} us)")
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     ws = torch.empty(cfg.workspace_bytes(w.n_q_heads), dtype=torch.uint8, device="cuda")
-    n_tok = [w.n_tokens] * n_layers
+
+    # Append timings on a scratch copy of the first cache: a plain append and
+    # a freezing one, each repeated back to back (a repeated append rewrites
+    # the same slot and group with the same data).
+    scratch = kvq.Cache(cfg)
+    for name in kvq.Cache.BUFFERS:
+        getattr(scratch, name).copy_(getattr(layers[0], name))
+    n = T0
+    while partition(n + 1, w.sink, w.residual, w.group)[1] == partition(n, w.sink, w.residual, w.group)[1]:
+        kvq.kvq_append_token(cfg, scratch, n, kn[(n - T0) % n_gen], vn[(n - T0) % n_gen])
+        n += 1
+    n_freeze, n_plain = n, n - 1
+
+    def time_appends(nb, reps):
+        j = (nb - T0) % n_gen
+        e0, e1 = _events()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            kvq.kvq_append_token(cfg, scratch, nb, kn[j], vn[j])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    append_plain_us = time_appends(n_plain, 200) if n_plain >= T0 else None
+    append_freeze_us = time_appends(n_freeze, 100)
+    del scratch
+    torch.cuda.synchronize()
+
+    n_tok = [T0] * n_layers
 
     def step(i):
         li = i % n_layers
-        j = (n_tok[li] - w.n_tokens) % n_gen
-        kvq.kvq_append_token(cfg, layers[li], n_tok[li], kn[j], vn[j])
-        n_tok[li] += 1
+        j = (n_tok[li] - T0) % n_gen
+        if streaming:
+            kvq.kvq_append_token(cfg, layers[li], n_tok[li], kn[j], vn[j])
+            n_tok[li] += 1
         kvq.kvq_decode_attention(cfg, layers[li], n_tok[li], qn[j], out=out, workspace=ws)
         return n_tok[li]
 
     if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib * 2**20 // 4
-        src_probe = torch.ones(n, dtype=torch.float32, device="cuda")
+        nn = args.copy_probe_mib * 2**20 // 4
+        src_probe = torch.ones(nn, dtype=torch.float32, device="cuda")
         dst_probe = torch.empty_like(src_probe)
         torch.cuda.synchronize()
         dst_probe.copy_(src_probe)
@@ -209,9 +322,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
     K_ = args.steps
-    # Timed region: K whole steps back to back (append + attention), inputs
-    # resident in HBM, bracketed by synchronizations.
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region: K whole steps back to back (append + attention, or
+    # attention alone for a workload that does not stream), inputs resident
+    # in HBM, bracketed by synchronizations.
+    start, end = _events()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
@@ -223,27 +337,56 @@ def main():
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K_
     value = w.batch * K_ / (total_ms / 1e3)
-    # Per-call duration of kvq_decode_attention: K more calls back to back
-    # (each layer cache at its current length, no appends in between), with
-    # HIP events on the launch stream around the loop only; an event between
-    # two launches costs time of its own.
-    attn_T = [n_tok[(args.warmup + K_ + i) % n_layers] for i in range(K_)]
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Per-call duration of kvq_decode_attention: at least 200 more calls back
+    # to back (each layer cache at its current length, no appends between),
+    # with HIP events on the launch stream around the loop only: an event
+    # between two launches costs time of its own.  The spread: the same in
+    # groups of 20 calls.
+    n_calls = max(K_, 200)
+
+    def attn_loop(count, offset):
+        for i in range(count):
+            li = (offset + i) % n_layers
+            kvq.kvq_decode_attention(cfg, layers[li], n_tok[li], qn[(offset + i) % n_gen], out=out,
+                                     workspace=ws)
+
+    attn_T = [n_tok[i % n_layers] for i in range(n_calls)]
+    a0, a1 = _events()
     torch.cuda.synchronize()
     a0.record()
-    for i in range(K_):
-        li = (args.warmup + K_ + i) % n_layers
-        kvq.kvq_decode_attention(cfg, layers[li], n_tok[li], qn[i % n_gen], out=out, workspace=ws)
+    attn_loop(n_calls, 0)
     a1.record()
     torch.cuda.synchronize()
-    attn_total_ms = a0.elapsed_time(a1)
-    bytes_per_call = [algorithmic_bytes(w, T) for T in attn_T]
-    mean_attn_ms = attn_total_ms / K_
-    achieved = (sum(bytes_per_call) / K_) / (mean_attn_ms / 1e3) / 1e9
+    mean_attn_ms = a0.elapsed_time(a1) / n_calls
+    groups = []
+    for gi in range(10):
+        g0, g1 = _events()
+        g0.record()
+        attn_loop(20, 20 * gi)
+        g1.record()
+        torch.cuda.synchronize()
+        groups.append(g0.elapsed_time(g1) / 20 * 1e3)
+    bytes_per_call = sum(algorithmic_bytes(w, T) for T in attn_T) / n_calls
+    achieved = bytes_per_call / (mean_attn_ms / 1e3) / 1e9
+    splits = decode_splits(w, n_tok[0], cus)
+    pbytes = prefill_bytes(w, T0)
     detail = {
-        "attn_us_mean": mean_attn_ms * 1e3,
-        "step_us_minus_attn_us": ms_per_step * 1e3 - mean_attn_ms * 1e3,
-        "algorithmic_bytes_per_call": sum(bytes_per_call) // K_,
+        "attn_us_mean": round(mean_attn_ms * 1e3, 3),
+        "attn_us_groups_of_20": {"median": round(float(np.median(groups)), 3),
+                                 "p10": round(float(np.percentile(groups, 10)), 3),
+                                 "p90": round(float(np.percentile(groups, 90)), 3)},
+        "attn_calls_timed": n_calls,
+        "step_us_minus_attn_us": round(ms_per_step * 1e3 - mean_attn_ms * 1e3, 3),
+        "append_plain_us": None if append_plain_us is None else round(append_plain_us, 3),
+        "append_freeze_us": round(append_freeze_us, 3),
+        "prefill_us": round(prefill_ms * 1e3, 1),
+        "prefill_bytes": pbytes,
+        "prefill_GBps": round(pbytes / (prefill_ms / 1e3) / 1e9, 1),
+        "algorithmic_bytes_per_call": int(bytes_per_call),
+        "cached_tokens_at_timing": sorted(set(n_tok)),
+        "split_partial_bytes_per_call": (None if splits is None else
+                                         2 * w.batch * w.n_q_heads * splits * (w.head_dim + 2) * 4),
+        "splits_per_row": splits,
         "layer_caches": n_layers,
         "cache_mib_per_layer": round(layers[0].nbytes() / 2**20, 1),
         "host_wall_s": round(wall, 3),
@@ -264,17 +407,18 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: layer B{w.batch} Hq{w.n_q_heads} Hkv{w.n_kv_heads} "
-                        f"D{w.head_dim} T{w.n_tokens}+decode {w.dtype} inputs int{w.bits} "
-                        f"G{w.group} R{w.residual} S{w.sink}",
+                        f"D{w.head_dim} T{w.n_tokens}{'+decode' if streaming else ''} {w.dtype} "
+                        f"inputs int{w.bits} G{w.group} R{w.residual} S{w.sink}",
             "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "cached_tokens": w.n_tokens, "bits": w.bits,
             "group": w.group, "residual": w.residual, "sink": w.sink, "input_dtype": w.dtype,
-            "step": "append + decode attention, one layer",
+            "step": ("append + decode attention, one layer" if streaming
+                     else "decode attention, one layer"),
         },
         "roofline": {
             "bound": "hbm",
             "kernel": (f"kvq_decode_attention: {attn_kernel_name(w)} (split-K attention) + k_merge; "
-                       "mean over back-to-back calls, HIP events on the launch stream"),
+                       f"mean over {n_calls} back-to-back calls, HIP events on the launch stream"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

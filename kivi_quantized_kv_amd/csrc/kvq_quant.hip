@@ -3,130 +3,344 @@
 // freeze.  Method: pigeon guide "KV-cache quantization", How it works steps
 // 1-4; tract PR "quantized KV-cache storage op (int8/int4)" (frozen
 // fixed-size key blocks, values per token, sinks kept exact).
+//
+// Both halves work from registers: every thread loads 16-byte pieces of its
+// rows up front, the min / max reductions run across lanes (DPP and the
+// permlane swaps) with one small LDS step across waves, and codes go
+// straight from registers to the packed rows.  The affine code of an
+// element is rint(fl(fl(x - zp) / delta)) with a correctly rounded division;
+// it is computed as rint(y), y = fl(fl(x - zp) * r) with r the hardware
+// reciprocal of delta (within 2 ulp), which equals it unless y lies within
+// |y| 2^-21 of a half integer (r, the product and the division's own
+// rounding move the quotient by less than |y| 1.5 2^-22).  Since 0 <= y <=
+// (2^b - 1)(1 + 2^-21), one band (2^b) 2^-21 wide around the half integers
+// covers every element; waves holding an element in it, or a delta below
+// 2^-125 (kept off the reciprocal), take the exact division instead.  The prefill and the freeze run the same group and step
+// routines; only the row source differs (input tensor or residual ring).
 #include "kvq_kernels.h"
 
 namespace kvq {
 
 // ----------------------------------------------------------------------------
-// Key group: per-channel min/max over the G rows of an fp32 LDS tile, then
-// delta / zero point and the packed rows.  256 threads.
+// Row sources: the byte address of row r of the group / step being quantized.
 // ----------------------------------------------------------------------------
-template <int D, int BITS>
-__device__ void key_group_from_tile(const float* tile, int G, float* s_red, float* s_delta,
-                                    float* s_zp, float* k_scale, float* k_zero,
-                                    uint8_t* code_rows) {
+struct InputRows {            // rows of the caller's [.., T, D] tensor
+  const uint8_t* base;        // row 0
+  int64_t stride;             // bytes between rows
+  __device__ const uint8_t* row(int r) const { return base + r * stride; }
+};
+struct RingRows {             // tokens first .. first + n of the residual ring
+  const uint8_t* ring;        // slot 0 of this (batch, head)
+  const uint8_t* fresh;       // the token being appended (read from its input)
+  int64_t slot0, ring_len;    // ring slot of row 0; slots in the ring
+  int fresh_row;              // row index of the appended token, or -1
+  int row_bytes;
+  __device__ const uint8_t* row(int r) const {
+    if (r == fresh_row) return fresh;
+    int64_t s = slot0 + r;
+    if (s >= ring_len) s -= ring_len;
+    return ring + s * row_bytes;
+  }
+};
+
+// 16 bytes of a row widened exactly to fp32 (4 or 8 elements).
+template <int DT>
+__device__ __forceinline__ void widen16(uint4 v, float* out) {
+  if constexpr (DT == DT_F32) {
+    out[0] = __builtin_bit_cast(float, v.x); out[1] = __builtin_bit_cast(float, v.y);
+    out[2] = __builtin_bit_cast(float, v.z); out[3] = __builtin_bit_cast(float, v.w);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[2 * k] = DT == DT_F16 ? f16_bits_to_f32(w[k] & 0xFFFFu) : bf16_bits_to_f32(w[k] & 0xFFFFu);
+      out[2 * k + 1] = DT == DT_F16 ? f16_bits_to_f32(w[k] >> 16) : bf16_bits_to_f32(w[k] >> 16);
+    }
+  }
+}
+
+// Reciprocal used by affine_codes: 1 / delta within 2 ulp (v_rcp_f32), 0
+// for delta == 0 (every code 0).  `exact` is set for a delta in (0, 2^-125).
+__device__ __forceinline__ float code_rcp(float delta, bool& exact) {
+  exact |= delta != 0.0f && !(delta >= 0x1p-125f);
+  return delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
+}
+
+// Codes of n elements x[i] against per-element (delta, zero, 1/delta):
+// guarded reciprocal first, the exact division for the whole wave when any
+// lane holds an element near a rounding boundary or flagged `exact`.
+template <int N, int BITS>
+__device__ __forceinline__ void affine_codes(const float* x, const float* delta, const float* zp,
+                                             const float* rcp, bool exact, uint32_t* code) {
+  constexpr float levels = float((1 << BITS) - 1);
+  constexpr float kBand = 0.5f - float(1 << BITS) * 0x1p-21f;
+  bool risky = exact;
+  float c[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float a = x[i] - zp[i];
+    const float y = a * rcp[i];
+    const float r = __builtin_rintf(y);   // 0 <= y < levels + 1/2: no clamp needed
+    risky |= __builtin_fabsf(y - r) >= kBand;
+    c[i] = r;
+  }
+  if (__builtin_amdgcn_ballot_w64(risky) != 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) code[i] = affine_code(x[i], delta[i], zp[i], levels);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) code[i] = uint32_t(c[i]);
+  }
+}
+
+// All-reduce of min and max over the lanes l, l ^ S, l ^ 2S, ... (S = step,
+// a power of two; lanes sharing l mod S).
+template <int S>
+__device__ __forceinline__ void minmax_across(float& mn, float& mx) {
+  if constexpr (S <= 8) {
+    mn = __builtin_fminf(mn, dpp_mov<kRowRor8>(mn));
+    mx = __builtin_fmaxf(mx, dpp_mov<kRowRor8>(mx));
+  }
+  if constexpr (S <= 16) {
+    float a, b;
+    partner_pair<false>(mn, a, b); mn = __builtin_fminf(a, b);
+    partner_pair<false>(mx, a, b); mx = __builtin_fmaxf(a, b);
+  }
+  float a, b;
+  partner_pair<true>(mn, a, b); mn = __builtin_fminf(a, b);
+  partner_pair<true>(mx, a, b); mx = __builtin_fmaxf(a, b);
+}
+
+// All-reduce of min and max over aligned runs of N consecutive lanes (N =
+// 8, 16 or 32).
+template <int N>
+__device__ __forceinline__ void minmax_run(float& mn, float& mx) {
+  mn = __builtin_fminf(mn, dpp_mov<kQuadXor1>(mn));
+  mx = __builtin_fmaxf(mx, dpp_mov<kQuadXor1>(mx));
+  mn = __builtin_fminf(mn, dpp_mov<kQuadXor2>(mn));
+  mx = __builtin_fmaxf(mx, dpp_mov<kQuadXor2>(mx));
+  constexpr int kHalfMirror = 0x141, kMirror = 0x140;
+  mn = __builtin_fminf(mn, dpp_mov<kHalfMirror>(mn));   // quads of a half row meet
+  mx = __builtin_fmaxf(mx, dpp_mov<kHalfMirror>(mx));
+  if constexpr (N >= 16) {
+    mn = __builtin_fminf(mn, dpp_mov<kMirror>(mn));     // halves of a row meet
+    mx = __builtin_fmaxf(mx, dpp_mov<kMirror>(mx));
+  }
+  if constexpr (N >= 32) {
+    float a, b;
+    partner_pair<false>(mn, a, b); mn = __builtin_fminf(a, b);
+    partner_pair<false>(mx, a, b); mx = __builtin_fmaxf(a, b);
+  }
+}
+
+// Store n bits of codes (8, 16, 32 or 64) at an address aligned to n/8.
+template <int NBITS>
+__device__ __forceinline__ void store_bits(uint8_t* p, uint64_t v) {
+  if constexpr (NBITS == 8) *p = uint8_t(v);
+  else if constexpr (NBITS == 16) *reinterpret_cast<uint16_t*>(p) = uint16_t(v);
+  else if constexpr (NBITS == 32) *reinterpret_cast<uint32_t*>(p) = uint32_t(v);
+  else *reinterpret_cast<uint2*>(p) = make_uint2(uint32_t(v), uint32_t(v >> 32));
+}
+
+template <int DT, int D>
+struct RowSplit {
+  static constexpr int kVE = 16 / Elem<DT>::bytes;   // elements per 16-byte piece
+  static constexpr int kTPR = D / kVE;                // threads per row: 8, 16 or 32
+  static constexpr int kRPP = 256 / kTPR;             // rows per pass of 256 threads
+};
+
+// ----------------------------------------------------------------------------
+// One key group of G rows, 256 threads: per-channel min / max over the rows,
+// delta and zero point, the packed code rows.  Thread t holds piece t % kTPR
+// (channels kVE * (t % kTPR) ..) of rows t / kTPR + kRPP * i.
+// ----------------------------------------------------------------------------
+template <int DT, int D, int G>
+struct KeyRows {
+  static constexpr int kRPT = G / RowSplit<DT, D>::kRPP;   // rows per thread
+  static_assert(kRPT >= 1 && G % RowSplit<DT, D>::kRPP == 0, "group rows per thread");
+  uint4 raw[kRPT];
+};
+
+// This thread's pieces of a key group's rows.
+template <int DT, int D, int G, class Rows>
+__device__ __forceinline__ void load_key_rows(const Rows& rows, KeyRows<DT, D, G>& kr) {
+  using RS = RowSplit<DT, D>;
+  const int t = threadIdx.x, cs = t % RS::kTPR, r0 = t / RS::kTPR;
+#pragma unroll
+  for (int i = 0; i < KeyRows<DT, D, G>::kRPT; ++i)
+    kr.raw[i] = *reinterpret_cast<const uint4*>(rows.row(r0 + i * RS::kRPP) + cs * 16);
+}
+
+template <int DT, int D, int BITS, int G>
+__device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_scale, float* k_zero,
+                                          uint8_t* code_rows, float (*s_red)[D], float (*s_par)[D]) {
+  using RS = RowSplit<DT, D>;
+  constexpr int kVE = RS::kVE, kTPR = RS::kTPR, kRPP = RS::kRPP;
+  constexpr int kRPT = KeyRows<DT, D, G>::kRPT;
   constexpr float kLevels = float((1 << BITS) - 1);
-  constexpr int kSeg = 256 / D;  // threads per channel
-  const int t = threadIdx.x;
-  const int c = t % D, seg = t / D;
-  float mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int r = seg; r < G; r += kSeg) {
-    float x = tile[r * D + c];
-    mn = __builtin_fminf(mn, x);
-    mx = __builtin_fmaxf(mx, x);
+  const int t = threadIdx.x, cs = t % kTPR, r0 = t / kTPR;
+  const int lane = t & 63, wave = t >> 6;
+  const uint4* raw = kr.raw;
+  float x[kRPT][kVE];
+#pragma unroll
+  for (int i = 0; i < kRPT; ++i) widen16<DT>(raw[i], x[i]);
+  float mn[kVE], mx[kVE];
+#pragma unroll
+  for (int e = 0; e < kVE; ++e) {
+    mn[e] = x[0][e];
+    mx[e] = x[0][e];
+#pragma unroll
+    for (int i = 1; i < kRPT; ++i) {
+      mn[e] = __builtin_fminf(mn[e], x[i][e]);
+      mx[e] = __builtin_fmaxf(mx[e], x[i][e]);
+    }
+    minmax_across<kTPR>(mn[e], mx[e]);
   }
-  s_red[seg * D + c] = mn;
-  s_red[(kSeg + seg) * D + c] = mx;
+  // the waves meet in LDS: rows 0..3 of s_red hold minima, 4..7 maxima
+  if (lane < kTPR) {
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) {
+      s_red[wave][cs * kVE + e] = mn[e];
+      s_red[4 + wave][cs * kVE + e] = mx[e];
+    }
+  }
   __syncthreads();
+  // one thread per channel: delta, zero point and reciprocal, written out
+  // and shared through LDS (row 3 of s_par flags a delta that needs the
+  // exact division)
   if (t < D) {
-#pragma unroll
-    for (int k = 1; k < kSeg; ++k) {
-      mn = __builtin_fminf(mn, s_red[k * D + t]);
-      mx = __builtin_fmaxf(mx, s_red[(kSeg + k) * D + t]);
-    }
-    float delta, zp;
-    affine_params(mn, mx, kLevels, delta, zp);
-    s_delta[t] = delta;
-    s_zp[t] = zp;
-    k_scale[t] = delta;
-    k_zero[t] = zp;
+    const float lo = __builtin_fminf(__builtin_fminf(s_red[0][t], s_red[1][t]), __builtin_fminf(s_red[2][t], s_red[3][t]));
+    const float hi = __builtin_fmaxf(__builtin_fmaxf(s_red[4][t], s_red[5][t]), __builtin_fmaxf(s_red[6][t], s_red[7][t]));
+    float dl, z;
+    bool ex = false;
+    affine_params(lo, hi, kLevels, dl, z);
+    const float rc = code_rcp(dl, ex);
+    s_par[0][t] = dl;
+    s_par[1][t] = z;
+    s_par[2][t] = rc;
+    s_par[3][t] = ex ? 1.0f : 0.0f;
+    k_scale[t] = dl;
+    k_zero[t] = z;
   }
   __syncthreads();
-  constexpr int kPerWord = 32 / BITS;
-  constexpr int kWordsPerRow = D * BITS / 32;
-  uint32_t* rows = reinterpret_cast<uint32_t*>(code_rows);
-  for (int w = t; w < G * kWordsPerRow; w += 256) {
-    const int r = w / kWordsPerRow, wi = w % kWordsPerRow;
-    uint32_t word = 0;
+  float delta[kVE], zp[kVE], rcp[kVE];
+  bool exact = false;
 #pragma unroll
-    for (int i = 0; i < kPerWord; ++i) {
-      const int ch = wi * kPerWord + i;
-      word |= affine_code(tile[r * D + ch], s_delta[ch], s_zp[ch], kLevels) << (BITS * i);
-    }
-    rows[w] = word;
+  for (int e = 0; e < kVE; e += 4) {
+    const int c = cs * kVE + e;
+    const float4 d4 = *reinterpret_cast<const float4*>(&s_par[0][c]);
+    const float4 z4 = *reinterpret_cast<const float4*>(&s_par[1][c]);
+    const float4 r4 = *reinterpret_cast<const float4*>(&s_par[2][c]);
+    const float4 x4 = *reinterpret_cast<const float4*>(&s_par[3][c]);
+    delta[e] = d4.x; delta[e + 1] = d4.y; delta[e + 2] = d4.z; delta[e + 3] = d4.w;
+    zp[e] = z4.x; zp[e + 1] = z4.y; zp[e + 2] = z4.z; zp[e + 3] = z4.w;
+    rcp[e] = r4.x; rcp[e + 1] = r4.y; rcp[e + 2] = r4.z; rcp[e + 3] = r4.w;
+    exact |= (x4.x + x4.y + x4.z + x4.w) != 0.0f;
+  }
+  constexpr int kRB = D * BITS / 8;
+#pragma unroll
+  for (int i = 0; i < kRPT; ++i) {
+    uint32_t code[kVE];
+    affine_codes<kVE, BITS>(x[i], delta, zp, rcp, exact, code);
+    uint64_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) packed |= uint64_t(code[e]) << (BITS * e);
+    store_bits<kVE * BITS>(code_rows + (r0 + i * kRPP) * kRB + cs * (kVE * BITS / 8), packed);
   }
 }
 
 // ----------------------------------------------------------------------------
-// Value tokens [u0, u0 + n) (u0 and n multiples of 32) from an fp32 LDS
-// tile: per-token min/max by wave reductions, delta / zero point, and the
-// bytes of the value-code units that hold these tokens.  256 threads.
+// One 32-token step of values (quantized tokens u0 .. u0 + 31, u0 a multiple
+// of 32), 256 threads: per-token min / max across the lanes of the token,
+// delta and zero point, codes through LDS (channel-major) into the value-code
+// units of the layout in kvq.h.  At 2 bits a block holds two steps; a step
+// writes its own bytes of each unit (bytes s and s + 2).
 // ----------------------------------------------------------------------------
-template <int D, int BITS>
-__device__ void value_tokens_from_tile(const float* tile, int64_t u0, int n, float* s_delta,
-                                       float* s_zp, float* v_scale, float* v_zero,
-                                       uint8_t* v_codes_head) {
-  constexpr float kLevels = float((1 << BITS) - 1);
-  using VL = VLayout<BITS>;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  for (int i = wave; i < n; i += 4) {
-    float mn = __builtin_inff(), mx = -__builtin_inff();
+constexpr int kStepPitch = 36;   // bytes per channel row of the LDS code tile
+
+template <int DT, int D>
+struct StepRows {
+  static constexpr int kTPT = 32 / RowSplit<DT, D>::kRPP;   // tokens per thread
+  static_assert(kTPT >= 1 && 32 % RowSplit<DT, D>::kRPP == 0, "tokens per pass");
+  uint4 raw[kTPT];
+};
+
+// This thread's pieces of the 32 value rows of a step.
+template <int DT, int D, class Rows>
+__device__ __forceinline__ void load_step_rows(const Rows& rows, StepRows<DT, D>& sr) {
+  using RS = RowSplit<DT, D>;
+  const int t = threadIdx.x, cs = t % RS::kTPR, r0 = t / RS::kTPR;
 #pragma unroll
-    for (int c = lane; c < D; c += 64) {
-      float x = tile[i * D + c];
-      mn = __builtin_fminf(mn, x);
-      mx = __builtin_fmaxf(mx, x);
+  for (int j = 0; j < StepRows<DT, D>::kTPT; ++j)
+    sr.raw[j] = *reinterpret_cast<const uint4*>(rows.row(r0 + j * RS::kRPP) + cs * 16);
+}
+
+template <int DT, int D, int BITS>
+__device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0, float* v_scale,
+                                           float* v_zero, uint8_t* v_codes_head, uint8_t* s_codes) {
+  using RS = RowSplit<DT, D>;
+  using VL = VLayout<BITS>;
+  constexpr int kVE = RS::kVE, kTPR = RS::kTPR, kRPP = RS::kRPP;
+  constexpr int kTPT = StepRows<DT, D>::kTPT;
+  constexpr float kLevels = float((1 << BITS) - 1);
+  const int t = threadIdx.x, cs = t % kTPR, r0 = t / kTPR;
+  const uint4* raw = sr.raw;
+#pragma unroll
+  for (int j = 0; j < kTPT; ++j) {
+    const int tok = r0 + j * kRPP;
+    float x[kVE];
+    widen16<DT>(raw[j], x);
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < kVE; ++e) {
+      mn = __builtin_fminf(mn, x[e]);
+      mx = __builtin_fmaxf(mx, x[e]);
     }
-    mn = wave_min(mn);
-    mx = wave_max(mx);
-    if (lane == 0) {
-      float delta, zp;
-      affine_params(mn, mx, kLevels, delta, zp);
-      s_delta[i] = delta;
-      s_zp[i] = zp;
-      v_scale[u0 + i] = delta;
-      v_zero[u0 + i] = zp;
+    minmax_run<kTPR>(mn, mx);
+    float delta[kVE], zp[kVE], rcp[kVE];
+    bool exact = false;
+    affine_params(mn, mx, kLevels, delta[0], zp[0]);
+    rcp[0] = code_rcp(delta[0], exact);
+#pragma unroll
+    for (int e = 1; e < kVE; ++e) {
+      delta[e] = delta[0];
+      zp[e] = zp[0];
+      rcp[e] = rcp[0];
     }
+    if (cs == 0) {
+      v_scale[u0 + tok] = delta[0];
+      v_zero[u0 + tok] = zp[0];
+    }
+    uint32_t code[kVE];
+    affine_codes<kVE, BITS>(x, delta, zp, rcp, exact, code);
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) s_codes[(cs * kVE + e) * kStepPitch + tok] = uint8_t(code[e]);
   }
   __syncthreads();
-  const int64_t blk0 = u0 / VL::L;
-  const int64_t blk1 = (u0 + n + VL::L - 1) / VL::L;
-  const int units = int(blk1 - blk0) * 4 * D;
-  for (int x = t; x < units; x += 256) {
-    const int64_t blk = blk0 + x / (4 * D);
-    const int uin = x % (4 * D);
-    const int g = uin / (16 * (D / 16));
-    const int rem = uin % (16 * (D / 16));
-    const int j = rem / (D / 16), nn = rem % (D / 16);
-    const int d = nn * 16 + j;
-    uint64_t bits = 0;
-    uint32_t step_in = 0;  // bit s set when 32-token step s of the block is in range
-#pragma unroll
-    for (int i = 0; i < VL::U; ++i) {
-      const int o = vslot_token<BITS>(g, i);
-      const int64_t u = blk * VL::L + o;
-      if (u >= u0 && u < u0 + n) {
-        const int li = int(u - u0);
-        bits |= uint64_t(affine_code(tile[li * D + d], s_delta[li], s_zp[li], kLevels))
-                << (BITS * i);
-        step_in |= 1u << (o / 32);
-      }
-    }
-    uint8_t* dst = v_codes_head + (blk * 4 * D + uin) * VL::UB;
-    const uint32_t all_steps = (1u << (VL::L / 32)) - 1;
-    if (step_in == all_steps) {
-      if constexpr (VL::UB == 8) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(uint32_t(bits), uint32_t(bits >> 32));
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = uint32_t(bits);
-      }
+  // units of this step: unit x of the block holds channel d = 16 n + jj for
+  // lane group g; its tokens (h, r) of this step are offsets 16 h + 4 g + r
+  constexpr int kUnits = 4 * D;
+  const int64_t blk = u0 / VL::L;
+  const int s = int((u0 % VL::L) / 32);
+  for (int x = t; x < kUnits; x += 256) {
+    const int g = x / D, rem = x % D, jj = rem / (D / 16), n = rem % (D / 16);
+    const int d = 16 * n + jj;
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_codes + d * kStepPitch + 4 * g);
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_codes + d * kStepPitch + 16 + 4 * g);
+    uint8_t* dst = v_codes_head + (blk * kUnits + x) * VL::UB;
+    if constexpr (BITS == 8) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);         // slots r (h 0), 4 + r (h 1)
+    } else if constexpr (BITS == 4) {
+      const uint32_t a = w0 | (w0 >> 4), b = w1 | (w1 >> 4);        // nibble pairs in bytes 0, 2
+      *reinterpret_cast<uint32_t*>(dst) = (a & 0xFFu) | ((a >> 8) & 0xFF00u) | ((b & 0xFFu) << 16) |
+                                          ((b << 8) & 0xFF000000u);
     } else {
-      // partial block (2-bit codes): byte k holds slots 4k..4k+3, step k % 2
-#pragma unroll
-      for (int k = 0; k < VL::UB; ++k) {
-        const int s = (4 * k >> 2) % (VL::U / 8);
-        if (step_in & (1u << s)) dst[k] = uint8_t(bits >> (8 * k));
-      }
+      // 2 bits: slot r + 4 s + 8 h sits in byte s + 2 h
+      uint32_t a = w0 | (w0 >> 6), b = w1 | (w1 >> 6);
+      a = (a | (a >> 12)) & 0xFFu;
+      b = (b | (b >> 12)) & 0xFFu;
+      dst[s] = uint8_t(a);
+      dst[s + 2] = uint8_t(b);
     }
   }
 }
@@ -155,74 +369,62 @@ __global__ __launch_bounds__(64) void k_copy_fp_rows(FpCopyArgs a) {
     reinterpret_cast<uint4*>(dst)[v] = reinterpret_cast<const uint4*>(src)[v];
 }
 
-template <int DT, int D>
-__device__ void load_rows_to_tile(const void* base, int64_t row0_elem, int64_t stride_t, int rows,
-                                  int rows_valid, float* tile) {
-  constexpr int kV = D / 4;
-  for (int x = threadIdx.x; x < rows * kV; x += blockDim.x) {
-    const int r = x / kV, c4 = x % kV;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows_valid) load4<DT>(base, row0_elem + r * stride_t + c4 * 4, v);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) tile[r * D + c4 * 4 + k] = v[k];
-  }
-}
-
-template <int DT, int D, int BITS>
+// grid: x = unit (key group, or 32-token value step) of the quantized range,
+// y = head, z = batch.  One unit per workgroup: many small resident
+// workgroups at different phases overlap loads with arithmetic better than
+// fewer workgroups streaming several units each (measured).
+template <int DT, int D, int BITS, int G>
 __global__ __launch_bounds__(256) void k_quant_keys(QuantArgs a) {
-  // grid: x = key group k, y = head, z = batch
-  extern __shared__ float smem[];
-  const int G = a.G;
-  float* tile = smem;                       // G * D
-  float* s_red = tile + G * D;              // 2 * (256/D) * D
-  float* s_delta = s_red + 2 * 256;         // D
-  float* s_zp = s_delta + D;                // D
+  __shared__ __attribute__((aligned(16))) float s_red[8][D];
+  __shared__ __attribute__((aligned(16))) float s_par[4][D];
   const int64_t k = blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t row0 = b * a.sb + h * a.sh + (a.S + k * G) * a.st;
-  load_rows_to_tile<DT, D>(a.src, row0, a.st, G, G, tile);
-  __syncthreads();
+  constexpr int EB = Elem<DT>::bytes;
   const int64_t bh = int64_t(b) * a.H + h;
-  float* ks = a.scale + (bh * (a.qcap / G) + k) * D;
-  float* kz = a.zero + (bh * (a.qcap / G) + k) * D;
-  uint8_t* rows = a.codes + (bh * a.qcap + k * G) * (D * BITS / 8);
-  key_group_from_tile<D, BITS>(tile, G, s_red, s_delta, s_zp, ks, kz, rows);
+  KeyRows<DT, D, G> kr;
+  load_key_rows<DT, D, G>(
+      InputRows{reinterpret_cast<const uint8_t*>(a.src) + (b * a.sb + h * a.sh + (a.S + k * G) * a.st) * EB,
+                a.st * EB},
+      kr);
+  key_group<DT, D, BITS, G>(kr, a.scale + (bh * (a.qcap / G) + k) * D, a.zero + (bh * (a.qcap / G) + k) * D,
+                            a.codes + (bh * a.qcap + k * G) * (D * BITS / 8), s_red, s_par);
 }
 
 template <int DT, int D, int BITS>
 __global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
-  // grid: x = 32-token step of the quantized range, y = head, z = batch
-  __shared__ float tile[32 * D];
-  __shared__ float s_delta[32], s_zp[32];
-  const int64_t u0 = int64_t(blockIdx.x) * 32;
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[D * kStepPitch];
+  const int64_t st = blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t row0 = b * a.sb + h * a.sh + (a.S + u0) * a.st;
-  load_rows_to_tile<DT, D>(a.src, row0, a.st, 32, 32, tile);
-  __syncthreads();
+  constexpr int EB = Elem<DT>::bytes;
   const int64_t bh = int64_t(b) * a.H + h;
-  value_tokens_from_tile<D, BITS>(tile, u0, 32, s_delta, s_zp, a.scale + bh * a.qcap,
-                                  a.zero + bh * a.qcap,
-                                  a.codes + bh * (a.qcap * D * BITS / 8));
+  StepRows<DT, D> sr;
+  load_step_rows<DT, D>(
+      InputRows{reinterpret_cast<const uint8_t*>(a.src) + (b * a.sb + h * a.sh + (a.S + 32 * st) * a.st) * EB,
+                a.st * EB},
+      sr);
+  value_step<DT, D, BITS>(sr, 32 * st, a.scale + bh * a.qcap, a.zero + bh * a.qcap,
+                          a.codes + bh * (a.qcap * D * BITS / 8), s_codes);
 }
 
 // ----------------------------------------------------------------------------
-// Streaming append: write token t = n_before to its sink or ring slot; when
-// the full-precision count reaches R + G, quantize and freeze the oldest G
-// ring tokens as the next key group and G value tokens.
+// Streaming append: block 0 writes token t = n_before to its sink or ring
+// slot.  When the full-precision count reaches R + G, block 1 quantizes the
+// oldest G ring tokens as the next key group and blocks 2 .. 1 + G/32 their
+// values, one 32-token step each.  The appended token itself is read from
+// its input (it belongs to the group when R == 0), so the blocks need no
+// ordering among themselves.
 // ----------------------------------------------------------------------------
-template <int DT, int D, int BITS>
+template <int DT, int D, int BITS, int G>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
-  // grid: y = head, z = batch
-  extern __shared__ float smem[];
-  const int h = blockIdx.y, b = blockIdx.z;
+  // grid: x = role, y = head, z = batch
+  const int role = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = int64_t(b) * a.H + h;
   constexpr int EB = Elem<DT>::bytes;
   const int64_t t = a.n_before;
-  const int64_t ring = a.R + a.G;
-  // 1) the new token, K and V
-  {
-    const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_new) + (b * a.k_sb + h * a.k_sh) * EB;
-    const uint8_t* vs = reinterpret_cast<const uint8_t*>(a.v_new) + (b * a.v_sb + h * a.v_sh) * EB;
+  const int64_t ring = a.R + G;
+  const uint8_t* kin = reinterpret_cast<const uint8_t*>(a.k_new) + (b * a.k_sb + h * a.k_sh) * EB;
+  const uint8_t* vin = reinterpret_cast<const uint8_t*>(a.v_new) + (b * a.v_sb + h * a.v_sh) * EB;
+  if (role == 0) {
     uint8_t *kd, *vd;
     if (t < a.S) {
       kd = reinterpret_cast<uint8_t*>(a.k_sink) + (bh * a.S + t) * D * EB;
@@ -235,65 +437,52 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     constexpr int kVec = D * EB / 16;
     for (int v = threadIdx.x; v < 2 * kVec; v += blockDim.x) {
       if (v < kVec)
-        reinterpret_cast<uint4*>(kd)[v] = reinterpret_cast<const uint4*>(ks)[v];
+        reinterpret_cast<uint4*>(kd)[v] = reinterpret_cast<const uint4*>(kin)[v];
       else
-        reinterpret_cast<uint4*>(vd)[v - kVec] = reinterpret_cast<const uint4*>(vs)[v - kVec];
+        reinterpret_cast<uint4*>(vd)[v - kVec] = reinterpret_cast<const uint4*>(vin)[v - kVec];
     }
+    return;
   }
-  if (!a.flush) return;
-  // 2) flush: tokens S + q_old .. S + q_old + G - 1, read from their ring
-  // slots except the new token itself, which is read from the input (it may
-  // be part of the group when R == 0).
-  const int G = a.G;
-  float* ktile = smem;                  // G * D
-  float* vtile = ktile + G * D;         // G * D
-  float* s_red = vtile + G * D;         // 512
-  float* s_delta = s_red + 512;         // max(D, G)
-  float* s_zp = s_delta + 128;          // max(D, G)
-  constexpr int kV = D / 4;
-  for (int x = threadIdx.x; x < G * kV; x += blockDim.x) {
-    const int r = x / kV, c4 = x % kV;
-    const int64_t tok = a.S + a.q_old + r;
-    float kv4[4], vv4[4];
-    if (tok == t) {
-      load4<DT>(a.k_new, b * a.k_sb + h * a.k_sh + c4 * 4, kv4);
-      load4<DT>(a.v_new, b * a.v_sb + h * a.v_sh + c4 * 4, vv4);
-    } else {
-      const int64_t slot = (tok - a.S) % ring;
-      load4<DT>(a.k_resid, (bh * ring + slot) * D + c4 * 4, kv4);
-      load4<DT>(a.v_resid, (bh * ring + slot) * D + c4 * 4, vv4);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ktile[r * D + c4 * 4 + k] = kv4[k];
-      vtile[r * D + c4 * 4 + k] = vv4[k];
-    }
+  // freeze of tokens S + q_old .. S + q_old + G - 1
+  const int64_t first = a.S + a.q_old;
+  const int fresh_row = int(t - first);          // in [0, G) when t is in the group
+  if (role == 1) {
+    __shared__ __attribute__((aligned(16))) float s_red[8][D];
+    __shared__ __attribute__((aligned(16))) float s_par[4][D];
+    const RingRows rows{reinterpret_cast<const uint8_t*>(a.k_resid) + bh * ring * D * EB, kin,
+                        (first - a.S) % ring, ring, fresh_row, D * EB};
+    const int64_t kgrp = a.q_old / G;
+    KeyRows<DT, D, G> kr;
+    load_key_rows<DT, D, G>(rows, kr);
+    key_group<DT, D, BITS, G>(kr, a.k_scale + (bh * (a.qcap / G) + kgrp) * D,
+                              a.k_zero + (bh * (a.qcap / G) + kgrp) * D,
+                              a.k_codes + (bh * a.qcap + a.q_old) * (D * BITS / 8), s_red, s_par);
+  } else {
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[D * kStepPitch];
+    const int step = role - 2;
+    const RingRows rows{reinterpret_cast<const uint8_t*>(a.v_resid) + bh * ring * D * EB, vin,
+                        (first + 32 * step - a.S) % ring, ring, fresh_row - 32 * step, D * EB};
+    StepRows<DT, D> sr;
+    load_step_rows<DT, D>(rows, sr);
+    value_step<DT, D, BITS>(sr, a.q_old + 32 * step, a.v_scale + bh * a.qcap, a.v_zero + bh * a.qcap,
+                            a.v_codes + bh * (a.qcap * D * BITS / 8), s_codes);
   }
-  __syncthreads();
-  const int64_t kgrp = a.q_old / G;
-  float* ks = a.k_scale + (bh * (a.qcap / G) + kgrp) * D;
-  float* kz = a.k_zero + (bh * (a.qcap / G) + kgrp) * D;
-  uint8_t* rows = a.k_codes + (bh * a.qcap + a.q_old) * (D * BITS / 8);
-  key_group_from_tile<D, BITS>(ktile, G, s_red, s_delta, s_zp, ks, kz, rows);
-  __syncthreads();
-  value_tokens_from_tile<D, BITS>(vtile, a.q_old, G, s_delta, s_zp, a.v_scale + bh * a.qcap,
-                                  a.v_zero + bh * a.qcap,
-                                  a.v_codes + bh * (a.qcap * D * BITS / 8));
 }
 
 // ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
 template <int DT, int D, int BITS>
-hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_groups, int B, int H, hipStream_t s) {
-  size_t lds = (size_t(a.G) * D + 2 * 256 + 2 * D) * sizeof(float);
-  hipLaunchKernelGGL((k_quant_keys<DT, D, BITS>), dim3(unsigned(n_groups), H, B), dim3(256), lds,
-                     s, a);
+hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_units, int B, int H, hipStream_t s) {
+  const dim3 grid(unsigned(n_units), H, B);
+  if (a.G == 32) hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 32>), grid, dim3(256), 0, s, a);
+  else if (a.G == 64) hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 128>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <int DT, int D, int BITS>
-hipError_t launch_quant_values(const QuantArgs& a, int64_t n_steps, int B, int H, hipStream_t s) {
-  hipLaunchKernelGGL((k_quant_values<DT, D, BITS>), dim3(unsigned(n_steps), H, B), dim3(256), 0,
+hipError_t launch_quant_values(const QuantArgs& a, int64_t n_units, int B, int H, hipStream_t s) {
+  hipLaunchKernelGGL((k_quant_values<DT, D, BITS>), dim3(unsigned(n_units), H, B), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }
@@ -304,8 +493,10 @@ hipError_t launch_copy_fp(const FpCopyArgs& a, int64_t n_rows, int B, int H, hip
 }
 template <int DT, int D, int BITS>
 hipError_t launch_append(const AppendArgs& a, int B, int H, hipStream_t s) {
-  size_t lds = a.flush ? (size_t(2) * a.G * D + 512 + 256) * sizeof(float) : 0;
-  hipLaunchKernelGGL((k_append<DT, D, BITS>), dim3(1, H, B), dim3(256), lds, s, a);
+  const dim3 grid(a.flush ? 2 + a.G / 32 : 1, H, B);
+  if (a.G == 32) hipLaunchKernelGGL((k_append<DT, D, BITS, 32>), grid, dim3(256), 0, s, a);
+  else if (a.G == 64) hipLaunchKernelGGL((k_append<DT, D, BITS, 64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_append<DT, D, BITS, 128>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

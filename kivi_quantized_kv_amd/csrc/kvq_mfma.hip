@@ -552,10 +552,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     u32x4_t qB[kKS];
 
     // Field weights of one key group into qB (high or low parts): x_d
-    // (field-scaled q) times delta_d.
+    // (field-scaled q) times delta_d.  A high column and its low partner
+    // (kJoin apart in the row) split the K-steps: each computes both fp16
+    // parts of its own half (high lanes K-steps [0, kKS/2), low lanes the
+    // rest), keeps the part of its own kind and takes the other half's part
+    // of its kind from the partner by a DPP move masked to its banks.
+    constexpr int kHalfKS = kKS / 2;
+    constexpr int kHiBanks = (GQA == 8 || DUAL) ? 0x3 : 0x5;   // banks of high columns
+    constexpr int kLoBanks = 0xF ^ kHiBanks;
+    const int kk_own = is_lo ? kHalfKS : 0;
     auto group_weights = [&](const float* kpd) {
 #pragma unroll
-      for (int kk = 0; kk < kKS; ++kk) {
+      for (int j = 0; j < kHalfKS; ++j) {
+        const int kk = j + kk_own;
         const int wk = kk / kStepsPerWord, sp = kk % kStepsPerWord;
         // the 8 channels of this K-step: runs [cA, cA+4) (low halves of
         // the fields) and [cB, cB+4) (high halves) of word wk
@@ -571,7 +580,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         field_weights<BITS>(xa, fa, wa);
         field_weights<BITS>(xb, fb, wb);
 #pragma unroll
-        for (int r2 = 0; r2 < 4; ++r2) qB[kk][r2] = split_pack(wa[r2], wb[r2], neg_lo);
+        for (int r2 = 0; r2 < 4; ++r2) {
+          const uint32_t hi = pack_f16(wa[r2], wb[r2]);
+          const h2_t hv = __builtin_bit_cast(h2_t, hi);
+          const uint32_t lo = pack_f16(wa[r2] - (float)hv[0], wb[r2] - (float)hv[1]);
+          // K-step j: high lanes keep theirs, low lanes take the high
+          // partner's low part; K-step j + kHalfKS: the other way round
+          qB[j][r2] = uint32_t(__builtin_amdgcn_update_dpp(int(hi), int(lo), kJoin, 0xF, kLoBanks, false));
+          qB[j + kHalfKS][r2] = uint32_t(__builtin_amdgcn_update_dpp(int(lo), int(hi), kJoin, 0xF, kHiBanks, false));
+        }
       }
     };
     // S^T tiles [t_begin, t_end) of chunk r from the weights in qB.

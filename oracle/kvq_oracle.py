@@ -39,8 +39,22 @@ Readings where the pages are silent (each is listed in the design notes):
   R7 the zero point is the fp32 minimum, stored as mn + 0.0f (so -0 -> +0).
   R8 sink and residual tokens are stored losslessly in the input dtype.
   R9 GQA: q head hq reads KV head hq // (Hq / Hkv).
-  R10 default softmax scale 1/sqrt(D); the query attends to every cached token.
+  R10 default softmax scale 1/sqrt(D); the query attends to every cached token
+      (every token of the window when a window is set, W1).
   R11 codes are clamped to [0, 2^b - 1].
+
+Sliding window ([KIVI-PR] "The idea": the quantized store composes with the
+sliding-window cache; "Relationship to other PRs": a bounded window cache
+with int8 storage), readings:
+  W1 with a window of W tokens the decode query attends to the sinks and to
+     the last W tokens [max(S, T - W), T); with S = 0 this is plain sliding-
+     window attention.  W >= R + G, so the full-precision tokens always lie
+     inside the window.
+  W2 the store is bounded: quantized token u (token S + u) is kept at
+     storage row u mod qcap, with qcap = W + G rounded up to a multiple of
+     max(64, G); a group that freezes overwrites the rows of the oldest
+     one (eviction).  Tokens before the window inside a live chunk are
+     masked, so the window is exact to the token.
 
 Every function here is pinned by tests/test_oracle_pins.py against worked
 examples, closed forms, brute force and library routines.
@@ -285,14 +299,19 @@ def value_valid_byte_mask(n_valid: int, n_cap: int, bits: int, D: int) -> np.nda
 # ----------------------------------------------------------------------------
 class CacheGeometry:
     """Sizes of every cache buffer for a configuration.  The quantized-token
-    capacity is cap - S rounded up to a multiple of max(64, G)."""
+    capacity is cap - S (at most W + G with a window, W2) rounded up to a
+    multiple of max(64, G)."""
 
-    def __init__(self, B, Hkv, D, bits, G, S, R, capacity, dtype):
+    def __init__(self, B, Hkv, D, bits, G, S, R, capacity, dtype, window=0):
         assert bits in SUPPORTED_BITS
+        assert window == 0 or window >= R + G
         self.B, self.Hkv, self.D, self.bits = B, Hkv, D, bits
         self.G, self.S, self.R, self.capacity, self.dtype = G, S, R, capacity, dtype
+        self.window = window
         step = max(64, G)
         qcap = max(0, capacity - S)
+        if window:
+            qcap = min(qcap, window + G)
         self.qcap = -(-qcap // step) * step
         self.ring = R + G
         self.k_row_bytes = D * bits // 8
@@ -317,34 +336,53 @@ class CacheGeometry:
 
 def _store_groups(geo: CacheGeometry, st: dict, u0: int, Kq: np.ndarray, Vq: np.ndarray):
     """Quantize tokens [S+u0, S+u0+n) (fp32 [B, H, n, D], n a multiple of G,
-    u0 a multiple of G) into the state's code and parameter arrays."""
+    u0 a multiple of G) into the state's code and parameter arrays, at
+    storage rows u mod qcap (W2).  Groups are stored in token order, so a
+    group that wraps the ring overwrites the oldest ones."""
     n = Kq.shape[2]
     if n == 0:
         return
+    if u0 + n > geo.qcap or u0 >= geo.qcap:
+        for k in range(n // geo.G):
+            sl = slice(k * geo.G, (k + 1) * geo.G)
+            _store_groups_at(geo, st, (u0 + k * geo.G) % geo.qcap, Kq[:, :, sl], Vq[:, :, sl])
+        return
+    _store_groups_at(geo, st, u0, Kq, Vq)
+
+
+def _store_groups_at(geo: CacheGeometry, st: dict, r0: int, Kq: np.ndarray, Vq: np.ndarray):
+    """Quantize n tokens (fp32 [B, H, n, D]) into storage rows r0 .. r0 + n
+    (n and r0 multiples of G, no wrap)."""
+    n = Kq.shape[2]
     b = geo.bits
     kc, kd, kz = quantize_keys_per_channel(Kq, geo.G, b)
     vc, vd, vz = quantize_values_per_token(Vq, b)
-    st["k_codes"][:, :, u0:u0 + n] = pack_key_rows(kc, b)
-    st["k_scale"][:, :, u0 // geo.G:(u0 + n) // geo.G] = kd
-    st["k_zero"][:, :, u0 // geo.G:(u0 + n) // geo.G] = kz
-    st["v_scale"][:, :, u0:u0 + n] = vd
-    st["v_zero"][:, :, u0:u0 + n] = vz
-    # value codes: write only the bytes that belong to tokens [u0, u0+n).
+    st["k_codes"][:, :, r0:r0 + n] = pack_key_rows(kc, b)
+    st["k_scale"][:, :, r0 // geo.G:(r0 + n) // geo.G] = kd
+    st["k_zero"][:, :, r0 // geo.G:(r0 + n) // geo.G] = kz
+    st["v_scale"][:, :, r0:r0 + n] = vd
+    st["v_zero"][:, :, r0:r0 + n] = vz
+    # value codes: write only the bytes that belong to tokens [r0, r0+n).
     # Blocks are independent runs of bytes, so work on the covered blocks.
     L = value_block_tokens(b)
-    blk0, blk1 = u0 // L, -(-(u0 + n) // L)
+    blk0, blk1 = r0 // L, -(-(r0 + n) // L)
     span = (blk1 - blk0) * L
     part = np.zeros((geo.B, geo.Hkv, span, geo.D), np.uint8)
-    part[:, :, u0 - blk0 * L:u0 - blk0 * L + n] = vc
+    part[:, :, r0 - blk0 * L:r0 - blk0 * L + n] = vc
     packed = pack_value_codes(part, b)
     touched = np.zeros((span, geo.D), np.uint8)
-    touched[u0 - blk0 * L:u0 - blk0 * L + n] = 1
+    touched[r0 - blk0 * L:r0 - blk0 * L + n] = 1
     tmask = pack_value_codes(touched, b) != 0      # bytes holding these tokens
     # a byte only ever holds tokens of one 32-token step, and a step lies in
     # one G-group (G is a multiple of 32), so whole bytes move.
     blk_bytes = L * geo.D * b // 8
     dst = st["v_codes"][:, :, blk0 * blk_bytes:blk1 * blk_bytes]
     dst[:, :, tmask] = packed[:, :, tmask]
+
+
+def storage_row(geo: CacheGeometry, u):
+    """Storage row of quantized token u (token S + u), W2."""
+    return u % geo.qcap if geo.qcap else u
 
 
 def prefill(geo: CacheGeometry, K: np.ndarray, V: np.ndarray, T: int) -> dict:
@@ -391,44 +429,67 @@ def append(geo: CacheGeometry, st: dict, n_before: int, k_new: np.ndarray,
 
 
 def valid_masks(geo: CacheGeometry, T: int) -> dict:
-    """Which parts of each buffer hold cache contents after T tokens."""
+    """Which parts of each buffer hold cache contents after T tokens: the
+    sinks, the ring slots of the full-precision tokens, and the storage rows
+    of the last min(Q, qcap) quantized tokens (all Q without a window)."""
     ns, Q, nr = partition(T, geo.S, geo.R, geo.G)
     ring = np.zeros(geo.ring, bool)
     for t in range(geo.S + Q, T):
         ring[ring_slot(t, geo.S, geo.R, geo.G)] = True
+    rows = np.zeros(geo.qcap, bool)
+    for u in range(max(0, Q - geo.qcap), Q):
+        rows[storage_row(geo, u)] = True
+    ones = np.zeros((geo.qcap, geo.D), np.uint8)
+    ones[rows] = 2 ** geo.bits - 1
+    groups = rows.reshape(-1, geo.G).all(axis=1) if geo.qcap else np.zeros(0, bool)
     return {
-        "n_sink": ns, "Q": Q, "ring": ring,
-        "v_bytes": value_valid_byte_mask(Q, geo.qcap, geo.bits, geo.D),
+        "n_sink": ns, "Q": Q, "ring": ring, "rows": rows, "groups": groups,
+        "v_bytes": pack_value_codes(ones, geo.bits) != 0,
     }
+
+
+def window_start(geo: CacheGeometry, T: int) -> int:
+    """First quantized token u the decode query attends to (W1): tokens
+    before max(S, T - W) are outside the window."""
+    if not geo.window:
+        return 0
+    return max(0, T - geo.window - geo.S)
 
 
 # ----------------------------------------------------------------------------
 # step 5: dequantize in fp64 ([GUIDE] step 5: dequantized group by group)
 # ----------------------------------------------------------------------------
 def dequant_cache(geo: CacheGeometry, st: dict, T: int, heads=None):
-    """K_hat, V_hat in fp64, [B, len(heads), T, D], in token order."""
+    """K_hat, V_hat in fp64, [B, len(heads), n, D], of the n tokens the decode
+    query attends to, in token order: all T without a window; the sinks and
+    the last W tokens with one (W1)."""
     heads = range(geo.Hkv) if heads is None else heads
     heads = list(heads)
     ns, Q, nr = partition(T, geo.S, geo.R, geo.G)
+    u_lo = window_start(geo, T)
+    nq = max(0, Q - u_lo)
+    n = ns + nq + nr
     B, D = geo.B, geo.D
-    Kh = np.zeros((B, len(heads), T, D), np.float64)
-    Vh = np.zeros((B, len(heads), T, D), np.float64)
+    Kh = np.zeros((B, len(heads), n, D), np.float64)
+    Vh = np.zeros((B, len(heads), n, D), np.float64)
+    rows = storage_row(geo, np.arange(u_lo, Q))
     for i, h in enumerate(heads):
         Kh[:, i, :ns] = to_f32(st["k_sink"][:, h, :ns], geo.dtype)
         Vh[:, i, :ns] = to_f32(st["v_sink"][:, h, :ns], geo.dtype)
-        if Q:
-            kc = unpack_key_rows(st["k_codes"][:, h, :Q], geo.bits, D).astype(np.float64)
-            kd = np.repeat(st["k_scale"][:, h, :Q // geo.G], geo.G, axis=1).astype(np.float64)
-            kz = np.repeat(st["k_zero"][:, h, :Q // geo.G], geo.G, axis=1).astype(np.float64)
-            Kh[:, i, geo.S:geo.S + Q] = kc * kd + kz
-            vc = unpack_value_codes(st["v_codes"][:, h], geo.bits, D, Q).astype(np.float64)
-            vd = st["v_scale"][:, h, :Q].astype(np.float64)[..., None]
-            vz = st["v_zero"][:, h, :Q].astype(np.float64)[..., None]
-            Vh[:, i, geo.S:geo.S + Q] = vc * vd + vz
-        for t in range(geo.S + Q, T):
+        if nq:
+            kc = unpack_key_rows(st["k_codes"][:, h][:, rows], geo.bits, D).astype(np.float64)
+            kd = st["k_scale"][:, h][:, rows // geo.G].astype(np.float64)
+            kz = st["k_zero"][:, h][:, rows // geo.G].astype(np.float64)
+            Kh[:, i, ns:ns + nq] = kc * kd + kz
+            vc_all = unpack_value_codes(st["v_codes"][:, h], geo.bits, D, geo.qcap)
+            vc = vc_all[:, rows].astype(np.float64)
+            vd = st["v_scale"][:, h][:, rows].astype(np.float64)[..., None]
+            vz = st["v_zero"][:, h][:, rows].astype(np.float64)[..., None]
+            Vh[:, i, ns:ns + nq] = vc * vd + vz
+        for j, t in enumerate(range(geo.S + Q, T)):
             sl = ring_slot(t, geo.S, geo.R, geo.G)
-            Kh[:, i, t] = to_f32(st["k_resid"][:, h, sl], geo.dtype)
-            Vh[:, i, t] = to_f32(st["v_resid"][:, h, sl], geo.dtype)
+            Kh[:, i, ns + nq + j] = to_f32(st["k_resid"][:, h, sl], geo.dtype)
+            Vh[:, i, ns + nq + j] = to_f32(st["v_resid"][:, h, sl], geo.dtype)
     return Kh, Vh
 
 

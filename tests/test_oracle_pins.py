@@ -447,3 +447,89 @@ def test_row_rel_error_definition():
     o[0, 0, 1] += 0.002
     o[0, 1, 0] -= 0.0001
     assert O.row_rel_error(o, ref) == pytest.approx(max(0.002 / 2.0, 0.0001 / 0.5))
+
+
+# --------------------------------------------------------------- sliding window
+# [KIVI-PR] "The idea" and "Relationship to other PRs": the quantized store
+# composes with a bounded sliding-window cache.  Readings W1 (the query
+# attends to the sinks and the last W tokens) and W2 (ring storage of the
+# quantized tokens, the oldest group evicted).
+WINDOW_CASES = [
+    # B, Hq, Hkv, D, bits, G, S, R, W, T, dtype
+    (1, 2, 1, 16, 4, 4, 2, 4, 12, 300, "f32"),
+    (2, 4, 2, 16, 2, 8, 0, 8, 24, 260, "f16"),
+    (1, 2, 2, 16, 8, 32, 3, 0, 40, 333, "bf16"),
+    (1, 4, 1, 16, 4, 64, 4, 32, 200, 700, "f32"),
+]
+
+
+def _window_inputs(case, seed=0):
+    B, Hq, Hkv, D, bits, G, S, R, W, T, dt = case
+    data = synth.random_case(seed + sum(case[:10]), B, Hq, Hkv, D, T, dt)
+    return data, dt
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_window_decode_is_plain_attention_over_the_window(case):
+    """Decode through the bounded ring equals torch SDPA over the sinks and
+    the last W tokens, taken from the unbounded cache's dequantized tokens
+    (same groups, same codes), at every length from the window's first wrap
+    to T."""
+    B, Hq, Hkv, D, bits, G, S, R, W, T, dt = case
+    data, dt = _window_inputs(case)
+    geo_w = O.CacheGeometry(B, Hkv, D, bits, G, S, R, T, dt, window=W)
+    geo_u = O.CacheGeometry(B, Hkv, D, bits, G, S, R, T, dt)
+    assert geo_w.qcap < geo_u.qcap                    # the ring is smaller than the cache
+    g = Hq // Hkv
+    for n in sorted({T, T - 1, T - 7, geo_w.qcap + S + R + 1, geo_w.qcap + S + R + G + 3}):
+        st_w = O.prefill(geo_w, data["K"], data["V"], n)
+        st_u = O.prefill(geo_u, data["K"], data["V"], n)
+        Kh, Vh = O.dequant_cache(geo_u, st_u, n)       # all n tokens in order
+        idx = sorted(set(range(min(S, n))) | set(range(max(S, n - W), n)))
+        q = torch.from_numpy(O.to_f32(data["q"], dt).astype(np.float64))
+        k = torch.from_numpy(np.repeat(Kh[:, :, idx], g, axis=1))
+        v = torch.from_numpy(np.repeat(Vh[:, :, idx], g, axis=1))
+        ref = torch.nn.functional.scaled_dot_product_attention(q[:, :, None], k, v)[:, :, 0].numpy()
+        out = O.decode(geo_w, st_w, n, data["q"], Hq)
+        assert np.abs(out - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES[:3], ids=lambda c: "-".join(map(str, c)))
+def test_window_prefill_equals_streaming_appends(case):
+    """With a window, n appends leave the same live storage rows, key
+    groups, value bytes and full-precision slots as a prefill of n tokens,
+    through every eviction ([STORE-PR] frozen blocks; W2)."""
+    B, Hq, Hkv, D, bits, G, S, R, W, T, dt = case
+    data, dt = _window_inputs(case, seed=3)
+    geo = O.CacheGeometry(B, Hkv, D, bits, G, S, R, T, dt, window=W)
+    st = O.prefill(geo, data["K"], data["V"], 0)
+    for n in range(T):
+        st = O.append(geo, st, n, data["K"][:, :, n], data["V"][:, :, n])
+        ref = O.prefill(geo, data["K"], data["V"], n + 1)
+        vm = O.valid_masks(geo, n + 1)
+        rows, groups = vm["rows"], vm["groups"]
+        for name in ("k_codes", "v_scale", "v_zero"):
+            assert np.array_equal(st[name][:, :, rows], ref[name][:, :, rows]), (n, name)
+        for name in ("k_scale", "k_zero"):
+            assert np.array_equal(st[name][:, :, groups], ref[name][:, :, groups]), (n, name)
+        assert np.array_equal(st["v_codes"][:, :, vm["v_bytes"]], ref["v_codes"][:, :, vm["v_bytes"]])
+        assert np.array_equal(st["k_resid"][:, :, vm["ring"]], ref["k_resid"][:, :, vm["ring"]])
+
+
+def test_window_store_is_bounded():
+    """The store no longer grows with the sequence: qcap is W + G rounded up
+    to a multiple of max(64, G) for any capacity, and the live rows after
+    many evictions are exactly the last qcap quantized tokens."""
+    for W, G, R in ((4096, 32, 128), (200, 64, 32), (40, 32, 0)):
+        for cap in (W + 10, 10 ** 5, 10 ** 7):
+            geo = O.CacheGeometry(1, 1, 64, 4, G, 4, R, cap, "bf16", window=W)
+            step = max(64, G)
+            assert geo.qcap == -(-min(cap - 4, W + G) // step) * step
+    geo = O.CacheGeometry(1, 1, 16, 4, 8, 0, 8, 10 ** 4, "f32", window=24)
+    T = 1000
+    _, Q, _ = O.partition(T, 0, 8, 8)
+    rows = O.valid_masks(geo, T)["rows"]
+    assert rows.sum() == geo.qcap and Q > 4 * geo.qcap
+    # the window's quantized tokens all sit in live rows
+    u_lo = O.window_start(geo, T)
+    assert all(rows[u % geo.qcap] for u in range(u_lo, Q)) and u_lo >= Q - geo.qcap

@@ -85,25 +85,36 @@ def partition(T, S, R, G):
     return n_sink, Q, n - Q
 
 
+def window_start(w, T: int) -> int:
+    """First quantized token the query attends to (0 without a window)."""
+    return max(0, T - w.window - w.sink) if w.window else 0
+
+
 def algorithmic_bytes(w, T: int) -> int:
     """Bytes one decode-attention call must read: packed K and V codes, key
     group (delta, zero) pairs, value token (delta, zero) pairs and the
-    full-precision sink + residual tokens, over all (batch, KV head)."""
+    full-precision sink + residual tokens of the tokens it attends to (the
+    sinks and the last W tokens with a window), over all (batch, KV head)."""
     ns, Q, nr = partition(T, w.sink, w.residual, w.group)
+    u_lo = window_start(w, T)
+    nq = Q - u_lo
+    ng = (Q - 1) // w.group - u_lo // w.group + 1 if nq > 0 else 0
     D, b = w.head_dim, w.bits
     eb = 4 if w.dtype == "f32" else 2
-    per_head = (2 * Q * D * b // 8 + (Q // w.group) * D * 8 + Q * 8 + 2 * (ns + nr) * D * eb)
+    per_head = (2 * nq * D * b // 8 + ng * D * 8 + nq * 8 + 2 * (ns + nr) * D * eb)
     return per_head * w.batch * w.n_kv_heads
 
 
-def prefill_bytes(w, T: int) -> int:
+def prefill_bytes(w, T: int, qcap: int) -> int:
     """Bytes a prefill of T tokens moves: K and V read in the input dtype,
     packed codes, key group and value token (delta, zero) pairs and the
-    exact sink / residual rows written."""
+    exact sink / residual rows written.  With a window only the last qcap
+    quantized tokens are quantized (older ones would be evicted)."""
     ns, Q, nr = partition(T, w.sink, w.residual, w.group)
+    Q = min(Q, qcap)
     D, b = w.head_dim, w.bits
     eb = 4 if w.dtype == "f32" else 2
-    per_head = (2 * T * D * eb + 2 * Q * D * b // 8 + (Q // w.group) * D * 8 + Q * 8
+    per_head = (2 * (ns + Q + nr) * D * eb + 2 * Q * D * b // 8 + (Q // w.group) * D * 8 + Q * 8
                 + 2 * (ns + nr) * D * eb)
     return per_head * w.batch * w.n_kv_heads
 
@@ -116,7 +127,7 @@ def decode_splits(w, T: int, cus: int, ws_splits: int = 1024) -> int:
     ns, Q, nr = partition(T, w.sink, w.residual, w.group)
     n_fp = ns + nr
     if w.gqa in (4, 8) and w.bits != 8 and Q > 0:
-        nblk = -(-Q // 64)
+        nblk = -(-Q // 64) - window_start(w, T) // 64
         want = max(1, 2 * cus // (w.batch * w.n_kv_heads))
         want = min(want, nblk, ws_splits)
         bps = -(-nblk // want)
@@ -136,9 +147,9 @@ def cpu_baseline(w, data, sample_seconds: float):
 
     T = w.n_tokens
     geo = O.CacheGeometry(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink,
-                          w.residual, w.capacity, w.dtype)
+                          w.residual, w.capacity, w.dtype, w.window)
     geo1 = O.CacheGeometry(w.batch, 1, w.head_dim, w.bits, w.group, w.sink, w.residual,
-                           T + max(w.steps, 2 * w.group + w.residual + 1), w.dtype)
+                           T + max(w.steps, 2 * w.group + w.residual + 1), w.dtype, w.window)
     g = w.gqa
     rows = [(0, h) for h in range(g)]          # the q heads of KV head 0
     with threadpool_limits(limits=1):
@@ -235,7 +246,7 @@ def main():
     data = synth.generate(w, steps=n_gen)
     log(f"inputs generated in {time.time() - t0:.1f}s")
     cfg = kvq.Config(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink, w.residual,
-                     w.n_tokens + steps_cap, w.dtype)
+                     w.n_tokens + steps_cap, w.dtype, w.window)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def dev(a):
@@ -369,7 +380,7 @@ def main():
     bytes_per_call = sum(algorithmic_bytes(w, T) for T in attn_T) / n_calls
     achieved = bytes_per_call / (mean_attn_ms / 1e3) / 1e9
     splits = decode_splits(w, n_tok[0], cus)
-    pbytes = prefill_bytes(w, T0)
+    pbytes = prefill_bytes(w, T0, cfg.qcap)
     detail = {
         "attn_us_mean": round(mean_attn_ms * 1e3, 3),
         "attn_us_groups_of_20": {"median": round(float(np.median(groups)), 3),
@@ -408,10 +419,12 @@ def main():
         "config": {
             "workload": f"{w.name}: layer B{w.batch} Hq{w.n_q_heads} Hkv{w.n_kv_heads} "
                         f"D{w.head_dim} T{w.n_tokens}{'+decode' if streaming else ''} {w.dtype} "
-                        f"inputs int{w.bits} G{w.group} R{w.residual} S{w.sink}",
+                        f"inputs int{w.bits} G{w.group} R{w.residual} S{w.sink}"
+                        + (f" window {w.window}" if w.window else ""),
             "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "cached_tokens": w.n_tokens, "bits": w.bits,
             "group": w.group, "residual": w.residual, "sink": w.sink, "input_dtype": w.dtype,
+            "window": w.window,
             "step": ("append + decode attention, one layer" if streaming
                      else "decode attention, one layer"),
         },

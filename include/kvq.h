@@ -38,6 +38,14 @@
  *  - GQA: query head hq reads KV head hq / (Hq / Hkv).
  *  - The decode query attends to all n_tokens cached tokens (no mask);
  *    softmax_scale <= 0 selects 1/sqrt(D).
+ *  - Sliding window (tract PR "KIVI-style KV-cache quantization", The idea
+ *    and Relationship to other PRs: the quantized store composes with a
+ *    bounded sliding-window cache): with window W > 0 the query attends to
+ *    the sinks and to the last W tokens [max(S, n_tokens - W), n_tokens),
+ *    exactly to the token; W >= R + G is required.  The quantized store is
+ *    then a ring: quantized token u (token S + u) lives at storage row
+ *    u mod qcap, so each group that freezes evicts the oldest one, and the
+ *    cache's size no longer grows with n_tokens.
  *
  * Conventions for every entry point:
  *  - All pointers except `cfg`, `cache` (the structs themselves) are
@@ -87,21 +95,24 @@ typedef struct {
   int32_t residual;   /* R: most recent tokens kept exact               */
   int32_t dtype;      /* kvq_dtype of K, V, q and the exact stores      */
   int64_t capacity;   /* maximum number of cached tokens                */
+  int64_t window;     /* W: sliding window in tokens, 0 = none (below)  */
 } kvq_config;
 
 /*
  * Cache buffers (device memory, caller-allocated; sizes below).
  *
- * qcap = max(0, capacity - S) rounded up to a multiple of max(64, G).
+ * qcap = max(0, capacity - S), at most W + G with a window, rounded up to
+ * a multiple of max(64, G).  Storage row r holds quantized token u with
+ * r = u mod qcap (r = u without a window, as u < qcap).
  *
- * k_codes  u8 [B][Hkv][qcap][D*b/8]: token-major key codes.  Row u holds
+ * k_codes  u8 [B][Hkv][qcap][D*b/8]: token-major key codes.  Row r holds
  *          quantized token t = S + u; channel d sits at bit offset d*b of
  *          the row (byte d*b/8, bits (d*b)%8 .. +b), low bits first.
  * k_scale, k_zero  f32 [B][Hkv][qcap/G][D]: delta and zero point of key
- *          group k (tokens S+kG .. S+kG+G-1), per channel.  Frozen once
- *          written.
- * v_codes  u8 [B][Hkv][vbytes]: value codes in blocks of L tokens (L = 64
- *          at 2 bits, 32 at 4 and 8 bits), vbytes = qcap/L * L*D*b/8.  A
+ *          group k (tokens S+kG .. S+kG+G-1) in slot (kG mod qcap)/G, per
+ *          channel.  Frozen once written.
+ * v_codes  u8 [B][Hkv][vbytes]: value codes in blocks of L storage rows
+ *          (L = 64 at 2 bits, 32 at 4 and 8 bits), vbytes = qcap/L * L*D*b/8.  A
  *          token offset o inside its block is split as
  *          o = 32*s + 16*h + 4*g + r (s < L/32, h < 2, g < 4, r < 4).  A
  *          block holds 4*D units; unit (g*16 + d%16)*(D/16) + d/16 holds
@@ -112,7 +123,7 @@ typedef struct {
  *          each 32-token step, the 8 tokens one wave lane needs for one
  *          channel in one contiguous run.
  * v_scale, v_zero  f32 [B][Hkv][qcap]: delta and zero point of each
- *          quantized value token.
+ *          quantized value token, at its storage row.
  * k_sink, v_sink   dtype [B][Hkv][S][D]: tokens 0..S-1, exact.
  * k_resid, v_resid dtype [B][Hkv][R+G][D]: full-precision ring; token
  *          t >= S lives in slot (t - S) mod (R + G).
@@ -147,6 +158,7 @@ static inline int64_t kvq_qcap(const kvq_config *c) {
   int64_t step = c->group > 64 ? c->group : 64;
   int64_t n = c->capacity - c->sink;
   if (n < 0) n = 0;
+  if (c->window > 0 && n > c->window + c->group) n = c->window + c->group;
   return (n + step - 1) / step * step;
 }
 static inline int64_t kvq_dtype_bytes(int32_t dt) { return dt == KVQ_F32 ? 4 : 2; }

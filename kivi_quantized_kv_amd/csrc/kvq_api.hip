@@ -48,6 +48,8 @@ kvq_status check_config(const kvq_config* c) {
   if (c->group != 32 && c->group != 64 && c->group != 128) return KVQ_EUNSUPPORTED;
   if (c->dtype != KVQ_F32 && c->dtype != KVQ_F16 && c->dtype != KVQ_BF16) return KVQ_EUNSUPPORTED;
   if (c->capacity > (int64_t(1) << 40)) return KVQ_EINVAL;
+  // a window holds at least the full-precision tokens
+  if (c->window < 0 || (c->window > 0 && c->window < int64_t(c->residual) + c->group)) return KVQ_EINVAL;
   return KVQ_OK;
 }
 
@@ -171,8 +173,13 @@ kvq_status prefill_half(const kvq_config* c, const kvq_cache* k, const kvq_tenso
     q.scale = keys ? k->k_scale : k->v_scale;
     q.zero = keys ? k->k_zero : k->v_zero;
     q.S = S; q.qcap = kvq_qcap(c); q.H = H; q.G = int(G);
-    hipError_t e = keys ? dispatch3<QuantKeysFn>(c, q, Q / G, B, H, s)
-                        : dispatch3<QuantValuesFn>(c, q, Q / 32, B, H, s);
+    // with a window only the groups of the last qcap quantized tokens are
+    // kept (older ones would be evicted by them), each storage slot once
+    const int64_t k_first = Q > q.qcap ? (Q - q.qcap) / G : 0;
+    q.k0 = keys ? k_first : k_first * G / 32;
+    const int64_t n_units = keys ? Q / G - k_first : (Q - k_first * G) / 32;
+    hipError_t e = keys ? dispatch3<QuantKeysFn>(c, q, n_units, B, H, s)
+                        : dispatch3<QuantValuesFn>(c, q, n_units, B, H, s);
     if (e != hipSuccess) return KVQ_EHIP;
   }
   return KVQ_OK;
@@ -222,6 +229,7 @@ extern "C" kvq_status kvq_append_token(const kvq_config* cfg, const kvq_cache* c
     a.k_sink = cache->k_sink; a.v_sink = cache->v_sink;
     a.k_resid = cache->k_resid; a.v_resid = cache->v_resid;
     a.n_before = n_before; a.q_old = q_old; a.S = S; a.R = R; a.qcap = kvq_qcap(cfg);
+    a.r_old = a.qcap > 0 ? q_old % a.qcap : 0;
     a.H = cfg->n_kv_heads; a.G = int(G); a.flush = q_new > q_old ? 1 : 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (dispatch3<AppendFn>(cfg, a, cfg->batch, cfg->n_kv_heads, s) != hipSuccess) return KVQ_EHIP;
@@ -277,7 +285,12 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
   const int gqa = n_q_heads / H;
   const bool mfma = (gqa == 4 || gqa == 8) && cfg->bits != 8 && Q > 0;
   const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
-  const int64_t nblk = (Q + L - 1) / L;
+  const int64_t qcap = kvq_qcap(cfg);
+  // sliding window: quantized tokens before u_lo are not attended; the
+  // kernels' units (chunks or value blocks) start at c0
+  const int64_t u_lo = cfg->window > 0 && T - cfg->window - S > 0 ? T - cfg->window - S : 0;
+  const int64_t c0 = u_lo / L;
+  const int64_t nblk = (Q + L - 1) / L - c0;   // live units
   int64_t fp_per_split = 32;
   int64_t bps = 1;
   int64_t n_split = 0;
@@ -341,6 +354,11 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
   a.blocks_per_split = int(bps);
   a.fp_per_split = int(fp_per_split);
   a.ml_offset = int64_t(B) * n_q_heads * n_split * D;
+  a.u_lo = u_lo;
+  a.c0 = c0;
+  a.ncap = qcap / L;
+  a.cw = a.ncap > 0 ? c0 / a.ncap * a.ncap : 0;
+  a.lo_off = int(u_lo - c0 * L);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t ea = hipSuccess;
   if (a.n_split > 0) {

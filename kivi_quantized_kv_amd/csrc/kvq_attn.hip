@@ -276,7 +276,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
     return max_xor32(max_xor16(v));
   };
 
-  const int64_t nblk = (a.Q + VL::L - 1) / VL::L;
+  // Blocks are numbered from the first one the query attends to (block c0,
+  // the first of the sliding window; 0 without one).
+  const int64_t nblk = (a.Q + VL::L - 1) / VL::L - a.c0;
   const int64_t blk0 = int64_t(split) * a.blocks_per_split;
   const int64_t blk1 = blk0 + a.blocks_per_split < nblk ? blk0 + a.blocks_per_split : nblk;
   const int64_t per_wave = blk1 > blk0 ? (blk1 - blk0 + NW - 1) / NW : 0;
@@ -319,8 +321,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
   // tokens past the quantized count are masked after the loads.  Code words
   // are read once per call: non-temporal loads keep them out of the way of
   // the parameters in the caches.
+  // first storage row of block blk: the ring's block slot (c0 + blk) mod
+  // (qcap / L), by one conditional subtraction (the live blocks span at most
+  // qcap / L + 1 slots)
+  auto blk_base = [&](int64_t blk) -> int64_t {
+    int64_t s = a.c0 + blk - a.cw;
+    if (s >= a.ncap) s -= a.ncap;
+    return s * VL::L;
+  };
   auto load_blk = [&](int64_t blk, Blk& r) {
-    const int64_t base = blk * VL::L;
+    const int64_t base = blk_base(blk);
     const uint8_t* kb = kc_head + base * kRowBytes;
 #pragma unroll
     for (int st = 0; st < kNST; ++st) {
@@ -407,8 +417,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
 
   // ---- quantized blocks
   auto process = [&](int64_t blk, const Blk& r) {
-    const int64_t base = blk * VL::L;
+    const int64_t base = (a.c0 + blk) * VL::L;   // quantized index of the block's first token
     const int nvalid = int(a.Q - base < VL::L ? a.Q - base : VL::L);
+    const int lo = blk == 0 ? a.lo_off : 0;      // tokens before the window
     // key-group coefficients of each 32-token half
     float kap[kHalves];
 #pragma unroll
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
         // group past the count are never written and may hold anything)
         const int st = 2 * k + u;
         const float v = __builtin_fmaf(quad_sum(dot[u]), kS, kap[k]);
-        sc[st] = st * 16 + tl < nvalid ? v : -__builtin_inff();
+        sc[st] = st * 16 + tl < nvalid && st * 16 + tl >= lo ? v : -__builtin_inff();
       }
     }
     wave_lds_sync();
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
     float vmax = 0.f;
 #pragma unroll
     for (int st = 0; st < kNST; ++st) {
-      dvs[st] = st * 16 + tl < nvalid ? r.dv[st] : 0.f;
+      dvs[st] = st * 16 + tl < nvalid && st * 16 + tl >= lo ? r.dv[st] : 0.f;
       vmax = __builtin_fmaxf(vmax, dvs[st]);
     }
     if (__builtin_amdgcn_ballot_w64(vmax >= vthr) != 0) {   // rare: a larger value delta
@@ -467,7 +478,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
     const int vke = vexp + 24 + fsh;
 #pragma unroll
     for (int st = 0; st < kNST; ++st) {
-      const bool ok = st * 16 + tl < nvalid;
+      const bool ok = st * 16 + tl < nvalid && st * 16 + tl >= lo;
       const float p = __builtin_amdgcn_exp2f(sc[st] - m);   // 0 past the range
       const float zv = ok ? r.zv[st] : 0.f;
       l += p;

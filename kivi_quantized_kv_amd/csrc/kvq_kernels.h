@@ -26,6 +26,8 @@ struct QuantArgs {
   float* scale;
   float* zero;
   int64_t S, qcap;
+  int64_t k0;               // first unit quantized (groups or 32-token steps); unit k goes to
+                            // storage (k * unit tokens) mod qcap
   int H, G;
 };
 
@@ -38,6 +40,7 @@ struct AppendArgs {
   float *k_scale, *k_zero, *v_scale, *v_zero;
   void *k_sink, *v_sink, *k_resid, *v_resid;
   int64_t n_before, q_old, S, R, qcap;
+  int64_t r_old;            // storage row of quantized token q_old: q_old mod qcap
   int H, G, flush;
 };
 
@@ -65,6 +68,13 @@ struct AttnArgs {
                             // kernel deals chunks to its waves in turn instead)
   int fp_per_split;         // full-precision tokens per split
   int64_t ml_offset;        // floats before the (m, l) pairs in ws
+  // Sliding window: quantized tokens before u_lo are outside it.  The
+  // kernel's units (64-token chunks, or value blocks for the VALU kernel)
+  // start at unit c0; unit c sits at storage unit c - cw, less ncap when
+  // that reaches ncap (live units span at most ncap + 1, so one subtraction
+  // suffices); lo_off = u_lo - c0 * unit tokens of unit c0 are masked.
+  int64_t u_lo, c0, cw, ncap;
+  int lo_off;
 };
 
 __device__ __forceinline__ float* partial_o(const AttnArgs& a, int64_t row, int split, int D) {

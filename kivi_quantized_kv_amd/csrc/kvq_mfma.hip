@@ -250,12 +250,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   __shared__ float4 s_kp0[4][2][2 * D / 4], s_kp1[4][2][2 * D / 4];   // [wave][group][delta | zero]
   __shared__ float s_vp0[4][2][64], s_vp1[4][2][64];                  // [wave][delta | zero][token]
 
-  // this wave's chunks: gw, gw + nw_row, ... (none for waves past the
-  // chunk count, whose splits only take exact tokens)
-  const int64_t nch = (a.Q + 63) >> 6;
+  // Chunks are numbered from the first one the query attends to (chunk c0,
+  // the first of the sliding window; 0 without one).  This wave's chunks:
+  // gw, gw + nw_row, ... (none for waves past the chunk count, whose splits
+  // only take exact tokens).
+  const int64_t nch = ((a.Q + 63) >> 6) - a.c0;
   const int64_t nw_row = int64_t(a.n_split) * 4;
   const int64_t gw = int64_t(split) * 4 + wave;
   const int64_t wn = gw < nch ? (nch - gw + nw_row - 1) / nw_row : 0;
+  // first storage row of chunk ch: the ring's chunk slot (c0 + ch) mod
+  // (qcap / 64), by one conditional subtraction (the live chunks span at
+  // most qcap / 64 + 1 slots)
+  auto chunk_base = [&](int64_t ch) -> int64_t {
+    int64_t s = a.c0 + ch - a.cw;
+    if (s >= a.ncap) s -= a.ncap;
+    return s << 6;
+  };
   const uint8_t* kc_head = a.k_codes + bh * a.qcap * kRB;
   const uint8_t* vc_head = a.v_codes + bh * a.qcap * kRB;
   const float* vs_head = a.v_scale + bh * a.qcap;
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     constexpr int BUF = decltype(buf_tag)::value;
     auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
     auto& vpb = BUF == 0 ? s_vp0 : s_vp1;
-    const int64_t base = live ? ch << 6 : 0;
+    const int64_t base = live ? chunk_base(ch) : 0;
     const int cl = live ? col : 0, lgl = live ? lg : 0, ll = live ? lane : 0;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -727,6 +737,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         }
         return c;
       };
+      // the sliding window's first chunk: scores of the tokens before the
+      // window are -inf (p = 0)
+      auto mask_front = [&]() {
+        if (ch == 0 && a.lo_off > 0) {
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * t + 4 * lg + i < a.lo_off) sc[t][i] = -__builtin_inff();
+        }
+      };
+      mask_front();
       float cm = chunk_max();
       // the head's max over lanes is only needed when the running max
       // moves: any lane over m + slack means its head's max is
@@ -782,7 +804,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
               for (int t = 0; t < 4; ++t) {
                 if (t < t_begin || t >= t_end) continue;
                 const uint32_t w = reinterpret_cast<const uint32_t*>(
-                    kc_head + ((ch << 6) + 16 * t + col) * kRB + lg * (kQW * 4))[wk];
+                    kc_head + (chunk_base(ch) + 16 * t + col) * kRB + lg * (kQW * 4))[wk];
                 u32x4_t av;
                 if (kk % kStepsPerWord == 0) av = code_fields<BITS, 0>(w);
                 else av = code_fields<BITS, 1>(w);
@@ -805,6 +827,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           }
           kap[0] = 0.f;
           kap[1] = 0.f;
+          mask_front();
           cm = chunk_max();
           need_m = __builtin_amdgcn_ballot_w64(cm > m + kSlack);
         }

@@ -250,7 +250,7 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
 }
 
 // ----------------------------------------------------------------------------
-// One 32-token step of values (quantized tokens u0 .. u0 + 31, u0 a multiple
+// One 32-token step of values (storage rows u0 .. u0 + 31, u0 a multiple
 // of 32), 256 threads: per-token min / max across the lanes of the token,
 // delta and zero point, codes through LDS (channel-major) into the value-code
 // units of the layout in kvq.h.  At 2 bits a block holds two steps; a step
@@ -369,15 +369,17 @@ __global__ __launch_bounds__(64) void k_copy_fp_rows(FpCopyArgs a) {
     reinterpret_cast<uint4*>(dst)[v] = reinterpret_cast<const uint4*>(src)[v];
 }
 
-// grid: x = unit (key group, or 32-token value step) of the quantized range,
-// y = head, z = batch.  One unit per workgroup: many small resident
+// grid: x = unit (key group, or 32-token value step) of the quantized range
+// from unit a.k0 on, y = head, z = batch; unit k is stored at storage row
+// (k * unit tokens) mod qcap.  One unit per workgroup: many small resident
 // workgroups at different phases overlap loads with arithmetic better than
 // fewer workgroups streaming several units each (measured).
 template <int DT, int D, int BITS, int G>
 __global__ __launch_bounds__(256) void k_quant_keys(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) float s_red[8][D];
   __shared__ __attribute__((aligned(16))) float s_par[4][D];
-  const int64_t k = blockIdx.x;
+  const int64_t k = a.k0 + blockIdx.x;
+  const int64_t ks = k % (a.qcap / G);              // storage slot of group k
   const int h = blockIdx.y, b = blockIdx.z;
   constexpr int EB = Elem<DT>::bytes;
   const int64_t bh = int64_t(b) * a.H + h;
@@ -386,14 +388,15 @@ __global__ __launch_bounds__(256) void k_quant_keys(QuantArgs a) {
       InputRows{reinterpret_cast<const uint8_t*>(a.src) + (b * a.sb + h * a.sh + (a.S + k * G) * a.st) * EB,
                 a.st * EB},
       kr);
-  key_group<DT, D, BITS, G>(kr, a.scale + (bh * (a.qcap / G) + k) * D, a.zero + (bh * (a.qcap / G) + k) * D,
-                            a.codes + (bh * a.qcap + k * G) * (D * BITS / 8), s_red, s_par);
+  key_group<DT, D, BITS, G>(kr, a.scale + (bh * (a.qcap / G) + ks) * D, a.zero + (bh * (a.qcap / G) + ks) * D,
+                            a.codes + (bh * a.qcap + ks * G) * (D * BITS / 8), s_red, s_par);
 }
 
 template <int DT, int D, int BITS>
 __global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[D * kStepPitch];
-  const int64_t st = blockIdx.x;
+  const int64_t st = a.k0 + blockIdx.x;
+  const int64_t r0 = (32 * st) % a.qcap;            // storage row of the step's first token
   const int h = blockIdx.y, b = blockIdx.z;
   constexpr int EB = Elem<DT>::bytes;
   const int64_t bh = int64_t(b) * a.H + h;
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
       InputRows{reinterpret_cast<const uint8_t*>(a.src) + (b * a.sb + h * a.sh + (a.S + 32 * st) * a.st) * EB,
                 a.st * EB},
       sr);
-  value_step<DT, D, BITS>(sr, 32 * st, a.scale + bh * a.qcap, a.zero + bh * a.qcap,
+  value_step<DT, D, BITS>(sr, r0, a.scale + bh * a.qcap, a.zero + bh * a.qcap,
                           a.codes + bh * (a.qcap * D * BITS / 8), s_codes);
 }
 
@@ -451,12 +454,12 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     __shared__ __attribute__((aligned(16))) float s_par[4][D];
     const RingRows rows{reinterpret_cast<const uint8_t*>(a.k_resid) + bh * ring * D * EB, kin,
                         (first - a.S) % ring, ring, fresh_row, D * EB};
-    const int64_t kgrp = a.q_old / G;
+    const int64_t kgrp = a.r_old / G;                 // storage slot of the group
     KeyRows<DT, D, G> kr;
     load_key_rows<DT, D, G>(rows, kr);
     key_group<DT, D, BITS, G>(kr, a.k_scale + (bh * (a.qcap / G) + kgrp) * D,
                               a.k_zero + (bh * (a.qcap / G) + kgrp) * D,
-                              a.k_codes + (bh * a.qcap + a.q_old) * (D * BITS / 8), s_red, s_par);
+                              a.k_codes + (bh * a.qcap + a.r_old) * (D * BITS / 8), s_red, s_par);
   } else {
     __shared__ __attribute__((aligned(16))) uint8_t s_codes[D * kStepPitch];
     const int step = role - 2;
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
                         (first + 32 * step - a.S) % ring, ring, fresh_row - 32 * step, D * EB};
     StepRows<DT, D> sr;
     load_step_rows<DT, D>(rows, sr);
-    value_step<DT, D, BITS>(sr, a.q_old + 32 * step, a.v_scale + bh * a.qcap, a.v_zero + bh * a.qcap,
+    value_step<DT, D, BITS>(sr, a.r_old + 32 * step, a.v_scale + bh * a.qcap, a.v_zero + bh * a.qcap,
                             a.v_codes + bh * (a.qcap * D * BITS / 8), s_codes);
   }
 }

@@ -37,7 +37,7 @@ class c_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("sink", ctypes.c_int32),
                 ("residual", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("capacity", ctypes.c_int64)]
+                ("capacity", ctypes.c_int64), ("window", ctypes.c_int64)]
 
 
 class c_cache(ctypes.Structure):
@@ -92,11 +92,13 @@ class Config:
     residual: int
     capacity: int
     dtype: str = "bf16"
+    window: int = 0          # sliding window in tokens, 0 = none
 
     def c(self) -> c_config:
         """A new kvq_config struct of these fields."""
         return c_config(self.batch, self.n_kv_heads, self.head_dim, self.bits, self.group,
-                        self.sink, self.residual, DTYPE_CODE[self.dtype], self.capacity)
+                        self.sink, self.residual, DTYPE_CODE[self.dtype], self.capacity,
+                        self.window)
 
     def _cref(self):
         """Pointer to this config's struct, built once (the dataclass is frozen)."""
@@ -113,6 +115,8 @@ class Config:
     def qcap(self) -> int:
         step = max(64, self.group)
         n = max(0, self.capacity - self.sink)
+        if self.window > 0:
+            n = min(n, self.window + self.group)
         return -(-n // step) * step
 
     @property

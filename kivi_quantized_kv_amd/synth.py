@@ -42,6 +42,7 @@ class Workload:
     outlier_scale: float
     steps: int             # streaming decode steps (append + attention)
     seed: int
+    window: int = 0        # sliding window in tokens (0: attend to everything)
 
     @property
     def gqa(self) -> int:
@@ -61,6 +62,11 @@ WORKLOADS = {
     "mha7b": Workload("mha7b", 8, 32, 32, 128, 4096, "f16", 4, 32, 128, 4, 4, 25.0, 0, 3000),
     "mistral": Workload("mistral", 4, 32, 8, 128, 32768, "bf16", 2, 32, 128, 4, 3, 20.0, 0, 4000),
     "llama70b": Workload("llama70b", 1, 64, 8, 128, 131072, "bf16", 4, 64, 128, 4, 4, 30.0, 128, 5000),
+    # the Mistral-shaped layer with a 4096-token sliding window (the tract
+    # PR's example pairs a 4096-token window with a quantized store):
+    # bounded ring store, 64 streaming steps through evictions
+    "mistral_swa": Workload("mistral_swa", 4, 32, 8, 128, 32768, "bf16", 2, 32, 128, 4, 3, 20.0, 64, 6000,
+                            window=4096),
 }
 
 

@@ -31,7 +31,7 @@ def make(cfg_kw):
     from kivi_quantized_kv_amd import kvq
     cfg = kvq.Config(**cfg_kw)
     geo = O.CacheGeometry(cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.bits, cfg.group,
-                          cfg.sink, cfg.residual, cfg.capacity, cfg.dtype)
+                          cfg.sink, cfg.residual, cfg.capacity, cfg.dtype, cfg.window)
     return cfg, geo
 
 
@@ -50,7 +50,7 @@ def compare_state(geo, got: dict, ref: dict, T: int, heads=None):
     """Bit-exact comparison of every buffer region that holds cache
     contents after T tokens.  Returns nothing; raises AssertionError."""
     vm = O.valid_masks(geo, T)
-    Q, G, ns = vm["Q"], geo.G, vm["n_sink"]
+    rows, groups, ns = vm["rows"], vm["groups"], vm["n_sink"]
     sl = slice(None) if heads is None else heads
 
     def eq(name, a, b):
@@ -60,11 +60,11 @@ def compare_state(geo, got: dict, ref: dict, T: int, heads=None):
             raise AssertionError(f"{name} differs (shape {a.shape} vs {b.shape}); "
                                  f"first mismatches {None if bad is None else bad[:5].tolist()}")
 
-    eq("k_codes", got["k_codes"][:, sl, :Q], ref["k_codes"][:, sl, :Q])
-    eq("k_scale", got["k_scale"][:, sl, :Q // G], ref["k_scale"][:, sl, :Q // G])
-    eq("k_zero", got["k_zero"][:, sl, :Q // G], ref["k_zero"][:, sl, :Q // G])
-    eq("v_scale", got["v_scale"][:, sl, :Q], ref["v_scale"][:, sl, :Q])
-    eq("v_zero", got["v_zero"][:, sl, :Q], ref["v_zero"][:, sl, :Q])
+    eq("k_codes", got["k_codes"][:, sl][:, :, rows], ref["k_codes"][:, sl][:, :, rows])
+    eq("k_scale", got["k_scale"][:, sl][:, :, groups], ref["k_scale"][:, sl][:, :, groups])
+    eq("k_zero", got["k_zero"][:, sl][:, :, groups], ref["k_zero"][:, sl][:, :, groups])
+    eq("v_scale", got["v_scale"][:, sl][:, :, rows], ref["v_scale"][:, sl][:, :, rows])
+    eq("v_zero", got["v_zero"][:, sl][:, :, rows], ref["v_zero"][:, sl][:, :, rows])
     eq("v_codes", got["v_codes"][:, sl][:, :, vm["v_bytes"]], ref["v_codes"][:, sl][:, :, vm["v_bytes"]])
     eq("k_sink", got["k_sink"][:, sl, :ns], ref["k_sink"][:, sl, :ns])
     eq("v_sink", got["v_sink"][:, sl, :ns], ref["v_sink"][:, sl, :ns])

@@ -34,9 +34,9 @@ def _run_prefill(kvq, cfg, data, T):
     return cache
 
 
-def _cfg_kw(B, H, D, bits, G, S, R, cap, dtype):
+def _cfg_kw(B, H, D, bits, G, S, R, cap, dtype, window=0):
     return dict(batch=B, n_kv_heads=H, head_dim=D, bits=bits, group=G, sink=S, residual=R,
-                capacity=cap, dtype=dtype)
+                capacity=cap, dtype=dtype, window=window)
 
 
 # ----------------------------------------------------------------- small cases
@@ -343,6 +343,45 @@ def test_streaming_appends_match_oracle_every_step(case):
     compare_state(geo, read_state(fresh), st, Tmax)
 
 
+WINDOW = [
+    # B, Hq, Hkv, D, bits, G, S, R, W, T0, steps, dtype
+    (1, 16, 4, 128, 2, 32, 4, 32, 256, 900, 200, "bf16"),   # dual-group GQA 4, ring wraps
+    (1, 8, 1, 128, 4, 64, 4, 128, 320, 1200, 150, "bf16"),  # GQA 8, G 64
+    (2, 4, 4, 64, 4, 32, 0, 32, 100, 500, 130, "f16"),      # VALU, no sinks (plain window)
+    (1, 8, 2, 64, 8, 32, 2, 32, 128, 400, 100, "f32"),      # VALU 8-bit, GQA 4
+    (1, 8, 1, 64, 2, 32, 3, 0, 64, 300, 150, "f16"),        # R 0, small window, half chunks
+    (1, 4, 2, 128, 2, 64, 4, 64, 192, 700, 140, "bf16"),    # VALU 2-bit (64-token blocks), G 64
+]
+
+
+@pytest.mark.parametrize("case", WINDOW, ids=lambda c: "-".join(map(str, c)))
+def test_sliding_window_prefill_and_streaming(case):
+    """[KIVI-PR] the quantized store in a bounded sliding-window cache: the
+    live ring rows bit-exact against the oracle after a prefill and after
+    every append (groups evicted as they freeze), attention over the sinks
+    and the last W tokens within 2e-3 after every step."""
+    kvq = _kvq()
+    B, Hq, Hkv, D, bits, G, S, R, W, T0, steps, dt = case
+    log("window", case)
+    Tmax = T0 + steps
+    data = synth.random_case(31 + sum(case[:11]), B, Hq, Hkv, D, Tmax, dt)
+    cfg, geo = make(_cfg_kw(B, Hkv, D, bits, G, S, R, Tmax, dt, window=W))
+    assert cfg.qcap == geo.qcap < Tmax - S
+    cache = _run_prefill(kvq, cfg, data, T0)
+    st = O.prefill(geo, data["K"], data["V"], T0)
+    compare_state(geo, read_state(cache), st, T0)
+    Kd, Vd, qd = to_dev(data["K"], dt), to_dev(data["V"], dt), to_dev(data["q"], dt)
+    out = kvq.kvq_decode_attention(cfg, cache, T0, qd).cpu().numpy()
+    assert O.row_rel_error(out, O.decode(geo, st, T0, data["q"], Hq)) <= ATOL_ROW_REL
+    for n in range(T0, Tmax):
+        kvq.kvq_append_token(cfg, cache, n, Kd[:, :, n], Vd[:, :, n])
+        st = O.append(geo, st, n, data["K"][:, :, n], data["V"][:, :, n])
+        compare_state(geo, read_state(cache), st, n + 1)
+        out = kvq.kvq_decode_attention(cfg, cache, n + 1, qd).cpu().numpy()
+        err = O.row_rel_error(out, O.decode(geo, st, n + 1, data["q"], Hq))
+        assert err <= ATOL_ROW_REL, (n + 1, err)
+
+
 @pytest.mark.parametrize("Hq", [8, 4])
 def test_split_count_invariance(Hq):
     """The log-sum-exp merge makes the result independent of the split count
@@ -401,7 +440,7 @@ def test_workspace_needs_no_initialization(fill):
 def _workload(name):
     w = synth.WORKLOADS[name]
     cfg_kw = _cfg_kw(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink, w.residual,
-                     w.capacity, w.dtype)
+                     w.capacity, w.dtype, w.window)
     return w, cfg_kw
 
 
@@ -424,7 +463,7 @@ def test_workload_prefill_bit_exact_and_attention(name):
     assert err <= ATOL_ROW_REL
 
 
-@pytest.mark.parametrize("name", ["gpt2", "llama70b"])
+@pytest.mark.parametrize("name", ["gpt2", "llama70b", "mistral_swa"])
 def test_workload_streaming(name):
     """The streaming workloads: append + attention per step, the state
     checked against the oracle's append path at the steps around both group

@@ -64,7 +64,7 @@ from __future__ import annotations
 import math
 import numpy as np
 
-SUPPORTED_BITS = (2, 4, 8)
+SUPPORTED_BITS = (1, 2, 3, 4, 5, 6, 7, 8)   # [KIVI-PR] commit messages: bits configurable
 _F32 = np.float32
 
 
@@ -159,36 +159,70 @@ def quantize_values_per_token(V: np.ndarray, bits: int):
 # ----------------------------------------------------------------------------
 # step 4: packed byte layouts (the library header states them in prose)
 # ----------------------------------------------------------------------------
-def pack_key_rows(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Key codes are token-major: row u holds D codes in D*b/8 bytes, channel
-    d at bit offset d*b of the row, low bits first."""
-    *lead, n, D = codes.shape
-    per = 8 // bits
-    c = codes.astype(np.uint8).reshape(*lead, n, D // per, per)
-    out = np.zeros((*lead, n, D // per), dtype=np.uint8)
-    for i in range(per):
-        out |= (c[..., i] << np.uint8(bits * i)).astype(np.uint8)
+def pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack the last axis of `codes` (m codes, m * bits a multiple of 8) into
+    m * bits / 8 bytes: code i at bit offset i * bits, low bits first.  At
+    3, 5, 6 and 7 bits a code may straddle two bytes (its low bits end one
+    byte, its high bits start the next)."""
+    *lead, m = codes.shape
+    assert (m * bits) % 8 == 0
+    if 8 % bits == 0:                       # whole codes per byte
+        per = 8 // bits
+        c = codes.astype(np.uint8).reshape(*lead, m // per, per)
+        out = np.zeros((*lead, m // per), dtype=np.uint8)
+        for i in range(per):
+            out |= (c[..., i] << np.uint8(bits * i)).astype(np.uint8)
+        return out
+    c = codes.astype(np.uint16)
+    out = np.zeros((*lead, m * bits // 8), dtype=np.uint16)
+    for i in range(m):
+        byte, sh = divmod(i * bits, 8)
+        v = c[..., i] << np.uint16(sh)
+        out[..., byte] |= v & np.uint16(0xFF)
+        if sh + bits > 8:
+            out[..., byte + 1] |= v >> np.uint16(8)
+    return out.astype(np.uint8)
+
+
+def unpack_bits(packed: np.ndarray, bits: int, m: int) -> np.ndarray:
+    """Inverse of pack_bits: [..., m * bits / 8] bytes -> [..., m] codes."""
+    *lead, nb = packed.shape
+    mask = 2 ** bits - 1
+    if 8 % bits == 0:
+        per = 8 // bits
+        out = np.zeros((*lead, nb, per), dtype=np.uint8)
+        for i in range(per):
+            out[..., i] = (packed >> np.uint8(bits * i)) & np.uint8(mask)
+        return out.reshape(*lead, m)
+    p = packed.astype(np.uint16)
+    out = np.zeros((*lead, m), dtype=np.uint8)
+    for i in range(m):
+        byte, sh = divmod(i * bits, 8)
+        v = p[..., byte] >> np.uint16(sh)
+        if sh + bits > 8:
+            v = v | (p[..., byte + 1] << np.uint16(8 - sh))
+        out[..., i] = (v & np.uint16(mask)).astype(np.uint8)
     return out
 
 
+def pack_key_rows(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Key codes are token-major: row u holds D codes in D*b/8 bytes, channel
+    d at bit offset d*b of the row, low bits first."""
+    return pack_bits(codes, bits)
+
+
 def unpack_key_rows(packed: np.ndarray, bits: int, D: int) -> np.ndarray:
-    per = 8 // bits
-    mask = np.uint8(2 ** bits - 1)
-    *lead, n, nb = packed.shape
-    out = np.zeros((*lead, n, nb, per), dtype=np.uint8)
-    for i in range(per):
-        out[..., i] = (packed >> np.uint8(bits * i)) & mask
-    return out.reshape(*lead, n, D)
+    return unpack_bits(packed, bits, D)
 
 
 def value_block_tokens(bits: int) -> int:
-    """Tokens per value-code block: 64 at 2 bits, 32 at 4 and 8 bits."""
+    """Tokens per value-code block: 64 at 2 bits, 32 at every other width."""
     return 64 if bits == 2 else 32
 
 
 def value_unit_codes(bits: int) -> int:
-    """Codes of one channel held in one unit: 16 at 2 bits (32-bit unit),
-    8 at 4 bits (32-bit unit), 8 at 8 bits (64-bit unit)."""
+    """Codes of one channel held in one unit: 16 at 2 bits (a 32-bit unit),
+    8 at every other width (a unit of b bytes: 32 bits at 4, 64 at 8)."""
     return 16 if bits == 2 else 8
 
 
@@ -233,7 +267,10 @@ def pack_value_codes_loop(codes: np.ndarray, bits: int) -> np.ndarray:
     for u in range(n):
         for d in range(D):
             byte, sh = value_code_location(u, d, bits, D)
-            out[byte] |= np.uint8(int(codes[u, d]) << sh)
+            v = int(codes[u, d]) << sh
+            out[byte] |= np.uint8(v & 0xFF)
+            if sh + bits > 8:                 # a code straddling two bytes
+                out[byte + 1] |= np.uint8(v >> 8)
     return out
 
 
@@ -258,12 +295,8 @@ def pack_value_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     c = np.transpose(c, axes)  # [..., blk, g, j, n, h, s, r] -> slot i = r + 4s + (U/2)h
     U = value_unit_codes(bits)
     c = c.reshape(*lead, nblk * 4 * D, U)
-    per = 8 // bits
-    c = c.reshape(*lead, nblk * 4 * D, U // per, per)
-    out = np.zeros((*lead, nblk * 4 * D, U // per), dtype=np.uint8)
-    for i in range(per):
-        out |= (c[..., i] << np.uint8(bits * i)).astype(np.uint8)
-    return out.reshape(*lead, nblk * 4 * D * U // per)
+    out = pack_bits(c, bits)                # units of U * b / 8 bytes
+    return out.reshape(*lead, nblk * 4 * D * U * bits // 8)
 
 
 def unpack_value_codes(packed: np.ndarray, bits: int, D: int, n: int) -> np.ndarray:
@@ -271,13 +304,9 @@ def unpack_value_codes(packed: np.ndarray, bits: int, D: int, n: int) -> np.ndar
     *lead, nbytes = packed.shape
     L = value_block_tokens(bits)
     U = value_unit_codes(bits)
-    per = 8 // bits
     nblk = nbytes // (L * D * bits // 8)
-    p = packed.reshape(*lead, nblk * 4 * D, U // per)
-    c = np.zeros((*lead, nblk * 4 * D, U // per, per), dtype=np.uint8)
-    mask = np.uint8(2 ** bits - 1)
-    for i in range(per):
-        c[..., i] = (p >> np.uint8(bits * i)) & mask
+    p = packed.reshape(*lead, nblk * 4 * D, U * bits // 8)
+    c = unpack_bits(p, bits, U)
     S_ = L // 32
     c = c.reshape(*lead, nblk, 4, 16, D // 16, 2, S_, 4)   # [blk, g, j, n, h, s, r]
     nl = len(lead)

@@ -60,8 +60,10 @@
  *  - No entry point throws across the ABI; there is no global mutable
  *    state.
  *
- * Supported: bits in {2, 4, 8}; head_dim in {64, 128}; group in {32, 64,
- * 128}; sink >= 0; residual >= 0; dtype f32, f16 or bf16.
+ * Supported: bits 1 to 8 (2 and 4 are the method's settings; the other
+ * widths use the same affine codes, packed as a bit stream); head_dim in
+ * {64, 128}; group in {32, 64, 128}; sink >= 0; residual >= 0; dtype f32,
+ * f16 or bf16.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -89,7 +91,7 @@ typedef struct {
   int32_t batch;      /* B                                              */
   int32_t n_kv_heads; /* Hkv                                            */
   int32_t head_dim;   /* D: 64 or 128                                   */
-  int32_t bits;       /* b: 2, 4 or 8                                   */
+  int32_t bits;       /* b: code width, 1 .. 8                          */
   int32_t group;      /* G: key group length in tokens, 32/64/128       */
   int32_t sink;       /* S: first tokens kept exact                     */
   int32_t residual;   /* R: most recent tokens kept exact               */
@@ -112,13 +114,14 @@ typedef struct {
  *          group k (tokens S+kG .. S+kG+G-1) in slot (kG mod qcap)/G, per
  *          channel.  Frozen once written.
  * v_codes  u8 [B][Hkv][vbytes]: value codes in blocks of L storage rows
- *          (L = 64 at 2 bits, 32 at 4 and 8 bits), vbytes = qcap/L * L*D*b/8.  A
+ *          (L = 64 at 2 bits, 32 at every other width), vbytes =
+ *          qcap/L * L*D*b/8.  A
  *          token offset o inside its block is split as
  *          o = 32*s + 16*h + 4*g + r (s < L/32, h < 2, g < 4, r < 4).  A
  *          block holds 4*D units; unit (g*16 + d%16)*(D/16) + d/16 holds
  *          the U codes of channel d for the tokens sharing g (U = 16 at 2
- *          bits in 4 bytes, U = 8 at 4 bits in 4 bytes, U = 8 at 8 bits in
- *          8 bytes); token (s, h, r) is code slot i = r + 4*s + (U/2)*h at
+ *          bits in 4 bytes, U = 8 in b bytes at every other width b);
+ *          token (s, h, r) is code slot i = r + 4*s + (U/2)*h at
  *          bit offset i*b of the unit, low bits first.  This places, for
  *          each 32-token step, the 8 tokens one wave lane needs for one
  *          channel in one contiguous run.

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["kvq_quant.hip", "kvq_attn.hip", "kvq_mfma.hip", "kvq_api.hip"]
+SOURCES = ["kvq_quant.hip", "kvq_quant_any.hip", "kvq_attn.hip", "kvq_attn_any.hip",
+           "kvq_mfma.hip", "kvq_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

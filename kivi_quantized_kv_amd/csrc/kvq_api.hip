@@ -44,7 +44,7 @@ kvq_status check_config(const kvq_config* c) {
   if (c->batch < 1 || c->n_kv_heads < 1 || c->sink < 0 || c->residual < 0 || c->capacity < 1)
     return KVQ_EINVAL;
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_EUNSUPPORTED;
-  if (c->bits != 2 && c->bits != 4 && c->bits != 8) return KVQ_EUNSUPPORTED;
+  if (c->bits < 1 || c->bits > 8) return KVQ_EUNSUPPORTED;
   if (c->group != 32 && c->group != 64 && c->group != 128) return KVQ_EUNSUPPORTED;
   if (c->dtype != KVQ_F32 && c->dtype != KVQ_F16 && c->dtype != KVQ_BF16) return KVQ_EUNSUPPORTED;
   if (c->capacity > (int64_t(1) << 40)) return KVQ_EINVAL;
@@ -83,8 +83,13 @@ template <template <int, int, int> class Fn, typename... Args>
 auto dispatch3(const kvq_config* c, Args&&... args) -> decltype(Fn<DT_F32, 64, 2>::run(args...)) {
 #define KVQ_CASE_B(DT, D)                                                \
   switch (c->bits) {                                                     \
+    case 1: return Fn<DT, D, 1>::run(args...);                           \
     case 2: return Fn<DT, D, 2>::run(args...);                           \
+    case 3: return Fn<DT, D, 3>::run(args...);                           \
     case 4: return Fn<DT, D, 4>::run(args...);                           \
+    case 5: return Fn<DT, D, 5>::run(args...);                           \
+    case 6: return Fn<DT, D, 6>::run(args...);                           \
+    case 7: return Fn<DT, D, 7>::run(args...);                           \
     default: return Fn<DT, D, 8>::run(args...);                          \
   }
 #define KVQ_CASE_D(DT)                                                   \
@@ -120,13 +125,13 @@ template <int DT, int D, int BITS> struct AppendFn {
 };
 template <int DT, int D, int BITS> struct AttnMfma4Fn {
   static hipError_t run(const AttnArgs& a, int B, hipStream_t s) {
-    if constexpr (BITS == 8) return hipErrorInvalidValue;
+    if constexpr (BITS != 2 && BITS != 4) return hipErrorInvalidValue;
     else return launch_attn_mfma<DT, D, BITS, 4>(a, B, s);
   }
 };
 template <int DT, int D, int BITS> struct AttnMfma8Fn {
   static hipError_t run(const AttnArgs& a, int B, hipStream_t s) {
-    if constexpr (BITS == 8) return hipErrorInvalidValue;
+    if constexpr (BITS != 2 && BITS != 4) return hipErrorInvalidValue;
     else return launch_attn_mfma<DT, D, BITS, 8>(a, B, s);
   }
 };
@@ -283,7 +288,7 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
   // per query head on value-code blocks, again with the full-precision
   // tokens spread evenly over the splits.
   const int gqa = n_q_heads / H;
-  const bool mfma = (gqa == 4 || gqa == 8) && cfg->bits != 8 && Q > 0;
+  const bool mfma = (gqa == 4 || gqa == 8) && (cfg->bits == 2 || cfg->bits == 4) && Q > 0;
   const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
   const int64_t qcap = kvq_qcap(cfg);
   // sliding window: quantized tokens before u_lo are not attended; the

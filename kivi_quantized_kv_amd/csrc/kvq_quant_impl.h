@@ -1,0 +1,542 @@
+// Quantize-and-pack kernels: prefill of keys (per channel over G-token
+// groups) and values (per token), and the streaming append with its group
+// freeze.  Method: pigeon guide "KV-cache quantization", How it works steps
+// 1-4; tract PR "quantized KV-cache storage op (int8/int4)" (frozen
+// fixed-size key blocks, values per token, sinks kept exact).
+//
+// Both halves work from registers: every thread loads 16-byte pieces of its
+// rows up front, the min / max reductions run across lanes (DPP and the
+// permlane swaps) with one small LDS step across waves, and codes go
+// straight from registers to the packed rows.  The affine code of an
+// element is rint(fl(fl(x - zp) / delta)) with a correctly rounded division;
+// it is computed as rint(y), y = fl(fl(x - zp) * r) with r the hardware
+// reciprocal of delta (within 2 ulp), which equals it unless y lies within
+// |y| 2^-21 of a half integer (r, the product and the division's own
+// rounding move the quotient by less than |y| 1.5 2^-22).  Since 0 <= y <=
+// (2^b - 1)(1 + 2^-21), one band (2^b) 2^-21 wide around the half integers
+// covers every element; waves holding an element in it, or a delta below
+// 2^-125 (kept off the reciprocal), take the exact division instead.  The prefill and the freeze run the same group and step
+// routines; only the row source differs (input tensor or residual ring).
+#pragma once
+
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+// ----------------------------------------------------------------------------
+// Row sources: the byte address of row r of the group / step being quantized.
+// ----------------------------------------------------------------------------
+struct InputRows {            // rows of the caller's [.., T, D] tensor
+  const uint8_t* base;        // row 0
+  int64_t stride;             // bytes between rows
+  __device__ const uint8_t* row(int r) const { return base + r * stride; }
+};
+struct RingRows {             // tokens first .. first + n of the residual ring
+  const uint8_t* ring;        // slot 0 of this (batch, head)
+  const uint8_t* fresh;       // the token being appended (read from its input)
+  int64_t slot0, ring_len;    // ring slot of row 0; slots in the ring
+  int fresh_row;              // row index of the appended token, or -1
+  int row_bytes;
+  __device__ const uint8_t* row(int r) const {
+    if (r == fresh_row) return fresh;
+    int64_t s = slot0 + r;
+    if (s >= ring_len) s -= ring_len;
+    return ring + s * row_bytes;
+  }
+};
+
+// 16 bytes of a row widened exactly to fp32 (4 or 8 elements).
+template <int DT>
+__device__ __forceinline__ void widen16(uint4 v, float* out) {
+  if constexpr (DT == DT_F32) {
+    out[0] = __builtin_bit_cast(float, v.x); out[1] = __builtin_bit_cast(float, v.y);
+    out[2] = __builtin_bit_cast(float, v.z); out[3] = __builtin_bit_cast(float, v.w);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[2 * k] = DT == DT_F16 ? f16_bits_to_f32(w[k] & 0xFFFFu) : bf16_bits_to_f32(w[k] & 0xFFFFu);
+      out[2 * k + 1] = DT == DT_F16 ? f16_bits_to_f32(w[k] >> 16) : bf16_bits_to_f32(w[k] >> 16);
+    }
+  }
+}
+
+// Reciprocal used by affine_codes: 1 / delta within 2 ulp (v_rcp_f32), 0
+// for delta == 0 (every code 0).  `exact` is set for a delta in (0, 2^-125).
+__device__ __forceinline__ float code_rcp(float delta, bool& exact) {
+  exact |= delta != 0.0f && !(delta >= 0x1p-125f);
+  return delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
+}
+
+// Codes of n elements x[i] against per-element (delta, zero, 1/delta):
+// guarded reciprocal first, the exact division for the whole wave when any
+// lane holds an element near a rounding boundary or flagged `exact`.
+template <int N, int BITS>
+__device__ __forceinline__ void affine_codes(const float* x, const float* delta, const float* zp,
+                                             const float* rcp, bool exact, uint32_t* code) {
+  constexpr float levels = float((1 << BITS) - 1);
+  constexpr float kBand = 0.5f - float(1 << BITS) * 0x1p-21f;
+  bool risky = exact;
+  float c[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float a = x[i] - zp[i];
+    const float y = a * rcp[i];
+    const float r = __builtin_rintf(y);   // 0 <= y < levels + 1/2: no clamp needed
+    risky |= __builtin_fabsf(y - r) >= kBand;
+    c[i] = r;
+  }
+  if (__builtin_amdgcn_ballot_w64(risky) != 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) code[i] = affine_code(x[i], delta[i], zp[i], levels);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) code[i] = uint32_t(c[i]);
+  }
+}
+
+// All-reduce of min and max over the lanes l, l ^ S, l ^ 2S, ... (S = step,
+// a power of two; lanes sharing l mod S).
+template <int S>
+__device__ __forceinline__ void minmax_across(float& mn, float& mx) {
+  if constexpr (S <= 8) {
+    mn = __builtin_fminf(mn, dpp_mov<kRowRor8>(mn));
+    mx = __builtin_fmaxf(mx, dpp_mov<kRowRor8>(mx));
+  }
+  if constexpr (S <= 16) {
+    float a, b;
+    partner_pair<false>(mn, a, b); mn = __builtin_fminf(a, b);
+    partner_pair<false>(mx, a, b); mx = __builtin_fmaxf(a, b);
+  }
+  float a, b;
+  partner_pair<true>(mn, a, b); mn = __builtin_fminf(a, b);
+  partner_pair<true>(mx, a, b); mx = __builtin_fmaxf(a, b);
+}
+
+// All-reduce of min and max over aligned runs of N consecutive lanes (N =
+// 8, 16 or 32).
+template <int N>
+__device__ __forceinline__ void minmax_run(float& mn, float& mx) {
+  mn = __builtin_fminf(mn, dpp_mov<kQuadXor1>(mn));
+  mx = __builtin_fmaxf(mx, dpp_mov<kQuadXor1>(mx));
+  mn = __builtin_fminf(mn, dpp_mov<kQuadXor2>(mn));
+  mx = __builtin_fmaxf(mx, dpp_mov<kQuadXor2>(mx));
+  constexpr int kHalfMirror = 0x141, kMirror = 0x140;
+  mn = __builtin_fminf(mn, dpp_mov<kHalfMirror>(mn));   // quads of a half row meet
+  mx = __builtin_fmaxf(mx, dpp_mov<kHalfMirror>(mx));
+  if constexpr (N >= 16) {
+    mn = __builtin_fminf(mn, dpp_mov<kMirror>(mn));     // halves of a row meet
+    mx = __builtin_fmaxf(mx, dpp_mov<kMirror>(mx));
+  }
+  if constexpr (N >= 32) {
+    float a, b;
+    partner_pair<false>(mn, a, b); mn = __builtin_fminf(a, b);
+    partner_pair<false>(mx, a, b); mx = __builtin_fmaxf(a, b);
+  }
+}
+
+// Store the n = 8 b bits of eight b-bit codes at p (aligned to b bytes):
+// one store at 1, 2, 4 and 8 bits, byte stores at the widths whose codes
+// straddle bytes.
+template <int BITS>
+__device__ __forceinline__ void store_codes8(uint8_t* p, uint64_t v) {
+  if constexpr (BITS == 1) *p = uint8_t(v);
+  else if constexpr (BITS == 2) *reinterpret_cast<uint16_t*>(p) = uint16_t(v);
+  else if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(p) = uint32_t(v);
+  else if constexpr (BITS == 8) *reinterpret_cast<uint2*>(p) = make_uint2(uint32_t(v), uint32_t(v >> 32));
+  else {
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) p[k] = uint8_t(v >> (8 * k));
+  }
+}
+
+// Rows are split into pieces of 8 channels (16 bytes of 16-bit inputs, 32
+// bytes of fp32), so that a thread's codes fill whole bytes at any width.
+template <int DT, int D>
+struct RowSplit {
+  static constexpr int kVE = 8;                       // channels per piece
+  static constexpr int kTPR = D / kVE;                // threads per row: 8 or 16
+  static constexpr int kRPP = 256 / kTPR;             // rows per pass of 256 threads
+};
+
+// A piece of a row: its 16-byte loads.
+template <int DT>
+struct Piece {
+  uint4 v[Elem<DT>::bytes / 2];
+};
+template <int DT>
+__device__ __forceinline__ void load_piece(const uint8_t* p, Piece<DT>& pc) {
+#pragma unroll
+  for (int i = 0; i < Elem<DT>::bytes / 2; ++i) pc.v[i] = reinterpret_cast<const uint4*>(p)[i];
+}
+template <int DT>
+__device__ __forceinline__ void widen_piece(const Piece<DT>& pc, float* out) {
+#pragma unroll
+  for (int i = 0; i < Elem<DT>::bytes / 2; ++i) widen16<DT>(pc.v[i], out + i * (16 / Elem<DT>::bytes));
+}
+
+// ----------------------------------------------------------------------------
+// One key group of G rows, 256 threads: per-channel min / max over the rows,
+// delta and zero point, the packed code rows.  Thread t holds piece t % kTPR
+// (channels kVE * (t % kTPR) ..) of rows t / kTPR + kRPP * i.
+// ----------------------------------------------------------------------------
+template <int DT, int D, int G>
+struct KeyRows {
+  static constexpr int kRPT = G / RowSplit<DT, D>::kRPP;   // rows per thread
+  static_assert(kRPT >= 1 && G % RowSplit<DT, D>::kRPP == 0, "group rows per thread");
+  Piece<DT> raw[kRPT];
+};
+
+// This thread's pieces of a key group's rows.
+template <int DT, int D, int G, class Rows>
+__device__ __forceinline__ void load_key_rows(const Rows& rows, KeyRows<DT, D, G>& kr) {
+  using RS = RowSplit<DT, D>;
+  const int t = threadIdx.x, cs = t % RS::kTPR, r0 = t / RS::kTPR;
+#pragma unroll
+  for (int i = 0; i < KeyRows<DT, D, G>::kRPT; ++i)
+    load_piece<DT>(rows.row(r0 + i * RS::kRPP) + cs * RS::kVE * Elem<DT>::bytes, kr.raw[i]);
+}
+
+template <int DT, int D, int BITS, int G>
+__device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_scale, float* k_zero,
+                                          uint8_t* code_rows, float (*s_red)[D], float (*s_par)[D]) {
+  using RS = RowSplit<DT, D>;
+  constexpr int kVE = RS::kVE, kTPR = RS::kTPR, kRPP = RS::kRPP;
+  constexpr int kRPT = KeyRows<DT, D, G>::kRPT;
+  constexpr float kLevels = float((1 << BITS) - 1);
+  const int t = threadIdx.x, cs = t % kTPR, r0 = t / kTPR;
+  const int lane = t & 63, wave = t >> 6;
+  const Piece<DT>* raw = kr.raw;
+  float x[kRPT][kVE];
+#pragma unroll
+  for (int i = 0; i < kRPT; ++i) widen_piece<DT>(raw[i], x[i]);
+  float mn[kVE], mx[kVE];
+#pragma unroll
+  for (int e = 0; e < kVE; ++e) {
+    mn[e] = x[0][e];
+    mx[e] = x[0][e];
+#pragma unroll
+    for (int i = 1; i < kRPT; ++i) {
+      mn[e] = __builtin_fminf(mn[e], x[i][e]);
+      mx[e] = __builtin_fmaxf(mx[e], x[i][e]);
+    }
+    minmax_across<kTPR>(mn[e], mx[e]);
+  }
+  // the waves meet in LDS: rows 0..3 of s_red hold minima, 4..7 maxima
+  if (lane < kTPR) {
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) {
+      s_red[wave][cs * kVE + e] = mn[e];
+      s_red[4 + wave][cs * kVE + e] = mx[e];
+    }
+  }
+  __syncthreads();
+  // one thread per channel: delta, zero point and reciprocal, written out
+  // and shared through LDS (row 3 of s_par flags a delta that needs the
+  // exact division)
+  if (t < D) {
+    const float lo = __builtin_fminf(__builtin_fminf(s_red[0][t], s_red[1][t]), __builtin_fminf(s_red[2][t], s_red[3][t]));
+    const float hi = __builtin_fmaxf(__builtin_fmaxf(s_red[4][t], s_red[5][t]), __builtin_fmaxf(s_red[6][t], s_red[7][t]));
+    float dl, z;
+    bool ex = false;
+    affine_params(lo, hi, kLevels, dl, z);
+    const float rc = code_rcp(dl, ex);
+    s_par[0][t] = dl;
+    s_par[1][t] = z;
+    s_par[2][t] = rc;
+    s_par[3][t] = ex ? 1.0f : 0.0f;
+    k_scale[t] = dl;
+    k_zero[t] = z;
+  }
+  __syncthreads();
+  float delta[kVE], zp[kVE], rcp[kVE];
+  bool exact = false;
+#pragma unroll
+  for (int e = 0; e < kVE; e += 4) {
+    const int c = cs * kVE + e;
+    const float4 d4 = *reinterpret_cast<const float4*>(&s_par[0][c]);
+    const float4 z4 = *reinterpret_cast<const float4*>(&s_par[1][c]);
+    const float4 r4 = *reinterpret_cast<const float4*>(&s_par[2][c]);
+    const float4 x4 = *reinterpret_cast<const float4*>(&s_par[3][c]);
+    delta[e] = d4.x; delta[e + 1] = d4.y; delta[e + 2] = d4.z; delta[e + 3] = d4.w;
+    zp[e] = z4.x; zp[e + 1] = z4.y; zp[e + 2] = z4.z; zp[e + 3] = z4.w;
+    rcp[e] = r4.x; rcp[e + 1] = r4.y; rcp[e + 2] = r4.z; rcp[e + 3] = r4.w;
+    exact |= (x4.x + x4.y + x4.z + x4.w) != 0.0f;
+  }
+  constexpr int kRB = D * BITS / 8;
+#pragma unroll
+  for (int i = 0; i < kRPT; ++i) {
+    uint32_t code[kVE];
+    affine_codes<kVE, BITS>(x[i], delta, zp, rcp, exact, code);
+    uint64_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) packed |= uint64_t(code[e]) << (BITS * e);
+    store_codes8<BITS>(code_rows + (r0 + i * kRPP) * kRB + cs * BITS, packed);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// One 32-token step of values (storage rows u0 .. u0 + 31, u0 a multiple
+// of 32), 256 threads: per-token min / max across the lanes of the token,
+// delta and zero point, codes through LDS (channel-major) into the value-code
+// units of the layout in kvq.h.  At 2 bits a block holds two steps; a step
+// writes its own bytes of each unit (bytes s and s + 2).
+// ----------------------------------------------------------------------------
+constexpr int kStepPitch = 36;   // bytes per channel row of the LDS code tile
+
+template <int DT, int D>
+struct StepRows {
+  static constexpr int kTPT = 32 / RowSplit<DT, D>::kRPP;   // tokens per thread
+  static_assert(kTPT >= 1 && 32 % RowSplit<DT, D>::kRPP == 0, "tokens per pass");
+  Piece<DT> raw[kTPT];
+};
+
+// This thread's pieces of the 32 value rows of a step.
+template <int DT, int D, class Rows>
+__device__ __forceinline__ void load_step_rows(const Rows& rows, StepRows<DT, D>& sr) {
+  using RS = RowSplit<DT, D>;
+  const int t = threadIdx.x, cs = t % RS::kTPR, r0 = t / RS::kTPR;
+#pragma unroll
+  for (int j = 0; j < StepRows<DT, D>::kTPT; ++j)
+    load_piece<DT>(rows.row(r0 + j * RS::kRPP) + cs * RS::kVE * Elem<DT>::bytes, sr.raw[j]);
+}
+
+template <int DT, int D, int BITS>
+__device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0, float* v_scale,
+                                           float* v_zero, uint8_t* v_codes_head, uint8_t* s_codes) {
+  using RS = RowSplit<DT, D>;
+  using VL = VLayout<BITS>;
+  constexpr int kVE = RS::kVE, kTPR = RS::kTPR, kRPP = RS::kRPP;
+  constexpr int kTPT = StepRows<DT, D>::kTPT;
+  constexpr float kLevels = float((1 << BITS) - 1);
+  const int t = threadIdx.x, cs = t % kTPR, r0 = t / kTPR;
+  const Piece<DT>* raw = sr.raw;
+#pragma unroll
+  for (int j = 0; j < kTPT; ++j) {
+    const int tok = r0 + j * kRPP;
+    float x[kVE];
+    widen_piece<DT>(raw[j], x);
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < kVE; ++e) {
+      mn = __builtin_fminf(mn, x[e]);
+      mx = __builtin_fmaxf(mx, x[e]);
+    }
+    minmax_run<kTPR>(mn, mx);
+    float delta[kVE], zp[kVE], rcp[kVE];
+    bool exact = false;
+    affine_params(mn, mx, kLevels, delta[0], zp[0]);
+    rcp[0] = code_rcp(delta[0], exact);
+#pragma unroll
+    for (int e = 1; e < kVE; ++e) {
+      delta[e] = delta[0];
+      zp[e] = zp[0];
+      rcp[e] = rcp[0];
+    }
+    if (cs == 0) {
+      v_scale[u0 + tok] = delta[0];
+      v_zero[u0 + tok] = zp[0];
+    }
+    uint32_t code[kVE];
+    affine_codes<kVE, BITS>(x, delta, zp, rcp, exact, code);
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) s_codes[(cs * kVE + e) * kStepPitch + tok] = uint8_t(code[e]);
+  }
+  __syncthreads();
+  // units of this step: unit x of the block holds channel d = 16 n + jj for
+  // lane group g; its tokens (h, r) of this step are offsets 16 h + 4 g + r
+  constexpr int kUnits = 4 * D;
+  const int64_t blk = u0 / VL::L;
+  const int s = int((u0 % VL::L) / 32);
+  for (int x = t; x < kUnits; x += 256) {
+    const int g = x / D, rem = x % D, jj = rem / (D / 16), n = rem % (D / 16);
+    const int d = 16 * n + jj;
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_codes + d * kStepPitch + 4 * g);
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_codes + d * kStepPitch + 16 + 4 * g);
+    uint8_t* dst = v_codes_head + (blk * kUnits + x) * VL::UB;
+    if constexpr (BITS == 8) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);         // slots r (h 0), 4 + r (h 1)
+    } else if constexpr (BITS == 4) {
+      const uint32_t a = w0 | (w0 >> 4), b = w1 | (w1 >> 4);        // nibble pairs in bytes 0, 2
+      *reinterpret_cast<uint32_t*>(dst) = (a & 0xFFu) | ((a >> 8) & 0xFF00u) | ((b & 0xFFu) << 16) |
+                                          ((b << 8) & 0xFF000000u);
+    } else if constexpr (BITS == 2) {
+      // slot r + 4 s + 8 h sits in byte s + 2 h
+      uint32_t a = w0 | (w0 >> 6), b = w1 | (w1 >> 6);
+      a = (a | (a >> 12)) & 0xFFu;
+      b = (b | (b >> 12)) & 0xFFu;
+      dst[s] = uint8_t(a);
+      dst[s + 2] = uint8_t(b);
+    } else {
+      // any other width: slots r (h 0) and 4 + r (h 1) of an 8-code unit of
+      // BITS bytes, slot i at bit i * BITS
+      uint64_t v = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v |= uint64_t((w0 >> (8 * r)) & 0xFFu) << (BITS * r);
+        v |= uint64_t((w1 >> (8 * r)) & 0xFFu) << (BITS * (4 + r));
+      }
+      store_codes8<BITS>(dst, v);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Prefill kernels
+// ----------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(64) void k_copy_fp_rows(FpCopyArgs a) {
+  // grid: x = fp row (sinks first, then residual tokens), y = head, z = batch
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t row = blockIdx.x;
+  const int64_t tok = row < a.n_sink ? row : a.first_resid + (row - a.n_sink);
+  constexpr int EB = Elem<DT>::bytes;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.src) +
+                       (b * a.sb + h * a.sh + tok * a.st) * EB;
+  uint8_t* dst;
+  if (tok < a.S) {
+    dst = reinterpret_cast<uint8_t*>(a.sink) + ((int64_t(b) * a.H + h) * a.S + tok) * D * EB;
+  } else {
+    const int64_t slot = (tok - a.S) % a.ring;
+    dst = reinterpret_cast<uint8_t*>(a.resid) + ((int64_t(b) * a.H + h) * a.ring + slot) * D * EB;
+  }
+  constexpr int kVec = D * EB / 16;  // 16-byte vectors per row
+  for (int v = threadIdx.x; v < kVec; v += 64)
+    reinterpret_cast<uint4*>(dst)[v] = reinterpret_cast<const uint4*>(src)[v];
+}
+
+// grid: x = unit (key group, or 32-token value step) of the quantized range
+// from unit a.k0 on, y = head, z = batch; unit k is stored at storage row
+// (k * unit tokens) mod qcap.  One unit per workgroup: many small resident
+// workgroups at different phases overlap loads with arithmetic better than
+// fewer workgroups streaming several units each (measured).
+template <int DT, int D, int BITS, int G>
+__global__ __launch_bounds__(256) void k_quant_keys(QuantArgs a) {
+  __shared__ __attribute__((aligned(16))) float s_red[8][D];
+  __shared__ __attribute__((aligned(16))) float s_par[4][D];
+  const int64_t k = a.k0 + blockIdx.x;
+  const int64_t ks = k % (a.qcap / G);              // storage slot of group k
+  const int h = blockIdx.y, b = blockIdx.z;
+  constexpr int EB = Elem<DT>::bytes;
+  const int64_t bh = int64_t(b) * a.H + h;
+  KeyRows<DT, D, G> kr;
+  load_key_rows<DT, D, G>(
+      InputRows{reinterpret_cast<const uint8_t*>(a.src) + (b * a.sb + h * a.sh + (a.S + k * G) * a.st) * EB,
+                a.st * EB},
+      kr);
+  key_group<DT, D, BITS, G>(kr, a.scale + (bh * (a.qcap / G) + ks) * D, a.zero + (bh * (a.qcap / G) + ks) * D,
+                            a.codes + (bh * a.qcap + ks * G) * (D * BITS / 8), s_red, s_par);
+}
+
+template <int DT, int D, int BITS>
+__global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[D * kStepPitch];
+  const int64_t st = a.k0 + blockIdx.x;
+  const int64_t r0 = (32 * st) % a.qcap;            // storage row of the step's first token
+  const int h = blockIdx.y, b = blockIdx.z;
+  constexpr int EB = Elem<DT>::bytes;
+  const int64_t bh = int64_t(b) * a.H + h;
+  StepRows<DT, D> sr;
+  load_step_rows<DT, D>(
+      InputRows{reinterpret_cast<const uint8_t*>(a.src) + (b * a.sb + h * a.sh + (a.S + 32 * st) * a.st) * EB,
+                a.st * EB},
+      sr);
+  value_step<DT, D, BITS>(sr, r0, a.scale + bh * a.qcap, a.zero + bh * a.qcap,
+                          a.codes + bh * (a.qcap * D * BITS / 8), s_codes);
+}
+
+// ----------------------------------------------------------------------------
+// Streaming append: block 0 writes token t = n_before to its sink or ring
+// slot.  When the full-precision count reaches R + G, block 1 quantizes the
+// oldest G ring tokens as the next key group and blocks 2 .. 1 + G/32 their
+// values, one 32-token step each.  The appended token itself is read from
+// its input (it belongs to the group when R == 0), so the blocks need no
+// ordering among themselves.
+// ----------------------------------------------------------------------------
+template <int DT, int D, int BITS, int G>
+__global__ __launch_bounds__(256) void k_append(AppendArgs a) {
+  // grid: x = role, y = head, z = batch
+  const int role = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = int64_t(b) * a.H + h;
+  constexpr int EB = Elem<DT>::bytes;
+  const int64_t t = a.n_before;
+  const int64_t ring = a.R + G;
+  const uint8_t* kin = reinterpret_cast<const uint8_t*>(a.k_new) + (b * a.k_sb + h * a.k_sh) * EB;
+  const uint8_t* vin = reinterpret_cast<const uint8_t*>(a.v_new) + (b * a.v_sb + h * a.v_sh) * EB;
+  if (role == 0) {
+    uint8_t *kd, *vd;
+    if (t < a.S) {
+      kd = reinterpret_cast<uint8_t*>(a.k_sink) + (bh * a.S + t) * D * EB;
+      vd = reinterpret_cast<uint8_t*>(a.v_sink) + (bh * a.S + t) * D * EB;
+    } else {
+      const int64_t slot = (t - a.S) % ring;
+      kd = reinterpret_cast<uint8_t*>(a.k_resid) + (bh * ring + slot) * D * EB;
+      vd = reinterpret_cast<uint8_t*>(a.v_resid) + (bh * ring + slot) * D * EB;
+    }
+    constexpr int kVec = D * EB / 16;
+    for (int v = threadIdx.x; v < 2 * kVec; v += blockDim.x) {
+      if (v < kVec)
+        reinterpret_cast<uint4*>(kd)[v] = reinterpret_cast<const uint4*>(kin)[v];
+      else
+        reinterpret_cast<uint4*>(vd)[v - kVec] = reinterpret_cast<const uint4*>(vin)[v - kVec];
+    }
+    return;
+  }
+  // freeze of tokens S + q_old .. S + q_old + G - 1
+  const int64_t first = a.S + a.q_old;
+  const int fresh_row = int(t - first);          // in [0, G) when t is in the group
+  if (role == 1) {
+    __shared__ __attribute__((aligned(16))) float s_red[8][D];
+    __shared__ __attribute__((aligned(16))) float s_par[4][D];
+    const RingRows rows{reinterpret_cast<const uint8_t*>(a.k_resid) + bh * ring * D * EB, kin,
+                        (first - a.S) % ring, ring, fresh_row, D * EB};
+    const int64_t kgrp = a.r_old / G;                 // storage slot of the group
+    KeyRows<DT, D, G> kr;
+    load_key_rows<DT, D, G>(rows, kr);
+    key_group<DT, D, BITS, G>(kr, a.k_scale + (bh * (a.qcap / G) + kgrp) * D,
+                              a.k_zero + (bh * (a.qcap / G) + kgrp) * D,
+                              a.k_codes + (bh * a.qcap + a.r_old) * (D * BITS / 8), s_red, s_par);
+  } else {
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[D * kStepPitch];
+    const int step = role - 2;
+    const RingRows rows{reinterpret_cast<const uint8_t*>(a.v_resid) + bh * ring * D * EB, vin,
+                        (first + 32 * step - a.S) % ring, ring, fresh_row - 32 * step, D * EB};
+    StepRows<DT, D> sr;
+    load_step_rows<DT, D>(rows, sr);
+    value_step<DT, D, BITS>(sr, a.r_old + 32 * step, a.v_scale + bh * a.qcap, a.v_zero + bh * a.qcap,
+                            a.v_codes + bh * (a.qcap * D * BITS / 8), s_codes);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------
+template <int DT, int D, int BITS>
+hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_units, int B, int H, hipStream_t s) {
+  const dim3 grid(unsigned(n_units), H, B);
+  if (a.G == 32) hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 32>), grid, dim3(256), 0, s, a);
+  else if (a.G == 64) hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 128>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+template <int DT, int D, int BITS>
+hipError_t launch_quant_values(const QuantArgs& a, int64_t n_units, int B, int H, hipStream_t s) {
+  hipLaunchKernelGGL((k_quant_values<DT, D, BITS>), dim3(unsigned(n_units), H, B), dim3(256), 0,
+                     s, a);
+  return hipGetLastError();
+}
+template <int DT, int D>
+hipError_t launch_copy_fp(const FpCopyArgs& a, int64_t n_rows, int B, int H, hipStream_t s) {
+  hipLaunchKernelGGL((k_copy_fp_rows<DT, D>), dim3(unsigned(n_rows), H, B), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+template <int DT, int D, int BITS>
+hipError_t launch_append(const AppendArgs& a, int B, int H, hipStream_t s) {
+  const dim3 grid(a.flush ? 2 + a.G / 32 : 1, H, B);
+  if (a.G == 32) hipLaunchKernelGGL((k_append<DT, D, BITS, 32>), grid, dim3(256), 0, s, a);
+  else if (a.G == 64) hipLaunchKernelGGL((k_append<DT, D, BITS, 64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_append<DT, D, BITS, 128>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -67,6 +67,11 @@ int main(int argc, char** argv) {
     (1, 8, 128, 4, 64, 4, 128, 131200, "bf16"),
     (2, 3, 128, 4, 128, 0, 0, 1000, "f16"),
     (1, 1, 64, 2, 32, 300, 0, 200, "f32"),
+    (1, 2, 64, 3, 32, 4, 32, 300, "f16"),
+    (2, 1, 128, 5, 64, 2, 64, 1000, "bf16"),
+    (1, 1, 64, 1, 32, 0, 0, 100, "f32"),
+    (1, 4, 128, 7, 128, 4, 128, 5000, "f16"),
+    (1, 1, 64, 6, 32, 4, 32, 300, "bf16"),
 ])
 def test_header_sizes_match_oracle_geometry(B, H, D, bits, G, S, R, cap, dt):
     code = {"f32": 0, "f16": 1, "bf16": 2}[dt]
@@ -97,7 +102,9 @@ def test_validation_rejects_bad_arguments_without_launching():
     good = cfg.c()
     assert qk(None) == 1
     assert qk(good, cc=None) == 1
-    bad = cfg.c(); bad.bits = 3
+    bad = cfg.c(); bad.bits = 0
+    assert qk(bad) == 2
+    bad = cfg.c(); bad.bits = 9
     assert qk(bad) == 2
     bad = cfg.c(); bad.head_dim = 96
     assert qk(bad) == 2

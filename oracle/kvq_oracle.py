@@ -56,6 +56,27 @@ with int8 storage), readings:
      one (eviction).  Tokens before the window inside a live chunk are
      masked, so the window is exact to the token.
 
+Dense-and-sparse outliers ([GUIDE] "KVQuant adds", third bullet: about 1%
+of outlier values kept in a sparse fp16 side table), readings:
+  O1 the unit is the quantization vector: a key group's channel (G values)
+     or a value token (D values).  Each keeps at most one entry exact, so
+     1/G of the keys and 1/D of the values (about 1-2% at G 32..128, D 64
+     or 128).
+  O2 the kept entry is the largest or the smallest, whichever leaves the
+     smaller range: with the two largest max1 >= max2 and the two smallest
+     min1 <= min2, gap_hi = fl32(max1 - max2) and gap_lo = fl32(min2 -
+     min1); the maximum if gap_hi >= gap_lo and gap_hi > 0, else the
+     minimum if gap_lo > 0, else none (the range would not shrink).
+  O3 delta and the zero point come from the other entries; every entry,
+     the kept one too, is coded with them (the kept one clamps to 2^b - 1
+     or 0).
+  O4 the side table holds the kept entry's position (u8: token offset in
+     the group for keys, channel for values; 255 = none) and its value,
+     losslessly in the input dtype (fp16 for fp16 inputs, as the page has
+     it); with none kept the value slot holds +0.
+  O5 reconstruction: the kept entry takes its exact value, every other
+     entry its dense dequantization.
+
 Every function here is pinned by tests/test_oracle_pins.py against worked
 examples, closed forms, brute force and library routines.
 """
@@ -81,6 +102,19 @@ def to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(_F32)
+    raise ValueError(dtype)
+
+
+def from_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Narrow fp32 values that the input dtype represents exactly back to
+    it (bf16 as uint16 bit patterns: the top 16 bits)."""
+    x = np.asarray(x, dtype=_F32)
+    if dtype == "f32":
+        return x.copy()
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     raise ValueError(dtype)
 
 
@@ -132,27 +166,59 @@ def affine_codes(x: np.ndarray, delta: np.ndarray, zp: np.ndarray, bits: int) ->
     return r.astype(np.uint8)
 
 
-def quantize_keys_per_channel(K: np.ndarray, G: int, bits: int):
+def split_outlier(v: np.ndarray):
+    """Dense-and-sparse split of vectors along the last axis (O1, O2).
+    v: [..., m] fp32, m >= 2.  Returns (pos, mn, mx): the position of the
+    entry kept exact ([...] int64, -1 = none) and the minimum and maximum
+    of the remaining (dense) entries."""
+    v = np.asarray(v, dtype=_F32)
+    s = np.sort(v, axis=-1)
+    min1, min2, max2, max1 = s[..., 0], s[..., 1], s[..., -2], s[..., -1]
+    gap_hi = (max1 - max2).astype(_F32)
+    gap_lo = (min2 - min1).astype(_F32)
+    take_hi = (gap_hi >= gap_lo) & (gap_hi > 0)
+    take_lo = ~take_hi & (gap_lo > 0)
+    # the kept extreme is unique (its gap is positive)
+    pos = np.where(take_hi, np.argmax(v, axis=-1), np.where(take_lo, np.argmin(v, axis=-1), -1))
+    mn = np.where(take_lo, min2, min1).astype(_F32)
+    mx = np.where(take_hi, max2, max1).astype(_F32)
+    return pos.astype(np.int64), mn, mx
+
+
+def quantize_keys_per_channel(K: np.ndarray, G: int, bits: int, outliers: bool = False):
     """Keys per channel over G-token groups ([GUIDE] step 1; [STORE-PR] frozen
     fixed-size blocks).  K: [..., n, D] fp32 with n a multiple of G.
-    Returns codes [..., n, D], delta and zp [..., n/G, D]."""
+    Returns codes [..., n, D], delta and zp [..., n/G, D]; with outliers
+    also the kept entry's token offset in its group [..., n/G, D] (-1 =
+    none, O1-O3)."""
     *lead, n, D = K.shape
     assert n % G == 0
     Kg = K.reshape(*lead, n // G, G, D)
-    mn = Kg.min(axis=-2)
-    mx = Kg.max(axis=-2)
+    if outliers:
+        pos, mn, mx = split_outlier(np.swapaxes(Kg, -1, -2))
+    else:
+        mn = Kg.min(axis=-2)
+        mx = Kg.max(axis=-2)
     delta, zp = affine_params(mn, mx, bits)
     codes = affine_codes(Kg, delta[..., None, :], zp[..., None, :], bits)
+    if outliers:
+        return codes.reshape(*lead, n, D), delta, zp, pos
     return codes.reshape(*lead, n, D), delta, zp
 
 
-def quantize_values_per_token(V: np.ndarray, bits: int):
+def quantize_values_per_token(V: np.ndarray, bits: int, outliers: bool = False):
     """Values per token ([GUIDE] step 2; [KIVI-PR] per-token value store).
-    V: [..., n, D] fp32.  Returns codes [..., n, D], delta and zp [..., n]."""
-    mn = V.min(axis=-1)
-    mx = V.max(axis=-1)
+    V: [..., n, D] fp32.  Returns codes [..., n, D], delta and zp [..., n];
+    with outliers also the kept entry's channel [..., n] (-1 = none)."""
+    if outliers:
+        pos, mn, mx = split_outlier(V)
+    else:
+        mn = V.min(axis=-1)
+        mx = V.max(axis=-1)
     delta, zp = affine_params(mn, mx, bits)
     codes = affine_codes(V, delta[..., None], zp[..., None], bits)
+    if outliers:
+        return codes, delta, zp, pos
     return codes, delta, zp
 
 
@@ -331,12 +397,14 @@ class CacheGeometry:
     capacity is cap - S (at most W + G with a window, W2) rounded up to a
     multiple of max(64, G)."""
 
-    def __init__(self, B, Hkv, D, bits, G, S, R, capacity, dtype, window=0):
+    def __init__(self, B, Hkv, D, bits, G, S, R, capacity, dtype, window=0, outliers=0):
         assert bits in SUPPORTED_BITS
         assert window == 0 or window >= R + G
+        assert outliers in (0, 1)
         self.B, self.Hkv, self.D, self.bits = B, Hkv, D, bits
         self.G, self.S, self.R, self.capacity, self.dtype = G, S, R, capacity, dtype
         self.window = window
+        self.outliers = outliers
         step = max(64, G)
         qcap = max(0, capacity - S)
         if window:
@@ -360,6 +428,11 @@ class CacheGeometry:
             "v_sink": np.zeros((B, H, self.S, D), sd),
             "k_resid": np.zeros((B, H, self.ring, D), sd),
             "v_resid": np.zeros((B, H, self.ring, D), sd),
+            # side tables (O4), empty without outliers
+            "k_oidx": np.zeros((B, H, self.qcap // self.G if self.outliers else 0, D), np.uint8),
+            "k_oval": np.zeros((B, H, self.qcap // self.G if self.outliers else 0, D), sd),
+            "v_oidx": np.zeros((B, H, self.qcap if self.outliers else 0), np.uint8),
+            "v_oval": np.zeros((B, H, self.qcap if self.outliers else 0), sd),
         }
 
 
@@ -384,8 +457,21 @@ def _store_groups_at(geo: CacheGeometry, st: dict, r0: int, Kq: np.ndarray, Vq: 
     (n and r0 multiples of G, no wrap)."""
     n = Kq.shape[2]
     b = geo.bits
-    kc, kd, kz = quantize_keys_per_channel(Kq, geo.G, b)
-    vc, vd, vz = quantize_values_per_token(Vq, b)
+    if geo.outliers:
+        kc, kd, kz, kpos = quantize_keys_per_channel(Kq, geo.G, b, outliers=True)
+        vc, vd, vz, vpos = quantize_values_per_token(Vq, b, outliers=True)
+        # side tables (O4): position (255 = none) and the exact value
+        g0, g1 = r0 // geo.G, (r0 + n) // geo.G
+        Kg = Kq.reshape(geo.B, geo.Hkv, n // geo.G, geo.G, geo.D)
+        kval = np.take_along_axis(Kg, np.maximum(kpos, 0)[..., None, :], axis=-2)[..., 0, :]
+        st["k_oidx"][:, :, g0:g1] = np.where(kpos < 0, 255, kpos).astype(np.uint8)
+        st["k_oval"][:, :, g0:g1] = from_f32(np.where(kpos < 0, _F32(0), kval), geo.dtype)
+        vval = np.take_along_axis(Vq, np.maximum(vpos, 0)[..., None], axis=-1)[..., 0]
+        st["v_oidx"][:, :, r0:r0 + n] = np.where(vpos < 0, 255, vpos).astype(np.uint8)
+        st["v_oval"][:, :, r0:r0 + n] = from_f32(np.where(vpos < 0, _F32(0), vval), geo.dtype)
+    else:
+        kc, kd, kz = quantize_keys_per_channel(Kq, geo.G, b)
+        vc, vd, vz = quantize_values_per_token(Vq, b)
     st["k_codes"][:, :, r0:r0 + n] = pack_key_rows(kc, b)
     st["k_scale"][:, :, r0 // geo.G:(r0 + n) // geo.G] = kd
     st["k_zero"][:, :, r0 // geo.G:(r0 + n) // geo.G] = kz
@@ -515,6 +601,16 @@ def dequant_cache(geo: CacheGeometry, st: dict, T: int, heads=None):
             vd = st["v_scale"][:, h][:, rows].astype(np.float64)[..., None]
             vz = st["v_zero"][:, h][:, rows].astype(np.float64)[..., None]
             Vh[:, i, ns:ns + nq] = vc * vd + vz
+            if geo.outliers:
+                # kept entries take their exact values (O5)
+                ki = st["k_oidx"][:, h][:, rows // geo.G]                      # [B, nq, D]
+                kv = to_f32(st["k_oval"][:, h][:, rows // geo.G], geo.dtype)
+                kmask = ki == (rows % geo.G)[None, :, None]
+                Kh[:, i, ns:ns + nq] = np.where(kmask, kv, Kh[:, i, ns:ns + nq])
+                vi = st["v_oidx"][:, h][:, rows]                               # [B, nq]
+                vv = to_f32(st["v_oval"][:, h][:, rows], geo.dtype)
+                vmask = np.arange(D)[None, None, :] == vi[..., None]
+                Vh[:, i, ns:ns + nq] = np.where(vmask, vv[..., None], Vh[:, i, ns:ns + nq])
         for j, t in enumerate(range(geo.S + Q, T)):
             sl = ring_slot(t, geo.S, geo.R, geo.G)
             Kh[:, i, ns + nq + j] = to_f32(st["k_resid"][:, h, sl], geo.dtype)

@@ -549,3 +549,196 @@ def test_window_store_is_bounded():
     # the window's quantized tokens all sit in live rows
     u_lo = O.window_start(geo, T)
     assert all(rows[u % geo.qcap] for u in range(u_lo, Q)) and u_lo >= Q - geo.qcap
+
+
+# --------------------------------------------------------------- dense-and-sparse outliers
+PADS = {"A": 1, "B": 5, "C": 3, "D": 3, "E": 7, "F": 4, "G": 0.5}
+
+
+def _outlier_cache(dtype):
+    """One 8-token key group (G = 8) of 16 channels and 8 value tokens of 16
+    channels built from the fixture's vectors: key channel 0 runs over
+    vector A, channel 1 over vector B, channel c >= 2 is the constant c;
+    value token i is vector i followed by eight copies of an on-grid
+    interior value (which moves neither extreme nor either gap)."""
+    g = gold("e9_outlier_side_table.json")
+    vecs = g["vectors"]
+    bits = 2
+    K = np.zeros((1, 1, 8, 16), np.float32)
+    K[0, 0, :, 0] = vecs[0]["x"]
+    K[0, 0, :, 1] = vecs[1]["x"]
+    for c in range(2, 16):
+        K[0, 0, :, c] = c
+    V = np.zeros((1, 1, 8, 16), np.float32)
+    for i in range(8):
+        v = vecs[i % 6]                       # the 2-bit vectors A..F, then A, B
+        V[0, 0, i, :8] = v["x"]
+        V[0, 0, i, 8:] = PADS[v["name"]]
+    geo = O.CacheGeometry(1, 1, 16, bits, 8, 0, 0, 8, dtype, outliers=1)
+    st = O.prefill(geo, O.from_f32(K, dtype), O.from_f32(V, dtype), 8)
+    return g, geo, st
+
+
+def test_e9_outlier_vectors():
+    """Hand-derived kept position, dense delta / zero point and codes of
+    seven vectors (O1-O3), per value token and per key channel."""
+    g = gold("e9_outlier_side_table.json")
+    for v in g["vectors"]:
+        x = np.array(v["x"], np.float32)
+        c, d, z, pos = O.quantize_values_per_token(x[None], v["bits"], outliers=True)
+        assert int(pos[0]) == v["pos"], v["name"]
+        assert float(d[0]) == v["delta"] and float(z[0]) == v["zp"], v["name"]
+        assert c[0].tolist() == v["codes"], v["name"]
+        # the same vector as one key channel over a group of 8 tokens
+        kc, kd, kz, kpos = O.quantize_keys_per_channel(x[:, None], 8, v["bits"], outliers=True)
+        assert int(kpos[0, 0]) == v["pos"] and kc[:, 0].tolist() == v["codes"], v["name"]
+        assert float(kd[0, 0]) == v["delta"] and float(kz[0, 0]) == v["zp"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_e9_outlier_side_tables_and_reconstruction(dtype):
+    """The cache's side tables hold the hand-derived positions (255 = none)
+    and exact values (bf16 bit patterns as derived), and the dequantized
+    cache reproduces the kept entries exactly and every other entry at its
+    dense value (O4, O5)."""
+    g, geo, st = _outlier_cache(dtype)
+    vecs = g["vectors"]
+    keys = g["keys"]
+    assert st["k_oidx"][0, 0, 0, :2].tolist() == keys["oidx"]
+    assert (st["k_oidx"][0, 0, 0, 2:] == 255).all()           # constant channels keep nothing
+    kval = O.to_f32(st["k_oval"][0, 0, 0, :2], dtype)
+    assert kval.tolist() == keys["oval"]
+    assert (O.to_f32(st["k_oval"][0, 0, 0, 2:], dtype) == 0).all()
+    if dtype == "bf16":
+        assert st["k_oval"][0, 0, 0, :2].tolist() == keys["oval_bf16"]
+    assert st["k_scale"][0, 0, 0, :2].tolist() == keys["delta"]
+    assert st["k_zero"][0, 0, 0, :2].tolist() == keys["zp"]
+    Kh, Vh = O.dequant_cache(geo, st, 8)
+    assert Kh[0, 0, :, 0].tolist() == vecs[0]["recon"]
+    assert Kh[0, 0, :, 1].tolist() == vecs[1]["recon"]
+    assert (Kh[0, 0, :, 2:] == np.arange(2, 16)).all()
+    for i in range(8):
+        v = vecs[i % 6]
+        assert int(st["v_oidx"][0, 0, i]) == (v["pos"] if v["pos"] >= 0 else 255), (i, v["name"])
+        assert float(O.to_f32(st["v_oval"][0, 0, i], dtype)) == (v["x"][v["pos"]] if v["pos"] >= 0 else 0)
+        assert float(st["v_scale"][0, 0, i]) == v["delta"] and float(st["v_zero"][0, 0, i]) == v["zp"]
+        assert Vh[0, 0, i].tolist() == v["recon"] + [PADS[v["name"]]] * 8, (i, v["name"])
+
+
+def test_outlier_choice_matches_brute_force():
+    """O2 against brute force over every single removal on integer vectors
+    (exact in fp32): the kept entry leaves the smallest range any single
+    removal can leave; nothing is kept exactly when no removal shrinks the
+    range; when removing the maximum reaches that smallest range the
+    maximum is kept (the tie rule)."""
+    rng = np.random.default_rng(5)
+    n_kept = 0
+    for trial in range(3000):
+        m = int(rng.integers(2, 13))
+        x = rng.integers(-6, 7, size=m).astype(np.float32)
+        if trial % 3 == 0:
+            x[rng.integers(0, m)] = rng.integers(-60, 61)
+        full = float(x.max() - x.min())
+        ranges = [float(np.delete(x, i).max() - np.delete(x, i).min()) for i in range(m)]
+        best = min(ranges)
+        pos, mn, mx = O.split_outlier(x)
+        pos = int(pos)
+        if best == full:
+            assert pos == -1, x
+            assert float(mn) == x.min() and float(mx) == x.max()
+            continue
+        n_kept += 1
+        assert pos >= 0 and ranges[pos] == best, (x, pos)
+        rest = np.delete(x, pos)
+        assert float(mn) == rest.min() and float(mx) == rest.max()
+        i_max = int(np.argmax(x))
+        if (x == x.max()).sum() == 1 and ranges[i_max] == best:
+            assert pos == i_max, x
+    assert n_kept > 1000
+
+
+@pytest.mark.parametrize("bits,dtype", [(2, "bf16"), (4, "f16"), (3, "f32")])
+def test_outliers_shrink_the_dense_range_and_reconstruct_exactly(bits, dtype):
+    """On heavy-tailed keys and values: the dense delta never exceeds the
+    plain one, kept entries come back exactly, every other entry within
+    delta / 2 of its input ([KIVI-PR] round-trip error <= scale/2, on the
+    dense part), and at most one entry per quantization vector is kept
+    (1/G of the keys, 1/D of the values)."""
+    B, H, D, G, S, R = 1, 2, 64, 32, 0, 0
+    T = 4 * G
+    rng = np.random.default_rng(bits)
+    K = rng.standard_t(2.0, size=(B, H, T, D)).astype(np.float32)
+    V = rng.standard_t(2.0, size=(B, H, T, D)).astype(np.float32)
+    Ks, Vs = synth.cast(K, dtype), synth.cast(V, dtype)
+    Kf, Vf = O.to_f32(Ks, dtype), O.to_f32(Vs, dtype)
+    geo = O.CacheGeometry(B, H, D, bits, G, S, R, T, dtype, outliers=1)
+    plain = O.CacheGeometry(B, H, D, bits, G, S, R, T, dtype)
+    st = O.prefill(geo, Ks, Vs, T)
+    sp = O.prefill(plain, Ks, Vs, T)
+    assert (st["k_scale"] <= sp["k_scale"]).all() and (st["v_scale"] <= sp["v_scale"]).all()
+    assert (st["k_scale"] < sp["k_scale"]).mean() > 0.5       # heavy tails: most ranges shrink
+    Kh, Vh = O.dequant_cache(geo, st, T)
+    rows = np.arange(T)
+    kmask = st["k_oidx"][:, :, rows // G] == (rows % G)[None, None, :, None]
+    vmask = np.arange(D)[None, None, None, :] == st["v_oidx"][..., None]
+    assert (Kh[kmask] == Kf[kmask]).all() and (Vh[vmask] == Vf[vmask]).all()
+    kd = np.repeat(st["k_scale"], G, axis=2).astype(np.float64)
+    vd = st["v_scale"][..., None].astype(np.float64)
+    tol = 1 + 2.0 ** -20
+    assert (np.abs(Kh - Kf) <= kd / 2 * tol + 2.0 ** -22 * np.abs(Kf))[~kmask].all()
+    assert (np.abs(Vh - Vf) <= np.broadcast_to(vd, Vh.shape) / 2 * tol + 2.0 ** -22 * np.abs(Vf))[~vmask].all()
+    # at most one per vector
+    assert kmask.reshape(B, H, T // G, G, D).sum(axis=3).max() <= 1
+    assert vmask.sum(axis=-1).max() <= 1
+    assert kmask.mean() <= 1 / G and vmask.mean() <= 1 / D
+
+
+@pytest.mark.parametrize("S,R,G,bits,dtype,W", [
+    (2, 32, 32, 4, "f32", 0), (0, 0, 32, 2, "bf16", 0), (3, 64, 64, 3, "f16", 0),
+    (4, 32, 32, 2, "bf16", 96)])
+def test_outlier_prefill_equals_streaming_appends(S, R, G, bits, dtype, W):
+    """[STORE-PR] streaming consistency with side tables: after every append
+    the live side-table entries equal those of a prefill of the same
+    tokens, as do codes and parameters (window case included)."""
+    B, H, D = 1, 2, 64
+    Tmax = S + 3 * (R + G) + 5 + (2 * W if W else 0)
+    case = synth.random_case(9, B, H, H, D, Tmax, dtype)
+    K, V = case["K"], case["V"]
+    geo = O.CacheGeometry(B, H, D, bits, G, S, R, Tmax, dtype, window=W, outliers=1)
+    st = geo.empty_state()
+    for n in range(Tmax):
+        st = O.append(geo, st, n, K[:, :, n], V[:, :, n])
+        T = n + 1
+        if T % 5 and T != Tmax:
+            continue
+        ref = O.prefill(geo, K, V, T)
+        vm = O.valid_masks(geo, T)
+        rows, groups = vm["rows"], vm["groups"]
+        for name in ("k_codes", "v_scale", "v_zero", "v_oidx", "v_oval"):
+            assert np.array_equal(st[name][:, :, rows], ref[name][:, :, rows]), (T, name)
+        for name in ("k_scale", "k_zero", "k_oidx", "k_oval"):
+            assert np.array_equal(st[name][:, :, groups], ref[name][:, :, groups]), (T, name)
+        assert (O.decode(geo, st, T, case["q"], H) == O.decode(geo, ref, T, case["q"], H)).all()
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_outliers_lift_attention_quality_on_spiky_caches(bits):
+    """[GUIDE] KVQuant's sparse side table: on caches where about 1% of the
+    entries are spikes 30x the typical magnitude, keeping the outliers
+    exact brings decode attention closer to fp64 attention on the inputs."""
+    B, Hq, Hkv, D, G, S, R = 1, 8, 2, 64, 32, 4, 32
+    T = S + 16 * G + R
+    rng = np.random.default_rng(bits + 40)
+    K = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    for A in (K, V):
+        spikes = rng.random(A.shape) < 0.01
+        A[spikes] *= 30
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    ref = O.attention(q, K.astype(np.float64), V.astype(np.float64))
+    err = {}
+    for o in (0, 1):
+        geo = O.CacheGeometry(B, Hkv, D, bits, G, S, R, T, "f32", outliers=o)
+        st = O.prefill(geo, K, V, T)
+        err[o] = O.row_rel_error(O.decode(geo, st, T, q, Hq), ref)
+    assert err[1] < 0.7 * err[0], err

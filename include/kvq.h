@@ -46,6 +46,18 @@
  *    then a ring: quantized token u (token S + u) lives at storage row
  *    u mod qcap, so each group that freezes evicts the oldest one, and the
  *    cache's size no longer grows with n_tokens.
+ *  - Dense-and-sparse outliers (pigeon guide "KV-cache quantization",
+ *    KVQuant adds, third bullet: about 1% of outlier values kept in a
+ *    sparse side table), with outliers = 1: each quantization vector (a
+ *    key group's channel over G tokens; a value token over D channels)
+ *    keeps at most one entry exact.  With the two largest entries max1 >=
+ *    max2 and the two smallest min1 <= min2, gap_hi = fl32(max1 - max2),
+ *    gap_lo = fl32(min2 - min1): the maximum is kept if gap_hi >= gap_lo
+ *    and gap_hi > 0, else the minimum if gap_lo > 0, else none.  delta and
+ *    the zero point come from the other entries; every entry, the kept
+ *    one too, is coded with them (the kept one's code clamps to 2^b - 1
+ *    or 0, so its dense value is zp + delta (2^b - 1) if it is >= zp,
+ *    else zp).  Attention reads the kept entry at its exact value.
  *
  * Conventions for every entry point:
  *  - All pointers except `cfg`, `cache` (the structs themselves) are
@@ -98,6 +110,8 @@ typedef struct {
   int32_t dtype;      /* kvq_dtype of K, V, q and the exact stores      */
   int64_t capacity;   /* maximum number of cached tokens                */
   int64_t window;     /* W: sliding window in tokens, 0 = none (below)  */
+  int32_t outliers;   /* 1: keep one exact entry per quantization       */
+                      /*    vector in side tables (above); 0: none       */
 } kvq_config;
 
 /*
@@ -130,6 +144,13 @@ typedef struct {
  * k_sink, v_sink   dtype [B][Hkv][S][D]: tokens 0..S-1, exact.
  * k_resid, v_resid dtype [B][Hkv][R+G][D]: full-precision ring; token
  *          t >= S lives in slot (t - S) mod (R + G).
+ * Side tables (outliers = 1 only; NULL otherwise):
+ * k_oidx   u8 [B][Hkv][qcap/G][D]: token offset (0..G-1) inside key group
+ *          slot k of channel d's kept entry, 255 = none.
+ * k_oval   dtype [B][Hkv][qcap/G][D]: its value (+0 when none).
+ * v_oidx   u8 [B][Hkv][qcap]: channel of the kept entry of the value token
+ *          at that storage row, 255 = none.
+ * v_oval   dtype [B][Hkv][qcap]: its value (+0 when none).
  *
  * Bytes of codes that belong to no quantized token yet are never written.
  */
@@ -144,6 +165,10 @@ typedef struct {
   void *v_sink;
   void *k_resid;
   void *v_resid;
+  uint8_t *k_oidx;
+  void *k_oval;
+  uint8_t *v_oidx;
+  void *v_oval;
 } kvq_cache;
 
 /* A strided device tensor whose last axis (D) is contiguous.  Strides are
@@ -177,6 +202,12 @@ static inline int64_t kvq_v_params_count(const kvq_config *c) {
 }
 static inline int64_t kvq_sink_bytes(const kvq_config *c) {
   return (int64_t)c->batch * c->n_kv_heads * c->sink * c->head_dim * kvq_dtype_bytes(c->dtype);
+}
+static inline int64_t kvq_k_side_count(const kvq_config *c) { /* entries per k_oidx / k_oval */
+  return c->outliers ? kvq_k_params_count(c) : 0;
+}
+static inline int64_t kvq_v_side_count(const kvq_config *c) { /* entries per v_oidx / v_oval */
+  return c->outliers ? kvq_v_params_count(c) : 0;
 }
 static inline int64_t kvq_resid_bytes(const kvq_config *c) {
   return (int64_t)c->batch * c->n_kv_heads * (c->residual + c->group) * c->head_dim *

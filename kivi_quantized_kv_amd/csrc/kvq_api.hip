@@ -50,6 +50,7 @@ kvq_status check_config(const kvq_config* c) {
   if (c->capacity > (int64_t(1) << 40)) return KVQ_EINVAL;
   // a window holds at least the full-precision tokens
   if (c->window < 0 || (c->window > 0 && c->window < int64_t(c->residual) + c->group)) return KVQ_EINVAL;
+  if (c->outliers != 0 && c->outliers != 1) return KVQ_EINVAL;
   return KVQ_OK;
 }
 
@@ -71,8 +72,10 @@ kvq_status check_cache(const kvq_config* c, const kvq_cache* k) {
     return KVQ_EINVAL;
   if (c->sink > 0 && (!k->k_sink || !k->v_sink)) return KVQ_EINVAL;
   if (!k->k_resid || !k->v_resid) return KVQ_EINVAL;
-  const void* ptrs[] = {k->k_codes, k->v_codes, k->k_scale, k->k_zero, k->v_scale,
-                        k->v_zero,  k->k_sink,  k->v_sink,  k->k_resid, k->v_resid};
+  if (q && c->outliers && (!k->k_oidx || !k->k_oval || !k->v_oidx || !k->v_oval)) return KVQ_EINVAL;
+  const void* ptrs[] = {k->k_codes, k->v_codes, k->k_scale, k->k_zero, k->v_scale, k->v_zero,
+                        k->k_sink,  k->v_sink,  k->k_resid, k->v_resid, k->k_oidx,  k->k_oval,
+                        k->v_oidx,  k->v_oval};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KVQ_EINVAL;
   return KVQ_OK;
@@ -178,6 +181,9 @@ kvq_status prefill_half(const kvq_config* c, const kvq_cache* k, const kvq_tenso
     q.scale = keys ? k->k_scale : k->v_scale;
     q.zero = keys ? k->k_zero : k->v_zero;
     q.S = S; q.qcap = kvq_qcap(c); q.H = H; q.G = int(G);
+    q.outliers = c->outliers;
+    q.oidx = keys ? k->k_oidx : k->v_oidx;
+    q.oval = static_cast<uint8_t*>(keys ? k->k_oval : k->v_oval);
     // with a window only the groups of the last qcap quantized tokens are
     // kept (older ones would be evicted by them), each storage slot once
     const int64_t k_first = Q > q.qcap ? (Q - q.qcap) / G : 0;
@@ -236,6 +242,9 @@ extern "C" kvq_status kvq_append_token(const kvq_config* cfg, const kvq_cache* c
     a.n_before = n_before; a.q_old = q_old; a.S = S; a.R = R; a.qcap = kvq_qcap(cfg);
     a.r_old = a.qcap > 0 ? q_old % a.qcap : 0;
     a.H = cfg->n_kv_heads; a.G = int(G); a.flush = q_new > q_old ? 1 : 0;
+    a.outliers = cfg->outliers;
+    a.k_oidx = cache->k_oidx; a.k_oval = static_cast<uint8_t*>(cache->k_oval);
+    a.v_oidx = cache->v_oidx; a.v_oval = static_cast<uint8_t*>(cache->v_oval);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (dispatch3<AppendFn>(cfg, a, cfg->batch, cfg->n_kv_heads, s) != hipSuccess) return KVQ_EHIP;
     return KVQ_OK;
@@ -282,13 +291,14 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
 
   // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit
   // codes, once at least one token is quantized (its chunk loads assume a
-  // chunk 0).  It works per KV head on 64-token chunks, with the grid sized
+  // chunk 0), for caches without side tables.  It works per KV head on 64-token chunks, with the grid sized
   // to one round of two workgroups per CU, and spreads the full-precision
   // tokens evenly over its splits.  Everything else runs the VALU kernel
   // per query head on value-code blocks, again with the full-precision
   // tokens spread evenly over the splits.
   const int gqa = n_q_heads / H;
-  const bool mfma = (gqa == 4 || gqa == 8) && (cfg->bits == 2 || cfg->bits == 4) && Q > 0;
+  const bool mfma = (gqa == 4 || gqa == 8) && (cfg->bits == 2 || cfg->bits == 4) && Q > 0 &&
+                    !cfg->outliers;
   const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
   const int64_t qcap = kvq_qcap(cfg);
   // sliding window: quantized tokens before u_lo are not attended; the
@@ -315,7 +325,7 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
     if (n_split < want_fp) n_split = want_fp;
     if (n_split < 1) n_split = 1;
     fp_per_split = (n_fp + n_split - 1) / n_split;
-  } else if (direct_rows(int64_t(B) * n_q_heads) && dispatch3<AttnValuDirectOkFn>(cfg)) {
+  } else if (direct_rows(int64_t(B) * n_q_heads) && !cfg->outliers && dispatch3<AttnValuDirectOkFn>(cfg)) {
     // the rows alone fill the GPU: one 16-wave workgroup per row takes
     // all of its tokens, merges in LDS and writes the output
     direct = true;
@@ -364,6 +374,9 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
   a.ncap = qcap / L;
   a.cw = a.ncap > 0 ? c0 / a.ncap * a.ncap : 0;
   a.lo_off = int(u_lo - c0 * L);
+  a.outliers = cfg->outliers;
+  a.k_oidx = cache->k_oidx; a.k_oval = cache->k_oval;
+  a.v_oidx = cache->v_oidx; a.v_oval = cache->v_oval;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t ea = hipSuccess;
   if (a.n_split > 0) {

@@ -238,8 +238,16 @@ constexpr int valu_waves_per_simd() {
   return (field_codes<BITS>() && (D == 64 || (BITS == 4 && DT == DT_F16))) ? 4 : 3;
 }
 
-template <int DT, int D, int BITS, int NW>
-__global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D, BITS>())) void k_attn_valu(
+// OUTL: caches with side tables (three waves per SIMD, two for fp32 rows
+// of 128 channels).
+template <int DT, int D, int BITS, bool OUTL>
+constexpr int valu_waves() {
+  if constexpr (OUTL) return (DT == DT_F32 && D == 128) ? 2 : 3;
+  else return valu_waves_per_simd<DT, D, BITS>();
+}
+
+template <int DT, int D, int BITS, int NW, bool OUTL>
+__global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OUTL>())) void k_attn_valu(
     AttnArgs a) {
   using VL = VLayout<BITS>;
   using WS = WordShape<BITS>;
@@ -273,9 +281,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
   constexpr int kThreads = 64 * NW;
   __shared__ __attribute__((aligned(16))) float s_x[NW][kHalves][D];
   __shared__ float s_out[NW][D + 2];
+  // side-table corrections: per key-group half, to the scores of its 32
+  // tokens; per block, to the value sums of each channel
+  __shared__ float s_kc[NW][kHalves * 32];
+  __shared__ float s_vc[NW][D];
+  constexpr bool outl = OUTL;
 
   for (int d = threadIdx.x; d < D; d += kThreads)
     s_q[d] = load1<DT>(a.q, b * a.q_sb + hq * a.q_sh + d) * a.sm_scale_log2;
+  if constexpr (outl) {
+    for (int i = threadIdx.x; i < NW * kHalves * 32; i += kThreads) (&s_kc[0][0])[i] = 0.f;
+    for (int i = threadIdx.x; i < NW * D; i += kThreads) (&s_vc[0][0])[i] = 0.f;
+  }
   __syncthreads();
 
   float m = -__builtin_inff(), l = 0.f, z = 0.f;
@@ -472,6 +489,30 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
       kap[k] = wave_sum_valu(kp);
     }
     wave_lds_sync();
+    if constexpr (outl) {
+      // keys kept exact: a channel's entry at group offset j adds
+      // s_q (x - dense) to the score of token j of its half, dense = zp +
+      // delta (2^b - 1) for an entry above the zero point, else zp (its
+      // code clamps to 2^b - 1 or 0)
+      constexpr float kLev = float((1 << BITS) - 1);
+#pragma unroll
+      for (int k = 0; k < kHalves; ++k) {
+        const int64_t row = blk_base(blk) + 32 * k;          // storage row of the half
+        const int64_t gi = ((row >> a.g_shift) + bh * a.kgroups) * D;
+        const int off = int(row & (a.G - 1));                 // the half's offset in its group
+#pragma unroll
+        for (int c = 0; c < kWC; ++c) {
+          const int ch = lane * kWC + c;
+          const int j = int(a.k_oidx[gi + ch]) - off;
+          if (j >= 0 && j < 32) {
+            const float xv = load1<DT>(a.k_oval, gi + ch);
+            const float dense = xv < r.kz[k][c] ? r.kz[k][c] : __builtin_fmaf(kLev, r.ks[k][c], r.kz[k][c]);
+            atomicAdd(&s_kc[wave][k * 32 + j], sq_w[c] * (xv - dense));
+          }
+        }
+      }
+      wave_lds_sync();
+    }
     // scores (log2 domain); lane (qt, tl) ends with token st*16 + tl
     float sc[kNST];
 #pragma unroll
@@ -500,11 +541,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
         // -inf past the quantized count (selected: the key parameters of a
         // group past the count are never written and may hold anything)
         const int st = 2 * k + u;
-        const float v = __builtin_fmaf(quad_sum(dot[u]), kS, kap[k]);
+        float v = __builtin_fmaf(quad_sum(dot[u]), kS, kap[k]);
+        if constexpr (outl) v += s_kc[wave][st * 16 + tl];
         sc[st] = st * 16 + tl < nvalid && st * 16 + tl >= lo ? v : -__builtin_inff();
       }
     }
     wave_lds_sync();
+    if constexpr (outl) if (qt == 0) {   // cleared for the next block (each wave reads in order)
+#pragma unroll
+      for (int st = 0; st < kNST; ++st) s_kc[wave][st * 16 + tl] = 0.f;
+    }
     float lmax = sc[0];
 #pragma unroll
     for (int st = 1; st < kNST; ++st) lmax = __builtin_fmaxf(lmax, sc[st]);
@@ -532,6 +578,25 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves_per_simd<DT, D,
       l += p;
       z = __builtin_fmaf(p, zv, z);
       pp[st] = p * __builtin_amdgcn_ldexpf(dvs[st], vke);
+      if constexpr (outl) if (qt == 0 && ok) {
+        // a value kept exact: p (x - dense) on its channel
+        const int64_t row = blk_base(blk) + st * 16 + tl;
+        const int vi = a.v_oidx[bh * a.qcap + row];
+        if (vi != 255) {
+          constexpr float kLev = float((1 << BITS) - 1);
+          const float xv = load1<DT>(a.v_oval, bh * a.qcap + row);
+          const float dense = xv < r.zv[st] ? r.zv[st] : __builtin_fmaf(kLev, r.dv[st], r.zv[st]);
+          atomicAdd(&s_vc[wave][vi], p * (xv - dense));
+        }
+      }
+    }
+    if constexpr (outl) {   // folded into the exact-token sums, which share p's scale
+      wave_lds_sync();
+#pragma unroll
+      for (int c = 0; c < kWC; ++c) {
+        accf[c] += s_vc[wave][lane * kWC + c];
+        s_vc[wave][lane * kWC + c] = 0.f;
+      }
     }
     // P . V: code slot i of lane group vg is token vslot_token(vg, i), whose
     // p sits in lane 4 * (i & 3) of this row, sub-tile o / 16
@@ -714,7 +779,7 @@ template <int DT, int D, int BITS>
 int attn_valu_blocks_per_cu() {
   static const int n = [] {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_valu<DT, D, BITS, 4>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_valu<DT, D, BITS, 4, false>, 256, 0) != hipSuccess ||
         v < 1)
       v = 1;
     return v;
@@ -732,13 +797,17 @@ template <int DT, int D, int BITS>
 hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s) {
   if (a.n_split == 1 && a.direct) {
     if constexpr (valu_waves_per_simd<DT, D, BITS>() == 4) {
-      hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 16>), dim3(1, a.Hq, B), dim3(1024), 0, s, a);
+      if (a.outliers) return hipErrorInvalidValue;   // the direct form has no side-table variant
+      hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 16, false>), dim3(1, a.Hq, B), dim3(1024), 0, s, a);
       return hipGetLastError();
     } else {
       return hipErrorInvalidValue;
     }
   }
-  hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 4>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
+  if (a.outliers)
+    hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 4, true>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 4, false>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <int DT, int D>

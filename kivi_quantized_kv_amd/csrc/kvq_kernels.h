@@ -28,7 +28,9 @@ struct QuantArgs {
   int64_t S, qcap;
   int64_t k0;               // first unit quantized (groups or 32-token steps); unit k goes to
                             // storage (k * unit tokens) mod qcap
-  int H, G;
+  uint8_t* oidx;            // side table (outliers != 0): positions, laid out as scale
+  uint8_t* oval;            // and the kept values in the input dtype
+  int H, G, outliers;
 };
 
 struct AppendArgs {
@@ -41,7 +43,8 @@ struct AppendArgs {
   void *k_sink, *v_sink, *k_resid, *v_resid;
   int64_t n_before, q_old, S, R, qcap;
   int64_t r_old;            // storage row of quantized token q_old: q_old mod qcap
-  int H, G, flush;
+  uint8_t *k_oidx, *k_oval, *v_oidx, *v_oval;   // side tables (outliers != 0)
+  int H, G, flush, outliers;
 };
 
 // Decode attention.  Split partials of row r = b*Hq + hq: o (D floats,
@@ -75,6 +78,11 @@ struct AttnArgs {
   // suffices); lo_off = u_lo - c0 * unit tokens of unit c0 are masked.
   int64_t u_lo, c0, cw, ncap;
   int lo_off;
+  // Dense-and-sparse outliers (outliers != 0, VALU kernel): side tables of
+  // one kept entry per key group channel and per value token.
+  const uint8_t *k_oidx, *v_oidx;
+  const void *k_oval, *v_oval;
+  int outliers;
 };
 
 __device__ __forceinline__ float* partial_o(const AttnArgs& a, int64_t row, int split, int D) {

@@ -82,9 +82,11 @@ __device__ __forceinline__ void affine_codes(const float* x, const float* delta,
   for (int i = 0; i < N; ++i) {
     const float a = x[i] - zp[i];
     const float y = a * rcp[i];
-    const float r = __builtin_rintf(y);   // 0 <= y < levels + 1/2: no clamp needed
+    const float r = __builtin_rintf(y);
     risky |= __builtin_fabsf(y - r) >= kBand;
-    c[i] = r;
+    // clamped: an entry kept exact in a side table lies outside the dense
+    // range (an infinite or NaN y, from x - zp overflowing, clamps too)
+    c[i] = __builtin_fminf(__builtin_fmaxf(r, 0.0f), levels);
   }
   if (__builtin_amdgcn_ballot_w64(risky) != 0) {
 #pragma unroll
@@ -134,6 +136,88 @@ __device__ __forceinline__ void minmax_run(float& mn, float& mx) {
     partner_pair<false>(mx, a, b); mx = __builtin_fmaxf(a, b);
   }
 }
+
+// ----------------------------------------------------------------------------
+// Dense-and-sparse split (pigeon guide "KV-cache quantization", KVQuant
+// adds: outliers kept in a sparse side table).  A vector keeps at most one
+// entry exact: the maximum or the minimum, whichever leaves the smaller
+// range.  The reductions carry the two largest and two smallest entries,
+// with multiplicity.
+// ----------------------------------------------------------------------------
+struct Ext2 {
+  float lo1, lo2, hi1, hi2;   // lo1 <= lo2, hi1 >= hi2
+};
+__device__ __forceinline__ Ext2 ext2_of(float x) { return {x, __builtin_inff(), x, -__builtin_inff()}; }
+__device__ __forceinline__ void ext2_add(Ext2& e, float x) {
+  e.hi2 = __builtin_fmaxf(e.hi2, __builtin_fminf(e.hi1, x));
+  e.hi1 = __builtin_fmaxf(e.hi1, x);
+  e.lo2 = __builtin_fminf(e.lo2, __builtin_fmaxf(e.lo1, x));
+  e.lo1 = __builtin_fminf(e.lo1, x);
+}
+__device__ __forceinline__ void ext2_merge(Ext2& e, const Ext2& o) {
+  e.hi2 = __builtin_fmaxf(__builtin_fminf(e.hi1, o.hi1), __builtin_fmaxf(e.hi2, o.hi2));
+  e.hi1 = __builtin_fmaxf(e.hi1, o.hi1);
+  e.lo2 = __builtin_fminf(__builtin_fmaxf(e.lo1, o.lo1), __builtin_fminf(e.lo2, o.lo2));
+  e.lo1 = __builtin_fminf(e.lo1, o.lo1);
+}
+template <int CTRL>
+__device__ __forceinline__ void ext2_dpp_merge(Ext2& e) {
+  const Ext2 o{dpp_mov<CTRL>(e.lo1), dpp_mov<CTRL>(e.lo2), dpp_mov<CTRL>(e.hi1), dpp_mov<CTRL>(e.hi2)};
+  ext2_merge(e, o);
+}
+template <bool X32>
+__device__ __forceinline__ void ext2_swap_merge(Ext2& e) {
+  Ext2 a, b;
+  partner_pair<X32>(e.lo1, a.lo1, b.lo1);
+  partner_pair<X32>(e.lo2, a.lo2, b.lo2);
+  partner_pair<X32>(e.hi1, a.hi1, b.hi1);
+  partner_pair<X32>(e.hi2, a.hi2, b.hi2);
+  ext2_merge(a, b);
+  e = a;
+}
+// ext2 all-reduce over the lanes l, l ^ S, l ^ 2S, ... (as minmax_across)
+template <int S>
+__device__ __forceinline__ void ext2_across(Ext2& e) {
+  if constexpr (S <= 8) ext2_dpp_merge<kRowRor8>(e);
+  if constexpr (S <= 16) ext2_swap_merge<false>(e);
+  ext2_swap_merge<true>(e);
+}
+// ext2 all-reduce over aligned runs of N = 8 or 16 lanes (as minmax_run)
+template <int N>
+__device__ __forceinline__ void ext2_run(Ext2& e) {
+  ext2_dpp_merge<kQuadXor1>(e);
+  ext2_dpp_merge<kQuadXor2>(e);
+  ext2_dpp_merge<0x141>(e);   // half-row mirror
+  if constexpr (N >= 16) ext2_dpp_merge<0x140>(e);   // row mirror
+}
+// The dense range [lo, hi] and the kept entry's value kv; returns 1 (the
+// maximum kept), -1 (the minimum) or 0 (none: neither removal shrinks the
+// range).  Gaps in fp32; a tie keeps the maximum.
+__device__ __forceinline__ int dense_split(const Ext2& e, float& lo, float& hi, float& kv) {
+  const float gh = e.hi1 - e.hi2, gl = e.lo2 - e.lo1;
+  const bool th = gh >= gl && gh > 0.0f;
+  const bool tl = !th && gl > 0.0f;
+  lo = tl ? e.lo2 : e.lo1;
+  hi = th ? e.hi2 : e.hi1;
+  kv = th ? e.hi1 : e.lo1;
+  return th ? 1 : (tl ? -1 : 0);
+}
+// Side-table slot i: position and the value, exactly, in the input dtype
+// (the value came from that dtype, so narrowing is exact).
+template <int DT>
+__device__ __forceinline__ void store_side(uint8_t* idx, uint8_t* val, int64_t i, int pos, float v) {
+  idx[i] = uint8_t(pos);
+  if constexpr (DT == DT_F32) reinterpret_cast<float*>(val)[i] = v;
+  else if constexpr (DT == DT_F16) reinterpret_cast<_Float16*>(val)[i] = _Float16(v);
+  else reinterpret_cast<uint16_t*>(val)[i] = uint16_t(__builtin_bit_cast(uint32_t, v) >> 16);
+}
+// Side tables of one unit (a key group: D entries; a value step: rows of
+// the head), or none.
+struct Side {
+  uint8_t* idx;
+  uint8_t* val;   // input dtype
+  bool on;
+};
 
 // Store the n = 8 b bits of eight b-bit codes at p (aligned to b bytes):
 // one store at 1, 2, 4 and 8 bits, byte stores at the widths whose codes
@@ -199,7 +283,8 @@ __device__ __forceinline__ void load_key_rows(const Rows& rows, KeyRows<DT, D, G
 
 template <int DT, int D, int BITS, int G>
 __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_scale, float* k_zero,
-                                          uint8_t* code_rows, float (*s_red)[D], float (*s_par)[D]) {
+                                          uint8_t* code_rows, Side side, float (*s_red)[D],
+                                          float (*s_par)[D]) {
   using RS = RowSplit<DT, D>;
   constexpr int kVE = RS::kVE, kTPR = RS::kTPR, kRPP = RS::kRPP;
   constexpr int kRPT = KeyRows<DT, D, G>::kRPT;
@@ -210,33 +295,63 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
   float x[kRPT][kVE];
 #pragma unroll
   for (int i = 0; i < kRPT; ++i) widen_piece<DT>(raw[i], x[i]);
-  float mn[kVE], mx[kVE];
-#pragma unroll
-  for (int e = 0; e < kVE; ++e) {
-    mn[e] = x[0][e];
-    mx[e] = x[0][e];
-#pragma unroll
-    for (int i = 1; i < kRPT; ++i) {
-      mn[e] = __builtin_fminf(mn[e], x[i][e]);
-      mx[e] = __builtin_fmaxf(mx[e], x[i][e]);
-    }
-    minmax_across<kTPR>(mn[e], mx[e]);
-  }
   // the waves meet in LDS: rows 0..3 of s_red hold minima, 4..7 maxima
-  if (lane < kTPR) {
+  // (with a side table, 8..11 the second smallest, 12..15 the second
+  // largest)
+  if (side.on) {
 #pragma unroll
     for (int e = 0; e < kVE; ++e) {
-      s_red[wave][cs * kVE + e] = mn[e];
-      s_red[4 + wave][cs * kVE + e] = mx[e];
+      Ext2 ex2 = ext2_of(x[0][e]);
+#pragma unroll
+      for (int i = 1; i < kRPT; ++i) ext2_add(ex2, x[i][e]);
+      ext2_across<kTPR>(ex2);
+      if (lane < kTPR) {
+        s_red[wave][cs * kVE + e] = ex2.lo1;
+        s_red[4 + wave][cs * kVE + e] = ex2.hi1;
+        s_red[8 + wave][cs * kVE + e] = ex2.lo2;
+        s_red[12 + wave][cs * kVE + e] = ex2.hi2;
+      }
+    }
+  } else {
+    float mn[kVE], mx[kVE];
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) {
+      mn[e] = x[0][e];
+      mx[e] = x[0][e];
+#pragma unroll
+      for (int i = 1; i < kRPT; ++i) {
+        mn[e] = __builtin_fminf(mn[e], x[i][e]);
+        mx[e] = __builtin_fmaxf(mx[e], x[i][e]);
+      }
+      minmax_across<kTPR>(mn[e], mx[e]);
+    }
+    if (lane < kTPR) {
+#pragma unroll
+      for (int e = 0; e < kVE; ++e) {
+        s_red[wave][cs * kVE + e] = mn[e];
+        s_red[4 + wave][cs * kVE + e] = mx[e];
+      }
     }
   }
   __syncthreads();
   // one thread per channel: delta, zero point and reciprocal, written out
   // and shared through LDS (row 3 of s_par flags a delta that needs the
-  // exact division)
+  // exact division; rows 4 and 5 the kept entry: flag and value)
   if (t < D) {
-    const float lo = __builtin_fminf(__builtin_fminf(s_red[0][t], s_red[1][t]), __builtin_fminf(s_red[2][t], s_red[3][t]));
-    const float hi = __builtin_fmaxf(__builtin_fmaxf(s_red[4][t], s_red[5][t]), __builtin_fmaxf(s_red[6][t], s_red[7][t]));
+    float lo, hi;
+    if (side.on) {
+      Ext2 ex2{s_red[0][t], s_red[8][t], s_red[4][t], s_red[12][t]};
+#pragma unroll
+      for (int w = 1; w < 4; ++w) ext2_merge(ex2, Ext2{s_red[w][t], s_red[8 + w][t], s_red[4 + w][t], s_red[12 + w][t]});
+      float kv;
+      const int keep = dense_split(ex2, lo, hi, kv);
+      s_par[4][t] = keep != 0 ? 1.0f : 0.0f;
+      s_par[5][t] = kv;
+      if (keep == 0) store_side<DT>(side.idx, side.val, t, 255, 0.0f);
+    } else {
+      lo = __builtin_fminf(__builtin_fminf(s_red[0][t], s_red[1][t]), __builtin_fminf(s_red[2][t], s_red[3][t]));
+      hi = __builtin_fmaxf(__builtin_fmaxf(s_red[4][t], s_red[5][t]), __builtin_fmaxf(s_red[6][t], s_red[7][t]));
+    }
     float dl, z;
     bool ex = false;
     affine_params(lo, hi, kLevels, dl, z);
@@ -262,6 +377,18 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
     zp[e] = z4.x; zp[e + 1] = z4.y; zp[e + 2] = z4.z; zp[e + 3] = z4.w;
     rcp[e] = r4.x; rcp[e + 1] = r4.y; rcp[e + 2] = r4.z; rcp[e + 3] = r4.w;
     exact |= (x4.x + x4.y + x4.z + x4.w) != 0.0f;
+  }
+  if (side.on) {   // the thread holding a kept entry writes its side-table slot
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) {
+      const int c = cs * kVE + e;
+      if (s_par[4][c] != 0.0f) {
+        const float kv = s_par[5][c];
+#pragma unroll
+        for (int i = 0; i < kRPT; ++i)
+          if (x[i][e] == kv) store_side<DT>(side.idx, side.val, c, r0 + i * kRPP, x[i][e]);
+      }
+    }
   }
   constexpr int kRB = D * BITS / 8;
 #pragma unroll
@@ -303,7 +430,8 @@ __device__ __forceinline__ void load_step_rows(const Rows& rows, StepRows<DT, D>
 
 template <int DT, int D, int BITS>
 __device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0, float* v_scale,
-                                           float* v_zero, uint8_t* v_codes_head, uint8_t* s_codes) {
+                                           float* v_zero, uint8_t* v_codes_head, Side side,
+                                           uint8_t* s_codes) {
   using RS = RowSplit<DT, D>;
   using VL = VLayout<BITS>;
   constexpr int kVE = RS::kVE, kTPR = RS::kTPR, kRPP = RS::kRPP;
@@ -316,13 +444,33 @@ __device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0
     const int tok = r0 + j * kRPP;
     float x[kVE];
     widen_piece<DT>(raw[j], x);
-    float mn = x[0], mx = x[0];
+    float mn, mx;
+    if (side.on) {
+      Ext2 ex2 = ext2_of(x[0]);
 #pragma unroll
-    for (int e = 1; e < kVE; ++e) {
-      mn = __builtin_fminf(mn, x[e]);
-      mx = __builtin_fmaxf(mx, x[e]);
+      for (int e = 1; e < kVE; ++e) ext2_add(ex2, x[e]);
+      ext2_run<kTPR>(ex2);
+      float kv;
+      const int keep = dense_split(ex2, mn, mx, kv);
+      // the lane holding the kept entry writes the token's slot; lane 0 of
+      // the token writes "none"
+      if (keep == 0) {
+        if (cs == 0) store_side<DT>(side.idx, side.val, u0 + tok, 255, 0.0f);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kVE; ++e)
+          if (x[e] == kv) store_side<DT>(side.idx, side.val, u0 + tok, cs * kVE + e, x[e]);
+      }
+    } else {
+      mn = x[0];
+      mx = x[0];
+#pragma unroll
+      for (int e = 1; e < kVE; ++e) {
+        mn = __builtin_fminf(mn, x[e]);
+        mx = __builtin_fmaxf(mx, x[e]);
+      }
+      minmax_run<kTPR>(mn, mx);
     }
-    minmax_run<kTPR>(mn, mx);
     float delta[kVE], zp[kVE], rcp[kVE];
     bool exact = false;
     affine_params(mn, mx, kLevels, delta[0], zp[0]);
@@ -412,8 +560,8 @@ __global__ __launch_bounds__(64) void k_copy_fp_rows(FpCopyArgs a) {
 // fewer workgroups streaming several units each (measured).
 template <int DT, int D, int BITS, int G>
 __global__ __launch_bounds__(256) void k_quant_keys(QuantArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_red[8][D];
-  __shared__ __attribute__((aligned(16))) float s_par[4][D];
+  __shared__ __attribute__((aligned(16))) float s_red[16][D];
+  __shared__ __attribute__((aligned(16))) float s_par[6][D];
   const int64_t k = a.k0 + blockIdx.x;
   const int64_t ks = k % (a.qcap / G);              // storage slot of group k
   const int h = blockIdx.y, b = blockIdx.z;
@@ -424,8 +572,9 @@ __global__ __launch_bounds__(256) void k_quant_keys(QuantArgs a) {
       InputRows{reinterpret_cast<const uint8_t*>(a.src) + (b * a.sb + h * a.sh + (a.S + k * G) * a.st) * EB,
                 a.st * EB},
       kr);
-  key_group<DT, D, BITS, G>(kr, a.scale + (bh * (a.qcap / G) + ks) * D, a.zero + (bh * (a.qcap / G) + ks) * D,
-                            a.codes + (bh * a.qcap + ks * G) * (D * BITS / 8), s_red, s_par);
+  const int64_t gi = (bh * (a.qcap / G) + ks) * D;   // first parameter of the group
+  key_group<DT, D, BITS, G>(kr, a.scale + gi, a.zero + gi, a.codes + (bh * a.qcap + ks * G) * (D * BITS / 8),
+                            Side{a.oidx + gi, a.oval + gi * EB, a.outliers != 0}, s_red, s_par);
 }
 
 template <int DT, int D, int BITS>
@@ -442,7 +591,8 @@ __global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
                 a.st * EB},
       sr);
   value_step<DT, D, BITS>(sr, r0, a.scale + bh * a.qcap, a.zero + bh * a.qcap,
-                          a.codes + bh * (a.qcap * D * BITS / 8), s_codes);
+                          a.codes + bh * (a.qcap * D * BITS / 8),
+                          Side{a.oidx + bh * a.qcap, a.oval + bh * a.qcap * EB, a.outliers != 0}, s_codes);
 }
 
 // ----------------------------------------------------------------------------
@@ -486,16 +636,17 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   const int64_t first = a.S + a.q_old;
   const int fresh_row = int(t - first);          // in [0, G) when t is in the group
   if (role == 1) {
-    __shared__ __attribute__((aligned(16))) float s_red[8][D];
-    __shared__ __attribute__((aligned(16))) float s_par[4][D];
+    __shared__ __attribute__((aligned(16))) float s_red[16][D];
+    __shared__ __attribute__((aligned(16))) float s_par[6][D];
     const RingRows rows{reinterpret_cast<const uint8_t*>(a.k_resid) + bh * ring * D * EB, kin,
                         (first - a.S) % ring, ring, fresh_row, D * EB};
     const int64_t kgrp = a.r_old / G;                 // storage slot of the group
+    const int64_t gi = (bh * (a.qcap / G) + kgrp) * D;
     KeyRows<DT, D, G> kr;
     load_key_rows<DT, D, G>(rows, kr);
-    key_group<DT, D, BITS, G>(kr, a.k_scale + (bh * (a.qcap / G) + kgrp) * D,
-                              a.k_zero + (bh * (a.qcap / G) + kgrp) * D,
-                              a.k_codes + (bh * a.qcap + a.r_old) * (D * BITS / 8), s_red, s_par);
+    key_group<DT, D, BITS, G>(kr, a.k_scale + gi, a.k_zero + gi,
+                              a.k_codes + (bh * a.qcap + a.r_old) * (D * BITS / 8),
+                              Side{a.k_oidx + gi, a.k_oval + gi * EB, a.outliers != 0}, s_red, s_par);
   } else {
     __shared__ __attribute__((aligned(16))) uint8_t s_codes[D * kStepPitch];
     const int step = role - 2;
@@ -504,7 +655,9 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     StepRows<DT, D> sr;
     load_step_rows<DT, D>(rows, sr);
     value_step<DT, D, BITS>(sr, a.r_old + 32 * step, a.v_scale + bh * a.qcap, a.v_zero + bh * a.qcap,
-                            a.v_codes + bh * (a.qcap * D * BITS / 8), s_codes);
+                            a.v_codes + bh * (a.qcap * D * BITS / 8),
+                            Side{a.v_oidx + bh * a.qcap, a.v_oval + bh * a.qcap * EB, a.outliers != 0},
+                            s_codes);
   }
 }
 

@@ -37,13 +37,14 @@ class c_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("sink", ctypes.c_int32),
                 ("residual", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("capacity", ctypes.c_int64), ("window", ctypes.c_int64)]
+                ("capacity", ctypes.c_int64), ("window", ctypes.c_int64),
+                ("outliers", ctypes.c_int32)]
 
 
 class c_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
-        "k_sink", "v_sink", "k_resid", "v_resid")]
+        "k_sink", "v_sink", "k_resid", "v_resid", "k_oidx", "k_oval", "v_oidx", "v_oval")]
 
 
 class c_tensor(ctypes.Structure):
@@ -93,12 +94,13 @@ class Config:
     capacity: int
     dtype: str = "bf16"
     window: int = 0          # sliding window in tokens, 0 = none
+    outliers: int = 0        # 1: one exact entry per quantization vector in side tables
 
     def c(self) -> c_config:
         """A new kvq_config struct of these fields."""
         return c_config(self.batch, self.n_kv_heads, self.head_dim, self.bits, self.group,
                         self.sink, self.residual, DTYPE_CODE[self.dtype], self.capacity,
-                        self.window)
+                        self.window, self.outliers)
 
     def _cref(self):
         """Pointer to this config's struct, built once (the dataclass is frozen)."""
@@ -148,6 +150,11 @@ class Cache:
         self.v_sink = torch.zeros((B, H, cfg.sink, D), dtype=td, **z)
         self.k_resid = torch.zeros((B, H, cfg.residual + G, D), dtype=td, **z)
         self.v_resid = torch.zeros((B, H, cfg.residual + G, D), dtype=td, **z)
+        no = 1 if cfg.outliers else 0     # side tables only with outliers
+        self.k_oidx = torch.zeros((B, H, no * qc // G, D), dtype=torch.uint8, **z)
+        self.k_oval = torch.zeros((B, H, no * qc // G, D), dtype=td, **z)
+        self.v_oidx = torch.zeros((B, H, no * qc), dtype=torch.uint8, **z)
+        self.v_oval = torch.zeros((B, H, no * qc), dtype=td, **z)
         if fill is not None:
             for n in self.BUFFERS:
                 t = getattr(self, n)
@@ -155,7 +162,7 @@ class Cache:
                     t.view(torch.uint8).fill_(fill)
 
     BUFFERS = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
-               "k_sink", "v_sink", "k_resid", "v_resid")
+               "k_sink", "v_sink", "k_resid", "v_resid", "k_oidx", "k_oval", "v_oidx", "v_oval")
 
     def __setattr__(self, name, value):
         # a replaced buffer invalidates the cached kvq_cache struct

@@ -150,3 +150,19 @@ def random_case(seed: int, B: int, Hq: int, Hkv: int, D: int, T: int, dtype: str
         "k_new": cast(k_new, dtype), "v_new": cast(v_new, dtype),
         "q_new": cast(q_new, dtype), "outlier_channels": chans, "workload": w,
     }
+
+
+def spiky_case(seed: int, B: int, Hq: int, Hkv: int, D: int, T: int, dtype: str,
+               frac: float = 0.01, spike: float = 30.0):
+    """random_case with about `frac` of the key and value entries scaled by
+    `spike` (sparse outliers on top of the fixed outlier channels), the
+    workload a dense-and-sparse side table is for."""
+    case = random_case(seed, B, Hq, Hkv, D, T, "f32")
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    out = dict(case)
+    for name in ("K", "V"):
+        x = case[name].copy()
+        x[rng.random(x.shape) < frac] *= np.float32(spike)
+        out[name] = cast(x, dtype)
+    out["q"] = cast(case["q"], dtype)
+    return out

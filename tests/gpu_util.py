@@ -31,7 +31,8 @@ def make(cfg_kw):
     from kivi_quantized_kv_amd import kvq
     cfg = kvq.Config(**cfg_kw)
     geo = O.CacheGeometry(cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.bits, cfg.group,
-                          cfg.sink, cfg.residual, cfg.capacity, cfg.dtype, cfg.window)
+                          cfg.sink, cfg.residual, cfg.capacity, cfg.dtype, cfg.window,
+                          cfg.outliers)
     return cfg, geo
 
 
@@ -70,3 +71,8 @@ def compare_state(geo, got: dict, ref: dict, T: int, heads=None):
     eq("v_sink", got["v_sink"][:, sl, :ns], ref["v_sink"][:, sl, :ns])
     eq("k_resid", got["k_resid"][:, sl][:, :, vm["ring"]], ref["k_resid"][:, sl][:, :, vm["ring"]])
     eq("v_resid", got["v_resid"][:, sl][:, :, vm["ring"]], ref["v_resid"][:, sl][:, :, vm["ring"]])
+    if geo.outliers:
+        for n in ("k_oidx", "k_oval"):
+            eq(n, got[n][:, sl][:, :, groups], ref[n][:, sl][:, :, groups])
+        for n in ("v_oidx", "v_oval"):
+            eq(n, got[n][:, sl][:, :, rows], ref[n][:, sl][:, :, rows])

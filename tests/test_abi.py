@@ -41,11 +41,12 @@ def _header_sizes(cfg):
 #include <stdio.h>
 #include "kvq.h"
 int main(int argc, char** argv) {
-  kvq_config c = {%d, %d, %d, %d, %d, %d, %d, %d, %dLL};
-  printf("%%lld %%lld %%lld %%lld %%lld %%lld %%lld\n", (long long)kvq_qcap(&c),
+  kvq_config c = {%d, %d, %d, %d, %d, %d, %d, %d, %dLL, 0LL, %d};
+  printf("%%lld %%lld %%lld %%lld %%lld %%lld %%lld %%lld %%lld\n", (long long)kvq_qcap(&c),
          (long long)kvq_k_codes_bytes(&c), (long long)kvq_v_codes_bytes(&c),
          (long long)kvq_k_params_count(&c), (long long)kvq_v_params_count(&c),
-         (long long)kvq_sink_bytes(&c), (long long)kvq_resid_bytes(&c));
+         (long long)kvq_sink_bytes(&c), (long long)kvq_resid_bytes(&c),
+         (long long)kvq_k_side_count(&c), (long long)kvq_v_side_count(&c));
   return 0;
 }
 """ % cfg
@@ -73,11 +74,14 @@ int main(int argc, char** argv) {
     (1, 4, 128, 7, 128, 4, 128, 5000, "f16"),
     (1, 1, 64, 6, 32, 4, 32, 300, "bf16"),
 ])
-def test_header_sizes_match_oracle_geometry(B, H, D, bits, G, S, R, cap, dt):
+@pytest.mark.parametrize("outl", [0, 1])
+def test_header_sizes_match_oracle_geometry(B, H, D, bits, G, S, R, cap, dt, outl):
     code = {"f32": 0, "f16": 1, "bf16": 2}[dt]
-    qcap, kc, vc, kp, vp, sink, resid = _header_sizes((B, H, D, bits, G, S, R, code, cap))
-    geo = O.CacheGeometry(B, H, D, bits, G, S, R, cap, dt)
+    qcap, kc, vc, kp, vp, sink, resid, ks, vs = _header_sizes((B, H, D, bits, G, S, R, code, cap, outl))
+    geo = O.CacheGeometry(B, H, D, bits, G, S, R, cap, dt, outliers=outl)
     st = geo.empty_state()
+    assert ks == st["k_oidx"].size == st["k_oval"].size
+    assert vs == st["v_oidx"].size == st["v_oval"].size
     assert qcap == geo.qcap
     assert kc == st["k_codes"].nbytes and vc == st["v_codes"].nbytes
     assert kp == st["k_scale"].size and vp == st["v_scale"].size
@@ -106,6 +110,10 @@ def test_validation_rejects_bad_arguments_without_launching():
     assert qk(bad) == 2
     bad = cfg.c(); bad.bits = 9
     assert qk(bad) == 2
+    bad = cfg.c(); bad.outliers = 2
+    assert qk(bad) == 1
+    bad = cfg.c(); bad.outliers = 1           # side tables missing from the cache
+    assert qk(bad) == 1
     bad = cfg.c(); bad.head_dim = 96
     assert qk(bad) == 2
     bad = cfg.c(); bad.group = 48

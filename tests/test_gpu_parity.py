@@ -34,9 +34,9 @@ def _run_prefill(kvq, cfg, data, T):
     return cache
 
 
-def _cfg_kw(B, H, D, bits, G, S, R, cap, dtype, window=0):
+def _cfg_kw(B, H, D, bits, G, S, R, cap, dtype, window=0, outliers=0):
     return dict(batch=B, n_kv_heads=H, head_dim=D, bits=bits, group=G, sink=S, residual=R,
-                capacity=cap, dtype=dtype, window=window)
+                capacity=cap, dtype=dtype, window=window, outliers=outliers)
 
 
 # ----------------------------------------------------------------- small cases
@@ -547,3 +547,77 @@ def test_workload_streaming(name):
             o = out.cpu().numpy()
             err = O.row_rel_error(o, O.decode(geo, st, n + 1, data["q_new"][i], w.n_q_heads))
             assert err <= ATOL_ROW_REL, (i + 1, err)
+
+
+# Dense-and-sparse outliers: one exact entry per key group channel and per
+# value token in side tables (both kept on the VALU kernel).
+OUTLIER = [
+    # B, Hq, Hkv, D, bits, G, S, R, T, dtype, window
+    (1, 4, 2, 64, 4, 32, 4, 32, 333, "f16", 0),
+    (2, 8, 2, 128, 2, 64, 2, 64, 700, "bf16", 0),      # GQA 4, 2-bit
+    (1, 8, 1, 128, 4, 32, 4, 128, 1500, "bf16", 0),    # GQA 8, 4-bit
+    (1, 2, 2, 64, 8, 128, 0, 0, 520, "f32", 0),
+    (1, 4, 1, 128, 3, 32, 3, 32, 611, "f16", 0),       # bit-stream width
+    (1, 2, 1, 128, 8, 32, 4, 32, 300, "f32", 0),       # fp32 rows of 128 channels
+    (1, 8, 2, 64, 2, 32, 4, 32, 900, "bf16", 192),     # sliding window
+]
+
+
+@pytest.mark.parametrize("case", OUTLIER, ids=lambda c: "-".join(map(str, c)))
+def test_outlier_side_tables_prefill_streaming_and_attention(case):
+    """[pigeon guide 'KV-cache quantization', KVQuant adds] the side tables,
+    codes and dense parameters bit-exact against the oracle after a prefill
+    of spiky keys and values and after each of 70 appends (across freezes),
+    and attention with the kept entries read exactly within 2e-3."""
+    kvq = _kvq()
+    B, Hq, Hkv, D, bits, G, S, R, T, dt, W = case
+    log("outliers", case)
+    steps = 70
+    data = synth.spiky_case(41 + sum(case[:9]), B, Hq, Hkv, D, T + steps, dt)
+    cfg, geo = make(_cfg_kw(B, Hkv, D, bits, G, S, R, T + steps, dt, window=W, outliers=1))
+    cache = kvq.Cache(cfg, fill=0xFF)
+    Kd, Vd, qd = to_dev(data["K"], dt), to_dev(data["V"], dt), to_dev(data["q"], dt)
+    kvq.prefill(cfg, cache, Kd, Vd, T)
+    torch.cuda.synchronize()
+    st = O.prefill(geo, data["K"], data["V"], T)
+    compare_state(geo, read_state(cache), st, T)
+    assert (st["v_oidx"] != 255).any() and (st["k_oidx"] != 255).any()
+    out = kvq.kvq_decode_attention(cfg, cache, T, qd).cpu().numpy()
+    err = O.row_rel_error(out, O.decode(geo, st, T, data["q"], Hq))
+    log("row rel err", err)
+    assert err <= ATOL_ROW_REL
+    for n in range(T, T + steps):
+        kvq.kvq_append_token(cfg, cache, n, Kd[:, :, n], Vd[:, :, n])
+        st = O.append(geo, st, n, data["K"][:, :, n], data["V"][:, :, n])
+        if (n + 1) % 16 == 0 or n + 1 == T + steps:
+            compare_state(geo, read_state(cache), st, n + 1)
+            out = kvq.kvq_decode_attention(cfg, cache, n + 1, qd).cpu().numpy()
+            err = O.row_rel_error(out, O.decode(geo, st, n + 1, data["q"], Hq))
+            assert err <= ATOL_ROW_REL, (n + 1, err)
+    fresh = kvq.Cache(cfg)
+    kvq.prefill(cfg, fresh, Kd, Vd, T + steps)
+    torch.cuda.synchronize()
+    compare_state(geo, read_state(fresh), st, T + steps)
+
+
+@pytest.mark.parametrize("kind", ["ties", "constant", "negzero", "vwide30", "outlier300"])
+def test_outlier_side_tables_on_edge_values(kind):
+    """Edge-value caches with side tables: tied extremes (nothing or the
+    maximum kept), constant vectors (nothing kept), -0, 1e30 values and
+    300x outlier channels, state bit-exact and attention within 2e-3."""
+    kvq = _kvq()
+    Hq, Hkv, bits, G, D = 4, 1, 4, 32, 128
+    B, S, R, T = 1, 2, 32, 524
+    log("outlier edge", kind)
+    data, dt = _edge_inputs(kind, B, Hq, Hkv, D, G, S, T, bits, seed=77)
+    cfg, geo = make(_cfg_kw(B, Hkv, D, bits, G, S, R, T, dt, outliers=1))
+    cache = _run_prefill(kvq, cfg, data, T)
+    ref = O.prefill(geo, data["K"], data["V"], T)
+    compare_state(geo, read_state(cache), ref, T)
+    out = kvq.kvq_decode_attention(cfg, cache, T, to_dev(data["q"], dt)).cpu().numpy()
+    assert np.isfinite(out).all()
+    exp = O.decode(geo, ref, T, data["q"], Hq)
+    err = O.row_rel_error(out, exp)
+    floor = _fp32_score_floor(geo, ref, T, data["q"], Hq, exp)
+    log("row rel err", err, "floor", floor)
+    assert err <= ATOL_ROW_REL + 2 * floor

@@ -68,10 +68,14 @@ def measured_traffic(workload: str):
         return None
 
 
+def uses_mfma(w) -> bool:
+    """The library's routing: matrix cores for GQA groups of 4 and 8 with
+    2/4-bit codes and no side tables, the VALU kernel otherwise."""
+    return w.gqa in (4, 8) and w.bits in (2, 4) and not w.outliers
+
+
 def attn_kernel_name(w) -> str:
-    """The split-K kernel the library picks: matrix cores for GQA groups of
-    4 and 8 with 2/4-bit codes, the VALU kernel otherwise."""
-    return "k_attn_mfma" if w.gqa in (4, 8) and w.bits != 8 else "k_attn_valu"
+    return "k_attn_mfma" if uses_mfma(w) else "k_attn_valu"
 
 
 def log(*a):
@@ -102,6 +106,8 @@ def algorithmic_bytes(w, T: int) -> int:
     D, b = w.head_dim, w.bits
     eb = 4 if w.dtype == "f32" else 2
     per_head = (2 * nq * D * b // 8 + ng * D * 8 + nq * 8 + 2 * (ns + nr) * D * eb)
+    if w.outliers:   # side tables: position byte and value per key group channel and value token
+        per_head += (ng * D + nq) * (1 + eb)
     return per_head * w.batch * w.n_kv_heads
 
 
@@ -116,6 +122,8 @@ def prefill_bytes(w, T: int, qcap: int) -> int:
     eb = 4 if w.dtype == "f32" else 2
     per_head = (2 * (ns + Q + nr) * D * eb + 2 * Q * D * b // 8 + (Q // w.group) * D * 8 + Q * 8
                 + 2 * (ns + nr) * D * eb)
+    if w.outliers:
+        per_head += ((Q // w.group) * D + Q) * (1 + eb)
     return per_head * w.batch * w.n_kv_heads
 
 
@@ -126,7 +134,7 @@ def decode_splits(w, T: int, cus: int, ws_splits: int = 1024) -> int:
     byte count."""
     ns, Q, nr = partition(T, w.sink, w.residual, w.group)
     n_fp = ns + nr
-    if w.gqa in (4, 8) and w.bits != 8 and Q > 0:
+    if uses_mfma(w) and Q > 0:
         nblk = -(-Q // 64) - window_start(w, T) // 64
         want = max(1, 2 * cus // (w.batch * w.n_kv_heads))
         want = min(want, nblk, ws_splits)
@@ -147,9 +155,10 @@ def cpu_baseline(w, data, sample_seconds: float):
 
     T = w.n_tokens
     geo = O.CacheGeometry(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink,
-                          w.residual, w.capacity, w.dtype, w.window)
+                          w.residual, w.capacity, w.dtype, w.window, w.outliers)
     geo1 = O.CacheGeometry(w.batch, 1, w.head_dim, w.bits, w.group, w.sink, w.residual,
-                           T + max(w.steps, 2 * w.group + w.residual + 1), w.dtype, w.window)
+                           T + max(w.steps, 2 * w.group + w.residual + 1), w.dtype, w.window,
+                           w.outliers)
     g = w.gqa
     rows = [(0, h) for h in range(g)]          # the q heads of KV head 0
     with threadpool_limits(limits=1):
@@ -246,7 +255,7 @@ def main():
     data = synth.generate(w, steps=n_gen)
     log(f"inputs generated in {time.time() - t0:.1f}s")
     cfg = kvq.Config(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink, w.residual,
-                     w.n_tokens + steps_cap, w.dtype, w.window)
+                     w.n_tokens + steps_cap, w.dtype, w.window, w.outliers)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def dev(a):
@@ -420,11 +429,12 @@ def main():
             "workload": f"{w.name}: layer B{w.batch} Hq{w.n_q_heads} Hkv{w.n_kv_heads} "
                         f"D{w.head_dim} T{w.n_tokens}{'+decode' if streaming else ''} {w.dtype} "
                         f"inputs int{w.bits} G{w.group} R{w.residual} S{w.sink}"
-                        + (f" window {w.window}" if w.window else ""),
+                        + (f" window {w.window}" if w.window else "")
+                        + (" outlier side tables" if w.outliers else ""),
             "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "cached_tokens": w.n_tokens, "bits": w.bits,
             "group": w.group, "residual": w.residual, "sink": w.sink, "input_dtype": w.dtype,
-            "window": w.window,
+            "window": w.window, "outliers": w.outliers,
             "step": ("append + decode attention, one layer" if streaming
                      else "decode attention, one layer"),
         },

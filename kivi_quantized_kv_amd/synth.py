@@ -43,6 +43,7 @@ class Workload:
     steps: int             # streaming decode steps (append + attention)
     seed: int
     window: int = 0        # sliding window in tokens (0: attend to everything)
+    outliers: int = 0      # 1: dense-and-sparse side tables
 
     @property
     def gqa(self) -> int:
@@ -67,6 +68,13 @@ WORKLOADS = {
     # bounded ring store, 64 streaming steps through evictions
     "mistral_swa": Workload("mistral_swa", 4, 32, 8, 128, 32768, "bf16", 2, 32, 128, 4, 3, 20.0, 64, 6000,
                             window=4096),
+    # the 70B-shaped layer at 3-bit codes (codes straddle bytes), and with
+    # dense-and-sparse side tables (one exact entry per key group channel
+    # and per value token)
+    "llama70b_3bit": Workload("llama70b_3bit", 1, 64, 8, 128, 131072, "bf16", 3, 64, 128, 4, 4, 30.0, 128,
+                              7000),
+    "llama70b_outliers": Workload("llama70b_outliers", 1, 64, 8, 128, 131072, "bf16", 4, 64, 128, 4, 4,
+                                  30.0, 128, 8000, outliers=1),
 }
 
 

@@ -489,7 +489,7 @@ def test_workspace_needs_no_initialization(fill):
 def _workload(name):
     w = synth.WORKLOADS[name]
     cfg_kw = _cfg_kw(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink, w.residual,
-                     w.capacity, w.dtype, w.window)
+                     w.capacity, w.dtype, w.window, outliers=w.outliers)
     return w, cfg_kw
 
 

@@ -77,6 +77,20 @@ of outlier values kept in a sparse fp16 side table), readings:
   O5 reconstruction: the kept entry takes its exact value, every other
      entry its dense dequantization.
 
+Pre-RoPE keys ([GUIDE] "KVQuant adds", first bullet: quantize keys before
+the rotary position embedding, which otherwise mixes channel pairs and
+smears the per-channel structure), readings:
+  P1 the rotation pairs channel i with channel i + D/2 (i < D/2) at
+     frequency theta_i = base^(-2i/D): x_i' = x_i cos(p theta_i) -
+     x_{i+D/2} sin(p theta_i), x_{i+D/2}' = x_{i+D/2} cos(p theta_i) + x_i
+     sin(p theta_i).
+  P2 cached token t sits at position p = t (its index in the sequence).
+  P3 with a RoPE base set, the cache stores keys as given (before the
+     rotation): sinks, residual and quantized alike; the query passed to
+     decode is already rotated to its own position; attention rotates each
+     (dequantized) key to its position before the dot product.  Values are
+     not rotated.
+
 Every function here is pinned by tests/test_oracle_pins.py against worked
 examples, closed forms, brute force and library routines.
 """
@@ -397,7 +411,8 @@ class CacheGeometry:
     capacity is cap - S (at most W + G with a window, W2) rounded up to a
     multiple of max(64, G)."""
 
-    def __init__(self, B, Hkv, D, bits, G, S, R, capacity, dtype, window=0, outliers=0):
+    def __init__(self, B, Hkv, D, bits, G, S, R, capacity, dtype, window=0, outliers=0,
+                 rope_base=0.0):
         assert bits in SUPPORTED_BITS
         assert window == 0 or window >= R + G
         assert outliers in (0, 1)
@@ -405,6 +420,8 @@ class CacheGeometry:
         self.G, self.S, self.R, self.capacity, self.dtype = G, S, R, capacity, dtype
         self.window = window
         self.outliers = outliers
+        assert rope_base >= 0
+        self.rope_base = float(rope_base)
         step = max(64, G)
         qcap = max(0, capacity - S)
         if window:
@@ -572,6 +589,35 @@ def window_start(geo: CacheGeometry, T: int) -> int:
 
 
 # ----------------------------------------------------------------------------
+# rotary position embedding of the keys (P1-P3)
+# ----------------------------------------------------------------------------
+def rope_angles(positions, D: int, base: float) -> np.ndarray:
+    """Angles p * theta_i, theta_i = base^(-2i/D), fp64 [n, D/2] (P1)."""
+    i = np.arange(D // 2, dtype=np.float64)
+    theta = np.power(np.float64(base), -2.0 * i / D)
+    return np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+
+
+def apply_rope(x: np.ndarray, positions, base: float) -> np.ndarray:
+    """Rotate x [..., n, D] (fp64) token by token to its position (P1)."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    ang = rope_angles(positions, D, base)
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :D // 2], x[..., D // 2:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def attended_positions(geo: CacheGeometry, T: int) -> np.ndarray:
+    """Positions (token indices, P2) of the tokens dequant_cache returns,
+    in its order: the sinks, the attended quantized tokens, the residual
+    tokens."""
+    ns, Q, nr = partition(T, geo.S, geo.R, geo.G)
+    u_lo = window_start(geo, T)
+    return np.concatenate([np.arange(ns), geo.S + np.arange(u_lo, Q), np.arange(geo.S + Q, T)])
+
+
+# ----------------------------------------------------------------------------
 # step 5: dequantize in fp64 ([GUIDE] step 5: dequantized group by group)
 # ----------------------------------------------------------------------------
 def dequant_cache(geo: CacheGeometry, st: dict, T: int, heads=None):
@@ -651,6 +697,8 @@ def decode(geo: CacheGeometry, st: dict, T: int, q_stored: np.ndarray,
     g = Hq // geo.Hkv
     if rows is None:
         Kh, Vh = dequant_cache(geo, st, T)
+        if geo.rope_base:
+            Kh = apply_rope(Kh, attended_positions(geo, T), geo.rope_base)
         return attention(q, Kh, Vh, scale)
     out = np.full((B, Hq, D), np.nan)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
@@ -659,6 +707,8 @@ def decode(geo: CacheGeometry, st: dict, T: int, q_stored: np.ndarray,
         by_head.setdefault(hq // g, []).append((b, hq))
     for kv, lst in by_head.items():
         Kh, Vh = dequant_cache(geo, st, T, heads=[kv])
+        if geo.rope_base:
+            Kh = apply_rope(Kh, attended_positions(geo, T), geo.rope_base)
         for (b, hq) in lst:
             s = sc * (Kh[b, 0] @ q[b, hq])
             p = np.exp(s - s.max())

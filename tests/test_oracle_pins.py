@@ -742,3 +742,114 @@ def test_outliers_lift_attention_quality_on_spiky_caches(bits):
         st = O.prefill(geo, K, V, T)
         err[o] = O.row_rel_error(O.decode(geo, st, T, q, Hq), ref)
     assert err[1] < 0.7 * err[0], err
+
+
+# --------------------------------------------------------------- pre-RoPE keys
+def test_e10_rope_worked_example():
+    """P1 against hand-derived rotations of a 4-channel vector (textbook
+    values of cos and sin at 0, 1, 2, 0.01 and 0.02 radians)."""
+    g = gold("e10_rope.json")
+    x = np.array(g["x"])[None, :]
+    for c in g["cases"]:
+        out = O.apply_rope(x, [c["position"]], g["base"])[0]
+        assert np.abs(out - np.array(c["out"])).max() < 1e-12, c["position"]
+
+
+def test_rope_matches_complex_rotation_in_torch():
+    """P1 against torch's complex arithmetic: channel pair (i, i + D/2) as the
+    complex number x_i + j x_{i+D/2}, multiplied by the unit phasor of angle
+    p theta_i (torch.polar)."""
+    rng = np.random.default_rng(3)
+    D, n, base = 128, 50, 500000.0
+    x = rng.standard_normal((2, n, D))
+    pos = rng.integers(0, 200000, size=n)
+    got = O.apply_rope(x, pos, base)
+    xt = torch.from_numpy(x)
+    z = torch.complex(xt[..., :D // 2], xt[..., D // 2:])
+    theta = torch.tensor(base, dtype=torch.float64) ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+    ang = torch.from_numpy(pos.astype(np.float64))[:, None] * theta[None, :]
+    r = z * torch.polar(torch.ones_like(ang), ang)
+    ref = torch.cat([r.real, r.imag], dim=-1).numpy()
+    assert np.abs(got - ref).max() < 1e-9
+
+
+def test_rope_is_a_relative_rotation():
+    """RoPE(q, a) . RoPE(k, b) depends on b - a only, norms are kept, and
+    position 0 is the identity."""
+    rng = np.random.default_rng(4)
+    D, base = 64, 10000.0
+    q, k = rng.standard_normal((1, D)), rng.standard_normal((1, D))
+    for a, b in ((0, 5), (100, 105), (7000, 7005), (12, 3), (1012, 1003)):
+        d1 = (O.apply_rope(q, [a], base) @ O.apply_rope(k, [b], base).T).item()
+        d0 = (q @ O.apply_rope(k, [b - a], base).T).item()
+        assert abs(d1 - d0) < 1e-10
+    r = O.apply_rope(k, [987654], base)
+    assert abs(np.linalg.norm(r) - np.linalg.norm(k)) < 1e-12
+    assert np.array_equal(O.apply_rope(k, [0], base), k)
+
+
+@pytest.mark.parametrize("W", [0, 96])
+def test_rope_decode_on_full_precision_cache_is_sdpa_on_rotated_keys(W):
+    """P2, P3: with nothing quantized (and with a window), decode equals torch
+    SDPA over the cached keys rotated by torch's complex arithmetic to their
+    token index."""
+    S, R, G, D, base = 4, 64, 32, 64, 10000.0
+    T = S + R + G - 1 if W == 0 else 300
+    case = synth.random_case(5, 1, 4, 2, D, T, "f32")
+    geo = O.CacheGeometry(1, 2, D, 4, G, S, R, T, "f32", window=W, rope_base=base)
+    geo_fp = O.CacheGeometry(1, 2, D, 4, G, S, T, T, "f32", window=0, rope_base=base)   # R = T: all exact
+    idx = list(range(T)) if W == 0 else sorted(set(range(S)) | set(range(T - W, T)))
+    K = torch.from_numpy(case["K"].astype(np.float64))[:, :, idx]
+    V = torch.from_numpy(case["V"].astype(np.float64))[:, :, idx]
+    z = torch.complex(K[..., :D // 2], K[..., D // 2:])
+    theta = torch.tensor(base, dtype=torch.float64) ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+    ang = torch.tensor(idx, dtype=torch.float64)[:, None] * theta[None, :]
+    zr = z * torch.polar(torch.ones_like(ang), ang)
+    Kr = torch.cat([zr.real, zr.imag], dim=-1)
+    q = torch.from_numpy(case["q"].astype(np.float64))[:, :, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, Kr, V, enable_gqa=True)[:, :, 0].numpy()
+    if W == 0:
+        st = O.prefill(geo_fp, case["K"], case["V"], T)
+        out = O.decode(geo_fp, st, T, case["q"], 4)
+    else:
+        # the window's keys come from the quantized store too: compare
+        # against SDPA over the dequantized (pre-RoPE) window instead
+        st = O.prefill(geo, case["K"], case["V"], T)
+        Kh, Vh = O.dequant_cache(geo, st, T)
+        Kt = torch.from_numpy(Kh)
+        z = torch.complex(Kt[..., :D // 2], Kt[..., D // 2:])
+        Kr = torch.cat([(z * torch.polar(torch.ones_like(ang), ang)).real,
+                        (z * torch.polar(torch.ones_like(ang), ang)).imag], dim=-1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, Kr, torch.from_numpy(Vh), enable_gqa=True)[:, :, 0].numpy()
+        assert O.attended_positions(geo, T).tolist() == idx
+        out = O.decode(geo, st, T, case["q"], 4)
+    assert np.abs(out - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("bits,margin", [(4, 0.5), (2, 0.8)])
+def test_pre_rope_quantization_keeps_the_per_channel_structure(bits, margin):
+    """[GUIDE] KVQuant: on keys with a few channels of large, steady
+    magnitude, keys quantized before the rotation come back closer to the
+    rotated keys than keys quantized after it, on the large channels and
+    their rotation partners: the rotation turns a steady channel into one
+    that swings with position inside every group, widening its range.  At
+    4 bits by at least 2x; at 2 bits by at least 1.25x."""
+    D, G, T, base = 128, 32, 32 * 16, 10000.0
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((T, D)).astype(np.float32)       # pre-RoPE keys [T, D]
+    # large channels at pairs that turn by 0.09 .. 0.75 radian per token, so
+    # that their phase sweeps a wide arc within each 32-token group
+    big = np.array([2, 5, 11, 64 + 17])
+    K[:, big] += np.float32(20) * np.array([1, -1, 1, -1], np.float32)
+    pos = np.arange(T)
+    K_post = O.apply_rope(K, pos, base).astype(np.float32)  # what a post-RoPE cache stores
+    kc, kd, kz = O.quantize_keys_per_channel(K, G, bits)
+    pre_deq = (kc.reshape(T // G, G, D) * kd[:, None].astype(np.float64) + kz[:, None]).reshape(T, D)
+    pre_hat = O.apply_rope(pre_deq, pos, base)
+    pc, pd, pz = O.quantize_keys_per_channel(K_post, G, bits)
+    post_hat = (pc.reshape(T // G, G, D) * pd[:, None].astype(np.float64) + pz[:, None]).reshape(T, D)
+    aff = sorted(set(big.tolist()) | set(((big + D // 2) % D).tolist()))
+    e_pre = np.abs(pre_hat - K_post)[:, aff].mean()
+    e_post = np.abs(post_hat - K_post)[:, aff].mean()
+    assert e_pre <= margin * e_post, (e_pre, e_post)

@@ -58,6 +58,16 @@
  *    one too, is coded with them (the kept one's code clamps to 2^b - 1
  *    or 0, so its dense value is zp + delta (2^b - 1) if it is >= zp,
  *    else zp).  Attention reads the kept entry at its exact value.
+ *  - Pre-RoPE keys (pigeon guide "KV-cache quantization", KVQuant adds,
+ *    first bullet: keys quantized before the rotary position embedding,
+ *    which would otherwise mix channel pairs and smear the per-channel
+ *    structure), with rope_base > 0: the cache holds keys as given, before
+ *    the rotation; decode rotates each dequantized (or exact) key to its
+ *    position, the token index t: channel i pairs with channel i + D/2 at
+ *    frequency theta_i = rope_base^(-2i/D), k_i' = k_i cos(t theta_i) -
+ *    k_{i+D/2} sin(t theta_i), k_{i+D/2}' = k_{i+D/2} cos(t theta_i) + k_i
+ *    sin(t theta_i).  The query is passed already rotated to its own
+ *    position; values are not rotated.
  *
  * Conventions for every entry point:
  *  - All pointers except `cfg`, `cache` (the structs themselves) are
@@ -112,6 +122,8 @@ typedef struct {
   int64_t window;     /* W: sliding window in tokens, 0 = none (below)  */
   int32_t outliers;   /* 1: keep one exact entry per quantization       */
                       /*    vector in side tables (above); 0: none       */
+  float rope_base;    /* > 0: keys are stored before RoPE of this base  */
+                      /*    and rotated in decode (above); 0: none       */
 } kvq_config;
 
 /*

@@ -51,6 +51,7 @@ kvq_status check_config(const kvq_config* c) {
   // a window holds at least the full-precision tokens
   if (c->window < 0 || (c->window > 0 && c->window < int64_t(c->residual) + c->group)) return KVQ_EINVAL;
   if (c->outliers != 0 && c->outliers != 1) return KVQ_EINVAL;
+  if (!(c->rope_base >= 0.0f) || std::isinf(c->rope_base)) return KVQ_EINVAL;
   return KVQ_OK;
 }
 
@@ -138,13 +139,26 @@ template <int DT, int D, int BITS> struct AttnMfma8Fn {
     else return launch_attn_mfma<DT, D, BITS, 8>(a, B, s);
   }
 };
+// VALU kernel modes: bit 0 side tables, bit 1 pre-RoPE keys
 template <int DT, int D, int BITS> struct AttnValuFn {
   static hipError_t run(const AttnArgs& a, int B, hipStream_t s) {
-    return launch_attn_valu<DT, D, BITS>(a, B, s);
+    switch ((a.outliers ? 1 : 0) | (a.rope ? 2 : 0)) {
+      case 0: return launch_attn_valu<DT, D, BITS, 0>(a, B, s);
+      case 1: return launch_attn_valu<DT, D, BITS, 1>(a, B, s);
+      case 2: return launch_attn_valu<DT, D, BITS, 2>(a, B, s);
+      default: return launch_attn_valu<DT, D, BITS, 3>(a, B, s);
+    }
   }
 };
 template <int DT, int D, int BITS> struct AttnValuOccFn {
-  static int run() { return attn_valu_blocks_per_cu<DT, D, BITS>(); }
+  static int run(int mode) {
+    switch (mode) {
+      case 0: return attn_valu_blocks_per_cu<DT, D, BITS, 0>();
+      case 1: return attn_valu_blocks_per_cu<DT, D, BITS, 1>();
+      case 2: return attn_valu_blocks_per_cu<DT, D, BITS, 2>();
+      default: return attn_valu_blocks_per_cu<DT, D, BITS, 3>();
+    }
+  }
 };
 template <int DT, int D, int BITS> struct AttnValuDirectOkFn {
   static bool run() { return attn_valu_direct_ok<DT, D, BITS>(); }
@@ -291,14 +305,16 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
 
   // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit
   // codes, once at least one token is quantized (its chunk loads assume a
-  // chunk 0), for caches without side tables.  It works per KV head on 64-token chunks, with the grid sized
+  // chunk 0), for caches without side tables or pre-RoPE keys.  It works per KV head on 64-token chunks, with the grid sized
   // to one round of two workgroups per CU, and spreads the full-precision
   // tokens evenly over its splits.  Everything else runs the VALU kernel
   // per query head on value-code blocks, again with the full-precision
   // tokens spread evenly over the splits.
   const int gqa = n_q_heads / H;
+  const bool rope = cfg->rope_base > 0.0f;
+  const int valu_mode = (cfg->outliers ? 1 : 0) | (rope ? 2 : 0);
   const bool mfma = (gqa == 4 || gqa == 8) && (cfg->bits == 2 || cfg->bits == 4) && Q > 0 &&
-                    !cfg->outliers;
+                    valu_mode == 0;
   const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
   const int64_t qcap = kvq_qcap(cfg);
   // sliding window: quantized tokens before u_lo are not attended; the
@@ -325,7 +341,7 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
     if (n_split < want_fp) n_split = want_fp;
     if (n_split < 1) n_split = 1;
     fp_per_split = (n_fp + n_split - 1) / n_split;
-  } else if (direct_rows(int64_t(B) * n_q_heads) && !cfg->outliers && dispatch3<AttnValuDirectOkFn>(cfg)) {
+  } else if (direct_rows(int64_t(B) * n_q_heads) && valu_mode == 0 && dispatch3<AttnValuDirectOkFn>(cfg)) {
     // the rows alone fill the GPU: one 16-wave workgroup per row takes
     // all of its tokens, merges in LDS and writes the output
     direct = true;
@@ -334,7 +350,7 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
     fp_per_split = n_fp > 0 ? n_fp : 1;
   } else {
     // one round of resident workgroups, at least one block per wave
-    const int64_t slots = int64_t(dispatch3<AttnValuOccFn>(cfg)) * device_cu_count();
+    const int64_t slots = int64_t(dispatch3<AttnValuOccFn>(cfg, valu_mode)) * device_cu_count();
     const int64_t rows = int64_t(B) * n_q_heads;
     int64_t want = slots / rows > 0 ? slots / rows : 1;
     if (want > (nblk + 3) / 4) want = (nblk + 3) / 4;
@@ -375,6 +391,8 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
   a.cw = a.ncap > 0 ? c0 / a.ncap * a.ncap : 0;
   a.lo_off = int(u_lo - c0 * L);
   a.outliers = cfg->outliers;
+  a.rope = rope ? 1 : 0;
+  a.rope_log2_base = rope ? std::log2(double(cfg->rope_base)) : 0.0;
   a.k_oidx = cache->k_oidx; a.k_oval = cache->k_oval;
   a.v_oidx = cache->v_oidx; a.v_oval = cache->v_oval;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -238,17 +238,28 @@ constexpr int valu_waves_per_simd() {
   return (field_codes<BITS>() && (D == 64 || (BITS == 4 && DT == DT_F16))) ? 4 : 3;
 }
 
-// OUTL: caches with side tables (three waves per SIMD, two for fp32 rows
-// of 128 channels).
-template <int DT, int D, int BITS, bool OUTL>
+// MODE: bit 0 caches with side tables, bit 1 pre-RoPE keys (three waves
+// per SIMD; two for fp32 rows of 128 channels, and for pre-RoPE keys of 128
+// channels, whose unrolled pair loop needs the registers).
+constexpr int kModeOutliers = 1, kModeRope = 2;
+template <int DT, int D, int BITS, int MODE>
 constexpr int valu_waves() {
-  if constexpr (OUTL) return (DT == DT_F32 && D == 128) ? 2 : 3;
+  if constexpr (MODE != 0) return ((DT == DT_F32 || (MODE & kModeRope)) && D == 128) ? 2 : 3;
   else return valu_waves_per_simd<DT, D, BITS>();
 }
 
-template <int DT, int D, int BITS, int NW, bool OUTL>
-__global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OUTL>())) void k_attn_valu(
+// Revolutions x in [0, 1) -> sin(2 pi x), cos(2 pi x) (the hardware
+// transcendental units take revolutions).
+__device__ __forceinline__ void sincos_rev(float x, float& sn, float& cs) {
+  sn = __builtin_amdgcn_sinf(x);
+  cs = __builtin_amdgcn_cosf(x);
+}
+
+template <int DT, int D, int BITS, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, MODE>())) void k_attn_valu(
     AttnArgs a) {
+  constexpr bool OUTL = (MODE & kModeOutliers) != 0;
+  constexpr bool ROPE = (MODE & kModeRope) != 0;
   using VL = VLayout<BITS>;
   using WS = WordShape<BITS>;
   constexpr bool kFields = field_codes<BITS>();
@@ -286,9 +297,26 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OU
   __shared__ float s_kc[NW][kHalves * 32];
   __shared__ float s_vc[NW][D];
   constexpr bool outl = OUTL;
+  // pre-RoPE keys: per frequency i < D/2 the rate C_i = theta_i / (2 pi) in
+  // revolutions per token (fp64, and rounded to fp32), and per wave the
+  // fraction of a revolution at its current block's first token; per wave
+  // and key-group half the delta and zero point of every channel
+  __shared__ double s_cd[ROPE ? D / 2 : 1];
+  __shared__ float s_c[ROPE ? D / 2 : 1];
+  __shared__ float s_fb[ROPE ? NW : 1][ROPE ? D / 2 : 1];
+  __shared__ float s_dz[ROPE ? NW : 1][ROPE ? kHalves : 1][2][ROPE ? D : 1];
 
   for (int d = threadIdx.x; d < D; d += kThreads)
     s_q[d] = load1<DT>(a.q, b * a.q_sb + hq * a.q_sh + d) * a.sm_scale_log2;
+  if constexpr (ROPE) {
+    for (int i = threadIdx.x; i < D / 2; i += kThreads) {
+      // theta_i = base^(-2i/D) (P1)
+      const double c = exp2(-2.0 * double(i) / double(D) * a.rope_log2_base) *
+                       0.15915494309189535;
+      s_cd[i] = c;
+      s_c[i] = float(c);
+    }
+  }
   if constexpr (outl) {
     for (int i = threadIdx.x; i < NW * kHalves * 32; i += kThreads) (&s_kc[0][0])[i] = 0.f;
     for (int i = threadIdx.x; i < NW * D; i += kThreads) (&s_vc[0][0])[i] = 0.f;
@@ -339,6 +367,25 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OU
     sq_w[c] = s_q[ch];
     xs_w[c] = s_q[ch] * code_field_scale<BITS>(ch);
   }
+  // Pre-RoPE keys: lane quarter qt pairs with quarter qt ^ 2 (channel i with
+  // i + D/2).  At step m2 a lane holds its channels 2 m2 and 2 m2 + 1;
+  // lanes of the low half take the pair of channel 2 m2, lanes of the high
+  // half that of their channel 2 m2 + 1, each receiving the partner's key
+  // by a quad swap.  rope_pair returns A = q_i k_i + q_i' k_i' and sets B =
+  // q_i' k_i - q_i k_i', so that the pair adds cos A + sin B to the score.
+  const bool rp_hi = qt >= 2;
+  const int rp_own = qt * kQuarterCh;                            // first own channel
+  const int rp_par = rp_hi ? rp_own - D / 2 : rp_own + D / 2;    // its partner
+  auto fr_index = [&](int m2) { return (rp_hi ? rp_own - D / 2 : rp_own) + 2 * m2 + (rp_hi ? 1 : 0); };
+  auto rope_pair = [&](float k0, float k1, int m2, float& bb) {
+    const float par = dpp_mov<kQuadXor2>(rp_hi ? k0 : k1);
+    const float own = rp_hi ? k1 : k0;
+    const int j = 2 * m2 + (rp_hi ? 1 : 0);
+    const float qo = s_q[rp_own + j], qp = s_q[rp_par + j];
+    const float cross = __builtin_fmaf(qp, own, -qo * par);
+    bb = rp_hi ? -cross : cross;
+    return __builtin_fmaf(qo, own, qp * par);
+  };
   // exponent of this lane's score token's value code field
   const int fsh = (!kFields || BITS == 8) ? 0 : -BITS * (tl % (8 / (kFields ? BITS : 8)));
   // value exponent; before any delta is seen the threshold 2^(7 - vexp) is
@@ -445,8 +492,23 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OU
         float kr[kQuarterCh];
         load_row_run<DT, kQuarterCh>(sk ? a.k_sink : a.k_resid, ko + qt * kQuarterCh, kr);
         float dot = 0.f;
+        if constexpr (ROPE) {
+          // the token's position (its index) and the key rotated to it
+          const int64_t pos = ik < a.n_sink ? ik : a.first_resid + (ik - a.n_sink);
 #pragma unroll
-        for (int j = 0; j < kQuarterCh; ++j) dot = __builtin_fmaf(kr[j], s_q[qt * kQuarterCh + j], dot);
+          for (int m2 = 0; m2 < kQuarterCh / 2; ++m2) {
+            float fr;
+            const float pr = rope_pair(kr[2 * m2], kr[2 * m2 + 1], m2, fr);
+            const double x = double(pos) * s_cd[fr_index(m2)];
+            const float rev = float(x - __builtin_floor(x));
+            float sn, cs;
+            sincos_rev(rev, sn, cs);
+            dot = __builtin_fmaf(cs, pr, __builtin_fmaf(sn, fr, dot));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < kQuarterCh; ++j) dot = __builtin_fmaf(kr[j], s_q[qt * kQuarterCh + j], dot);
+        }
         // value rows of the tile's tokens, channels lane*kWC ..
         float vr[16][kWC];
 #pragma unroll
@@ -476,17 +538,29 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OU
     const int64_t base = (a.c0 + blk) * VL::L;   // quantized index of the block's first token
     const int nvalid = int(a.Q - base < VL::L ? a.Q - base : VL::L);
     const int lo = blk == 0 ? a.lo_off : 0;      // tokens before the window
-    // key-group coefficients of each 32-token half
+    // key-group coefficients of each 32-token half (pre-RoPE keys: the
+    // deltas and zero points themselves, and the block's angle base)
     float kap[kHalves];
 #pragma unroll
     for (int k = 0; k < kHalves; ++k) {
       float kp = 0.f;
 #pragma unroll
       for (int c = 0; c < kWC; ++c) {
-        s_x[wave][k][lane * kWC + c] = xs_w[c] * r.ks[k][c];
-        kp = __builtin_fmaf(sq_w[c], r.kz[k][c], kp);
+        if constexpr (ROPE) {
+          s_dz[wave][k][0][lane * kWC + c] = r.ks[k][c];
+          s_dz[wave][k][1][lane * kWC + c] = r.kz[k][c];
+        } else {
+          s_x[wave][k][lane * kWC + c] = xs_w[c] * r.ks[k][c];
+          kp = __builtin_fmaf(sq_w[c], r.kz[k][c], kp);
+        }
       }
-      kap[k] = wave_sum_valu(kp);
+      kap[k] = ROPE ? 0.f : wave_sum_valu(kp);
+    }
+    if constexpr (ROPE) {
+      if (lane < D / 2) {   // revolutions at the block's first token, position S + base
+        const double x = double(a.S + base) * s_cd[lane];
+        s_fb[wave][lane] = float(x - __builtin_floor(x));
+      }
     }
     wave_lds_sync();
     if constexpr (outl) {
@@ -507,7 +581,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OU
           if (j >= 0 && j < 32) {
             const float xv = load1<DT>(a.k_oval, gi + ch);
             const float dense = xv < r.kz[k][c] ? r.kz[k][c] : __builtin_fmaf(kLev, r.ks[k][c], r.kz[k][c]);
-            atomicAdd(&s_kc[wave][k * 32 + j], sq_w[c] * (xv - dense));
+            float qe = sq_w[c];
+            if constexpr (ROPE) {
+              // the query rotated back by the token's angle, channel ch
+              const int fi = ch & (D / 2 - 1);
+              float rev = __builtin_fmaf(float(k * 32 + j), s_c[fi], s_fb[wave][fi]);
+              rev -= __builtin_floorf(rev);
+              float sn, cs;
+              sincos_rev(rev, sn, cs);
+              const float qp = s_q[ch ^ (D / 2)];
+              qe = __builtin_fmaf(sq_w[c], cs, (ch < D / 2 ? qp : -qp) * sn);
+            }
+            atomicAdd(&s_kc[wave][k * 32 + j], qe * (xv - dense));
           }
         }
       }
@@ -518,7 +603,32 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OU
 #pragma unroll
     for (int k = 0; k < kHalves; ++k) {
       float dot[2] = {0.f, 0.f};
-      if constexpr (kFields) {
+      if constexpr (ROPE) {
+        // dequantized pairs rotated to their positions: token st*16 + tl
+        // of the block turns its pair by its offset times C_i past the
+        // block's base
+#pragma unroll
+        for (int m2 = 0; m2 < kQuarterCh / 2; ++m2) {
+          const int c0 = rp_own + 2 * m2;
+          const float d0 = s_dz[wave][k][0][c0], z0 = s_dz[wave][k][1][c0];
+          const float d1 = s_dz[wave][k][0][c0 + 1], z1 = s_dz[wave][k][1][c0 + 1];
+          const int fi = fr_index(m2);
+          const float ci = s_c[fi], fb = s_fb[wave][fi];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int st = 2 * k + u;
+            const float k0 = __builtin_fmaf(stream_code<BITS>(r.kw[st], (2 * m2) * BITS), d0, z0);
+            const float k1 = __builtin_fmaf(stream_code<BITS>(r.kw[st], (2 * m2 + 1) * BITS), d1, z1);
+            float bb;
+            const float aa = rope_pair(k0, k1, m2, bb);
+            float rev = __builtin_fmaf(float(st * 16 + tl), ci, fb);
+            rev -= __builtin_floorf(rev);
+            float sn, cs;
+            sincos_rev(rev, sn, cs);
+            dot[u] = __builtin_fmaf(cs, aa, __builtin_fmaf(sn, bb, dot[u]));
+          }
+        }
+      } else if constexpr (kFields) {
 #pragma unroll
         for (int i = 0; i < kQW; ++i) {   // one word's coefficients at a time
           float x[WS::kCPW], qc[WS::kCPW];
@@ -541,7 +651,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, OU
         // -inf past the quantized count (selected: the key parameters of a
         // group past the count are never written and may hold anything)
         const int st = 2 * k + u;
-        float v = __builtin_fmaf(quad_sum(dot[u]), kS, kap[k]);
+        float v = ROPE ? quad_sum(dot[u]) : __builtin_fmaf(quad_sum(dot[u]), kS, kap[k]);
         if constexpr (outl) v += s_kc[wave][st * 16 + tl];
         sc[st] = st * 16 + tl < nvalid && st * 16 + tl >= lo ? v : -__builtin_inff();
       }
@@ -775,11 +885,11 @@ __global__ __launch_bounds__(256) void k_merge(AttnArgs a) {
 
 // Workgroups of the VALU kernel resident per CU (its register use decides),
 // asked of the runtime once per instantiation.
-template <int DT, int D, int BITS>
+template <int DT, int D, int BITS, int MODE>
 int attn_valu_blocks_per_cu() {
   static const int n = [] {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_valu<DT, D, BITS, 4, false>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_valu<DT, D, BITS, 4, MODE>, 256, 0) != hipSuccess ||
         v < 1)
       v = 1;
     return v;
@@ -787,27 +897,24 @@ int attn_valu_blocks_per_cu() {
   return n;
 }
 // Whether the one-split form (16 waves, output written directly) exists for
-// this instantiation: it needs the kernel to fit four waves per SIMD.
+// this instantiation: it needs the kernel to fit four waves per SIMD (plain
+// caches only).
 template <int DT, int D, int BITS>
 bool attn_valu_direct_ok() {
   return valu_waves_per_simd<DT, D, BITS>() == 4;
 }
 
-template <int DT, int D, int BITS>
+template <int DT, int D, int BITS, int MODE>
 hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s) {
   if (a.n_split == 1 && a.direct) {
-    if constexpr (valu_waves_per_simd<DT, D, BITS>() == 4) {
-      if (a.outliers) return hipErrorInvalidValue;   // the direct form has no side-table variant
-      hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 16, false>), dim3(1, a.Hq, B), dim3(1024), 0, s, a);
+    if constexpr (MODE == 0 && valu_waves_per_simd<DT, D, BITS>() == 4) {
+      hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 16, 0>), dim3(1, a.Hq, B), dim3(1024), 0, s, a);
       return hipGetLastError();
     } else {
       return hipErrorInvalidValue;
     }
   }
-  if (a.outliers)
-    hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 4, true>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 4, false>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 4, MODE>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <int DT, int D>

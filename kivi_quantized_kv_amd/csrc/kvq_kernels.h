@@ -83,6 +83,9 @@ struct AttnArgs {
   const uint8_t *k_oidx, *v_oidx;
   const void *k_oval, *v_oval;
   int outliers;
+  // Pre-RoPE keys (rope != 0): log2 of the rotation base.
+  double rope_log2_base;
+  int rope;
 };
 
 __device__ __forceinline__ float* partial_o(const AttnArgs& a, int64_t row, int split, int D) {
@@ -100,9 +103,10 @@ template <int DT, int D>
 hipError_t launch_copy_fp(const FpCopyArgs& a, int64_t n_rows, int B, int H, hipStream_t s);
 template <int DT, int D, int BITS>
 hipError_t launch_append(const AppendArgs& a, int B, int H, hipStream_t s);
-template <int DT, int D, int BITS>
+// MODE bit 0: side tables; bit 1: pre-RoPE keys.
+template <int DT, int D, int BITS, int MODE>
 hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s);
-template <int DT, int D, int BITS>
+template <int DT, int D, int BITS, int MODE>
 int attn_valu_blocks_per_cu();
 template <int DT, int D, int BITS>
 bool attn_valu_direct_ok();

@@ -38,7 +38,7 @@ class c_config(ctypes.Structure):
                 ("group", ctypes.c_int32), ("sink", ctypes.c_int32),
                 ("residual", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("capacity", ctypes.c_int64), ("window", ctypes.c_int64),
-                ("outliers", ctypes.c_int32)]
+                ("outliers", ctypes.c_int32), ("rope_base", ctypes.c_float)]
 
 
 class c_cache(ctypes.Structure):
@@ -95,12 +95,13 @@ class Config:
     dtype: str = "bf16"
     window: int = 0          # sliding window in tokens, 0 = none
     outliers: int = 0        # 1: one exact entry per quantization vector in side tables
+    rope_base: float = 0.0   # > 0: keys stored before RoPE of this base, rotated in decode
 
     def c(self) -> c_config:
         """A new kvq_config struct of these fields."""
         return c_config(self.batch, self.n_kv_heads, self.head_dim, self.bits, self.group,
                         self.sink, self.residual, DTYPE_CODE[self.dtype], self.capacity,
-                        self.window, self.outliers)
+                        self.window, self.outliers, self.rope_base)
 
     def _cref(self):
         """Pointer to this config's struct, built once (the dataclass is frozen)."""

@@ -32,7 +32,7 @@ def make(cfg_kw):
     cfg = kvq.Config(**cfg_kw)
     geo = O.CacheGeometry(cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.bits, cfg.group,
                           cfg.sink, cfg.residual, cfg.capacity, cfg.dtype, cfg.window,
-                          cfg.outliers)
+                          cfg.outliers, cfg.rope_base)
     return cfg, geo
 
 

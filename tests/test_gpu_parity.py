@@ -621,3 +621,64 @@ def test_outlier_side_tables_on_edge_values(kind):
     floor = _fp32_score_floor(geo, ref, T, data["q"], Hq, exp)
     log("row rel err", err, "floor", floor)
     assert err <= ATOL_ROW_REL + 2 * floor
+
+
+# Pre-RoPE keys: the cache holds keys before the rotation, decode rotates
+# each dequantized key to its token index (VALU kernel, every width).
+ROPE = [
+    # B, Hq, Hkv, D, bits, G, S, R, T, dtype, base, outliers, window
+    (1, 4, 2, 64, 4, 32, 4, 32, 333, "f16", 10000.0, 0, 0),
+    (2, 8, 2, 128, 2, 64, 2, 64, 700, "bf16", 500000.0, 0, 0),     # GQA 4, 2-bit (64-token blocks)
+    (1, 8, 1, 128, 4, 32, 4, 128, 1500, "bf16", 500000.0, 0, 0),   # GQA 8
+    (1, 2, 2, 64, 8, 128, 0, 0, 520, "f32", 10000.0, 0, 0),
+    (1, 4, 1, 128, 3, 32, 3, 32, 611, "f16", 10000.0, 0, 0),       # bit-stream width
+    (1, 2, 1, 128, 4, 32, 4, 32, 400, "f32", 10000.0, 1, 0),       # with side tables
+    (1, 4, 2, 64, 2, 32, 4, 32, 900, "bf16", 10000.0, 1, 192),     # side tables and a window
+    (1, 8, 2, 128, 5, 64, 4, 64, 800, "bf16", 1000000.0, 0, 256),  # window
+]
+
+
+@pytest.mark.parametrize("case", ROPE, ids=lambda c: "-".join(map(str, c)))
+def test_pre_rope_keys_prefill_streaming_and_attention(case):
+    """[pigeon guide 'KV-cache quantization', KVQuant adds] keys stored
+    before RoPE: the stored state bit-exact (it is the plain state), and
+    attention with every key rotated to its position within 2e-3 of the
+    oracle after the prefill and across 70 appends."""
+    kvq = _kvq()
+    B, Hq, Hkv, D, bits, G, S, R, T, dt, base, outl, W = case
+    log("rope", case)
+    steps = 70
+    data = synth.spiky_case(53 + sum(case[:9]), B, Hq, Hkv, D, T + steps, dt) if outl else \
+        synth.random_case(53 + sum(case[:9]), B, Hq, Hkv, D, T + steps, dt)
+    cfg, geo = make(dict(_cfg_kw(B, Hkv, D, bits, G, S, R, T + steps, dt, window=W, outliers=outl),
+                         rope_base=base))
+    cache = kvq.Cache(cfg, fill=0xFF)
+    Kd, Vd, qd = to_dev(data["K"], dt), to_dev(data["V"], dt), to_dev(data["q"], dt)
+    kvq.prefill(cfg, cache, Kd, Vd, T)
+    torch.cuda.synchronize()
+    st = O.prefill(geo, data["K"], data["V"], T)
+    compare_state(geo, read_state(cache), st, T)
+    out = kvq.kvq_decode_attention(cfg, cache, T, qd).cpu().numpy()
+    err = O.row_rel_error(out, O.decode(geo, st, T, data["q"], Hq))
+    log("row rel err", err)
+    assert err <= ATOL_ROW_REL
+    for n in range(T, T + steps):
+        kvq.kvq_append_token(cfg, cache, n, Kd[:, :, n], Vd[:, :, n])
+        st = O.append(geo, st, n, data["K"][:, :, n], data["V"][:, :, n])
+        if (n + 1) % 17 == 0 or n + 1 == T + steps:
+            out = kvq.kvq_decode_attention(cfg, cache, n + 1, qd).cpu().numpy()
+            err = O.row_rel_error(out, O.decode(geo, st, n + 1, data["q"], Hq))
+            assert err <= ATOL_ROW_REL, (n + 1, err)
+    compare_state(geo, read_state(cache), st, T + steps)
+
+
+def test_pre_rope_position_zero_is_the_plain_attention():
+    """With only the first token cached, its position is 0 and the rotation
+    is the identity: the output is that token's value, as without RoPE."""
+    kvq = _kvq()
+    data = synth.random_case(9, 1, 4, 2, 128, 1, "bf16")
+    cfg, geo = make(dict(_cfg_kw(1, 2, 128, 4, 32, 4, 32, 64, "bf16"), rope_base=10000.0))
+    cache = _run_prefill(kvq, cfg, data, 1)
+    out = kvq.kvq_decode_attention(cfg, cache, 1, to_dev(data["q"], "bf16")).cpu().numpy()
+    v = O.to_f32(data["V"][:, :, 0], "bf16")
+    assert np.abs(out - np.repeat(v, 2, axis=1)).max() < 1e-6

@@ -70,8 +70,9 @@ def measured_traffic(workload: str):
 
 def uses_mfma(w) -> bool:
     """The library's routing: matrix cores for GQA groups of 4 and 8 with
-    2/4-bit codes and no side tables, the VALU kernel otherwise."""
-    return w.gqa in (4, 8) and w.bits in (2, 4) and not w.outliers
+    2/4-bit codes, no side tables and no pre-RoPE keys, the VALU kernel
+    otherwise."""
+    return w.gqa in (4, 8) and w.bits in (2, 4) and not w.outliers and not w.rope_base
 
 
 def attn_kernel_name(w) -> str:
@@ -155,10 +156,10 @@ def cpu_baseline(w, data, sample_seconds: float):
 
     T = w.n_tokens
     geo = O.CacheGeometry(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink,
-                          w.residual, w.capacity, w.dtype, w.window, w.outliers)
+                          w.residual, w.capacity, w.dtype, w.window, w.outliers, w.rope_base)
     geo1 = O.CacheGeometry(w.batch, 1, w.head_dim, w.bits, w.group, w.sink, w.residual,
                            T + max(w.steps, 2 * w.group + w.residual + 1), w.dtype, w.window,
-                           w.outliers)
+                           w.outliers, w.rope_base)
     g = w.gqa
     rows = [(0, h) for h in range(g)]          # the q heads of KV head 0
     with threadpool_limits(limits=1):
@@ -255,7 +256,7 @@ def main():
     data = synth.generate(w, steps=n_gen)
     log(f"inputs generated in {time.time() - t0:.1f}s")
     cfg = kvq.Config(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink, w.residual,
-                     w.n_tokens + steps_cap, w.dtype, w.window, w.outliers)
+                     w.n_tokens + steps_cap, w.dtype, w.window, w.outliers, w.rope_base)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def dev(a):
@@ -430,11 +431,12 @@ def main():
                         f"D{w.head_dim} T{w.n_tokens}{'+decode' if streaming else ''} {w.dtype} "
                         f"inputs int{w.bits} G{w.group} R{w.residual} S{w.sink}"
                         + (f" window {w.window}" if w.window else "")
-                        + (" outlier side tables" if w.outliers else ""),
+                        + (" outlier side tables" if w.outliers else "")
+                        + (f" pre-RoPE keys (base {w.rope_base:g})" if w.rope_base else ""),
             "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "cached_tokens": w.n_tokens, "bits": w.bits,
             "group": w.group, "residual": w.residual, "sink": w.sink, "input_dtype": w.dtype,
-            "window": w.window, "outliers": w.outliers,
+            "window": w.window, "outliers": w.outliers, "rope_base": w.rope_base,
             "step": ("append + decode attention, one layer" if streaming
                      else "decode attention, one layer"),
         },

@@ -44,6 +44,7 @@ class Workload:
     seed: int
     window: int = 0        # sliding window in tokens (0: attend to everything)
     outliers: int = 0      # 1: dense-and-sparse side tables
+    rope_base: float = 0.0 # > 0: keys cached before RoPE, rotated in decode
 
     @property
     def gqa(self) -> int:
@@ -75,6 +76,10 @@ WORKLOADS = {
                               7000),
     "llama70b_outliers": Workload("llama70b_outliers", 1, 64, 8, 128, 131072, "bf16", 4, 64, 128, 4, 4,
                                   30.0, 128, 8000, outliers=1),
+    # and with keys cached before RoPE (base 500000, as the 70B-class
+    # models use), rotated inside the decode
+    "llama70b_rope": Workload("llama70b_rope", 1, 64, 8, 128, 131072, "bf16", 4, 64, 128, 4, 4, 30.0, 128,
+                              9000, rope_base=500000.0),
 }
 
 

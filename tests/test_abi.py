@@ -112,6 +112,12 @@ def test_validation_rejects_bad_arguments_without_launching():
     assert qk(bad) == 2
     bad = cfg.c(); bad.outliers = 2
     assert qk(bad) == 1
+    bad = cfg.c(); bad.rope_base = -1.0
+    assert qk(bad) == 1
+    bad = cfg.c(); bad.rope_base = float("inf")
+    assert qk(bad) == 1
+    bad = cfg.c(); bad.rope_base = float("nan")
+    assert qk(bad) == 1
     bad = cfg.c(); bad.outliers = 1           # side tables missing from the cache
     assert qk(bad) == 1
     bad = cfg.c(); bad.head_dim = 96

@@ -490,6 +490,7 @@ def _workload(name):
     w = synth.WORKLOADS[name]
     cfg_kw = _cfg_kw(w.batch, w.n_kv_heads, w.head_dim, w.bits, w.group, w.sink, w.residual,
                      w.capacity, w.dtype, w.window, outliers=w.outliers)
+    cfg_kw["rope_base"] = w.rope_base
     return w, cfg_kw
 
 

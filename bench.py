@@ -76,7 +76,9 @@ def uses_mfma(w) -> bool:
 
 
 def attn_kernel_name(w) -> str:
-    return "k_attn_mfma" if uses_mfma(w) else "k_attn_valu"
+    if uses_mfma(w):
+        return "k_attn_mfma"
+    return "k_attn_gqa" if 2 <= w.gqa <= 8 else "k_attn_valu"
 
 
 def log(*a):

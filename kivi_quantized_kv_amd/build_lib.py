@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["kvq_quant.hip", "kvq_quant_any.hip", "kvq_attn.hip", "kvq_attn_any.hip",
-           "kvq_attn_rope.hip", "kvq_attn_rope_any.hip", "kvq_mfma.hip", "kvq_api.hip"]
+           "kvq_attn_rope.hip", "kvq_attn_rope_any.hip", "kvq_gqa.hip", "kvq_gqa_outl.hip",
+           "kvq_gqa_rope.hip", "kvq_gqa_rope_outl.hip", "kvq_mfma.hip", "kvq_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

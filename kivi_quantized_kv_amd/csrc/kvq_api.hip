@@ -160,6 +160,26 @@ template <int DT, int D, int BITS> struct AttnValuOccFn {
     }
   }
 };
+template <int DT, int D, int BITS> struct AttnGqaFn {
+  static hipError_t run(const AttnArgs& a, int B, hipStream_t s) {
+    switch ((a.outliers ? 1 : 0) | (a.rope ? 2 : 0)) {
+      case 0: return launch_attn_gqa<DT, D, BITS, 0>(a, B, s);
+      case 1: return launch_attn_gqa<DT, D, BITS, 1>(a, B, s);
+      case 2: return launch_attn_gqa<DT, D, BITS, 2>(a, B, s);
+      default: return launch_attn_gqa<DT, D, BITS, 3>(a, B, s);
+    }
+  }
+};
+template <int DT, int D, int BITS> struct AttnGqaOccFn {
+  static int run(int mode) {
+    switch (mode) {
+      case 0: return attn_gqa_blocks_per_cu<DT, D, BITS, 0>();
+      case 1: return attn_gqa_blocks_per_cu<DT, D, BITS, 1>();
+      case 2: return attn_gqa_blocks_per_cu<DT, D, BITS, 2>();
+      default: return attn_gqa_blocks_per_cu<DT, D, BITS, 3>();
+    }
+  }
+};
 template <int DT, int D, int BITS> struct AttnValuDirectOkFn {
   static bool run() { return attn_valu_direct_ok<DT, D, BITS>(); }
 };
@@ -307,14 +327,18 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
   // codes, once at least one token is quantized (its chunk loads assume a
   // chunk 0), for caches without side tables or pre-RoPE keys.  It works per KV head on 64-token chunks, with the grid sized
   // to one round of two workgroups per CU, and spreads the full-precision
-  // tokens evenly over its splits.  Everything else runs the VALU kernel
-  // per query head on value-code blocks, again with the full-precision
-  // tokens spread evenly over the splits.
+  // tokens evenly over its splits.  Everything else runs a VALU kernel on
+  // value-code blocks, again with the full-precision tokens spread evenly
+  // over the splits: GQA groups of 2..8 heads the grouped one, MHA and
+  // larger groups the per-head one.
   const int gqa = n_q_heads / H;
   const bool rope = cfg->rope_base > 0.0f;
   const int valu_mode = (cfg->outliers ? 1 : 0) | (rope ? 2 : 0);
   const bool mfma = (gqa == 4 || gqa == 8) && (cfg->bits == 2 || cfg->bits == 4) && Q > 0 &&
                     valu_mode == 0;
+  // other GQA groups of 2..8 heads: the grouped VALU kernel, up to four
+  // heads per workgroup sharing each code's extraction
+  const bool grouped = !mfma && gqa >= 2 && gqa <= 8;
   const int64_t L = mfma ? 64 : (cfg->bits == 2 ? 64 : 32);
   const int64_t qcap = kvq_qcap(cfg);
   // sliding window: quantized tokens before u_lo are not attended; the
@@ -336,6 +360,21 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
     n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
     // at most ~64 exact tokens per split: splits past the chunks, if any,
     // take exact tokens only
+    int64_t want_fp = (n_fp + 63) / 64;
+    if (want_fp > cap_splits) want_fp = cap_splits;
+    if (n_split < want_fp) n_split = want_fp;
+    if (n_split < 1) n_split = 1;
+    fp_per_split = (n_fp + n_split - 1) / n_split;
+  } else if (grouped) {
+    // one round of resident workgroups over (b, KV head, head group) rows,
+    // at least one block per wave
+    const int64_t slots = int64_t(dispatch3<AttnGqaOccFn>(cfg, valu_mode)) * device_cu_count();
+    const int64_t rows = int64_t(B) * H * ((gqa + 3) / 4);
+    int64_t want = slots / rows > 0 ? slots / rows : 1;
+    if (want > (nblk + 3) / 4) want = (nblk + 3) / 4;
+    if (want > cap_splits) want = cap_splits;
+    bps = want > 0 ? (nblk + want - 1) / want : 1;
+    n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
     int64_t want_fp = (n_fp + 63) / 64;
     if (want_fp > cap_splits) want_fp = cap_splits;
     if (n_split < want_fp) n_split = want_fp;
@@ -400,6 +439,7 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
   if (a.n_split > 0) {
     if (mfma && gqa == 8) ea = dispatch3<AttnMfma8Fn>(cfg, a, B, s);
     else if (mfma) ea = dispatch3<AttnMfma4Fn>(cfg, a, B, s);
+    else if (grouped) ea = dispatch3<AttnGqaFn>(cfg, a, B, s);
     else ea = dispatch3<AttnValuFn>(cfg, a, B, s);
   }
   if (ea != hipSuccess) return KVQ_EHIP;

@@ -110,6 +110,11 @@ template <int DT, int D, int BITS, int MODE>
 int attn_valu_blocks_per_cu();
 template <int DT, int D, int BITS>
 bool attn_valu_direct_ok();
+// GQA groups of 2..8 query heads, up to four per workgroup (MODE as above).
+template <int DT, int D, int BITS, int MODE>
+hipError_t launch_attn_gqa(const AttnArgs& a, int B, hipStream_t s);
+template <int DT, int D, int BITS, int MODE>
+int attn_gqa_blocks_per_cu();
 template <int DT, int D, int BITS, int GQA>
 hipError_t launch_attn_mfma(const AttnArgs& a, int B, hipStream_t s);
 template <int DT, int D>

@@ -16,8 +16,10 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-OBJS = ["kvq_attn.o", "kvq_attn_any.o", "kvq_attn_rope.o", "kvq_attn_rope_any.o", "kvq_mfma.o",
-        "kvq_quant.o", "kvq_quant_any.o"]
+sys.path.insert(0, ROOT)
+from kivi_quantized_kv_amd import build_lib   # noqa: E402  (the list of translation units)
+
+OBJS = [os.path.splitext(f)[0] + ".o" for f in build_lib.SOURCES if f != "kvq_api.hip"]
 
 DRIVER = r'''
 import ctypes, sys

@@ -380,9 +380,13 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
     if (n_split < want_fp) n_split = want_fp;
     if (n_split < 1) n_split = 1;
     fp_per_split = (n_fp + n_split - 1) / n_split;
-  } else if (direct_rows(int64_t(B) * n_q_heads) && valu_mode == 0 && dispatch3<AttnValuDirectOkFn>(cfg)) {
-    // the rows alone fill the GPU: one 16-wave workgroup per row takes
-    // all of its tokens, merges in LDS and writes the output
+  } else if ((direct_rows(int64_t(B) * n_q_heads) || (nblk <= 16 && n_fp <= 256)) && valu_mode == 0 &&
+             dispatch3<AttnValuDirectOkFn>(cfg)) {
+    // the rows alone fill the GPU, or each row is short (at most one value
+    // block per wave; longer rows gain more from spreading over the CUs
+    // than the merge launch costs, measured at 30 blocks per row): one
+    // 16-wave workgroup per row takes all of its tokens, merges in LDS and
+    // writes the output, with no merge launch
     direct = true;
     n_split = 1;
     bps = nblk > 0 ? nblk : 1;

@@ -35,7 +35,7 @@ Readings where the pages are silent (each is listed in the design notes):
   R4 rounding is half to even (numpy.rint).
   R5 delta = fl32(fl32(max - min) / (2^b - 1)); code = rint(fl32(fl32(x - zp)
      / delta)), a true IEEE fp32 division.
-  R6 max == min gives delta = 0 and every code 0.
+  R6 max == min gives delta = +0 and every code 0.
   R7 the zero point is the fp32 minimum, stored as mn + 0.0f (so -0 -> +0).
   R8 sink and residual tokens are stored losslessly in the input dtype.
   R9 GQA: q head hq reads KV head hq // (Hq / Hkv).
@@ -160,10 +160,13 @@ def ring_slot(t: int, S: int, R: int, G: int) -> int:
 # steps 2-3: the asymmetric affine quantizer ([GUIDE] How it works, step 3)
 # ----------------------------------------------------------------------------
 def affine_params(mn: np.ndarray, mx: np.ndarray, bits: int):
-    """delta = (max - min) / (2^b - 1) and zero point = min, in fp32 (R5, R7)."""
+    """delta = (max - min) / (2^b - 1) and zero point = min, in fp32 (R5, R7);
+    delta = +0 when max = min (R6; which of -0 and +0 a min or max returns
+    among equal zeros is not fixed, their difference's sign would be)."""
     mn = np.asarray(mn, dtype=_F32)
     mx = np.asarray(mx, dtype=_F32)
     delta = (mx - mn) / _F32(2 ** bits - 1)
+    delta = np.where(mx == mn, _F32(0.0), delta)
     zp = mn + _F32(0.0)
     return delta.astype(_F32), zp.astype(_F32)
 

@@ -59,6 +59,19 @@ def test_e8_straddling_codes():
         assert O.pack_bits(codes, b)[0].tolist() == case["bytes"]
 
 
+def test_signed_zero_range_gives_positive_zero_delta():
+    """R6 with zeros of both signs: max = min numerically, so delta is +0
+    (bit pattern 0) whatever zero a min or max returns; the zero point is
+    +0 (R7) and every code 0."""
+    for x in ([-0.0, 0.0, -0.0, 0.0], [0.0, -0.0], [-0.0, -0.0, -0.0]):
+        v = np.array(x, np.float32)
+        for mn, mx in ((v.min(), v.max()), (np.float32(-0.0), np.float32(0.0)), (np.float32(0.0), np.float32(-0.0))):
+            d, z = O.affine_params(mn, mx, 4)
+            assert np.asarray(d).view(np.uint32) == 0 and np.asarray(z).view(np.uint32) == 0
+        c, d, z = O.quantize_values_per_token(v[None], 3)
+        assert c.tolist() == [[0] * len(x)] and d.view(np.uint32)[0] == 0
+
+
 def test_e3_degenerate_group():
     g = gold("e3_degenerate.json")
     x = np.array(g["x"], np.float32)

@@ -19,8 +19,11 @@ template <> struct Elem<DT_BF16> { using T = uint16_t; static constexpr int byte
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
+// Through the bf16 type rather than a bit cast: the same shift, but the
+// compiler then knows the value is canonical and adds no canonicalization
+// before min / max (the inputs are finite, so the two agree bit for bit).
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
-  return __builtin_bit_cast(float, h << 16);
+  return (float)__builtin_bit_cast(__bf16, (uint16_t)h);
 }
 
 // Four consecutive elements at element index `i` (16-byte aligned for f32,

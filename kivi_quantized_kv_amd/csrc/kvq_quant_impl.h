@@ -23,6 +23,12 @@
 
 namespace kvq {
 
+// Minimum and maximum in the IEEE 754-2019 sense (-0 below +0; the inputs
+// are finite): one gfx950 instruction each, with no canonicalization of
+// operands that come from loads, LDS or cross-lane moves.
+__device__ __forceinline__ float fmin2(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // ----------------------------------------------------------------------------
 // Row sources: the byte address of row r of the group / step being quantized.
 // ----------------------------------------------------------------------------
@@ -86,7 +92,7 @@ __device__ __forceinline__ void affine_codes(const float* x, const float* delta,
     risky |= __builtin_fabsf(y - r) >= kBand;
     // clamped: an entry kept exact in a side table lies outside the dense
     // range (an infinite or NaN y, from x - zp overflowing, clamps too)
-    c[i] = __builtin_fminf(__builtin_fmaxf(r, 0.0f), levels);
+    c[i] = fmin2(fmax2(r, 0.0f), levels);
   }
   if (__builtin_amdgcn_ballot_w64(risky) != 0) {
 #pragma unroll
@@ -102,38 +108,38 @@ __device__ __forceinline__ void affine_codes(const float* x, const float* delta,
 template <int S>
 __device__ __forceinline__ void minmax_across(float& mn, float& mx) {
   if constexpr (S <= 8) {
-    mn = __builtin_fminf(mn, dpp_mov<kRowRor8>(mn));
-    mx = __builtin_fmaxf(mx, dpp_mov<kRowRor8>(mx));
+    mn = fmin2(mn, dpp_mov<kRowRor8>(mn));
+    mx = fmax2(mx, dpp_mov<kRowRor8>(mx));
   }
   if constexpr (S <= 16) {
     float a, b;
-    partner_pair<false>(mn, a, b); mn = __builtin_fminf(a, b);
-    partner_pair<false>(mx, a, b); mx = __builtin_fmaxf(a, b);
+    partner_pair<false>(mn, a, b); mn = fmin2(a, b);
+    partner_pair<false>(mx, a, b); mx = fmax2(a, b);
   }
   float a, b;
-  partner_pair<true>(mn, a, b); mn = __builtin_fminf(a, b);
-  partner_pair<true>(mx, a, b); mx = __builtin_fmaxf(a, b);
+  partner_pair<true>(mn, a, b); mn = fmin2(a, b);
+  partner_pair<true>(mx, a, b); mx = fmax2(a, b);
 }
 
 // All-reduce of min and max over aligned runs of N consecutive lanes (N =
 // 8, 16 or 32).
 template <int N>
 __device__ __forceinline__ void minmax_run(float& mn, float& mx) {
-  mn = __builtin_fminf(mn, dpp_mov<kQuadXor1>(mn));
-  mx = __builtin_fmaxf(mx, dpp_mov<kQuadXor1>(mx));
-  mn = __builtin_fminf(mn, dpp_mov<kQuadXor2>(mn));
-  mx = __builtin_fmaxf(mx, dpp_mov<kQuadXor2>(mx));
+  mn = fmin2(mn, dpp_mov<kQuadXor1>(mn));
+  mx = fmax2(mx, dpp_mov<kQuadXor1>(mx));
+  mn = fmin2(mn, dpp_mov<kQuadXor2>(mn));
+  mx = fmax2(mx, dpp_mov<kQuadXor2>(mx));
   constexpr int kHalfMirror = 0x141, kMirror = 0x140;
-  mn = __builtin_fminf(mn, dpp_mov<kHalfMirror>(mn));   // quads of a half row meet
-  mx = __builtin_fmaxf(mx, dpp_mov<kHalfMirror>(mx));
+  mn = fmin2(mn, dpp_mov<kHalfMirror>(mn));   // quads of a half row meet
+  mx = fmax2(mx, dpp_mov<kHalfMirror>(mx));
   if constexpr (N >= 16) {
-    mn = __builtin_fminf(mn, dpp_mov<kMirror>(mn));     // halves of a row meet
-    mx = __builtin_fmaxf(mx, dpp_mov<kMirror>(mx));
+    mn = fmin2(mn, dpp_mov<kMirror>(mn));     // halves of a row meet
+    mx = fmax2(mx, dpp_mov<kMirror>(mx));
   }
   if constexpr (N >= 32) {
     float a, b;
-    partner_pair<false>(mn, a, b); mn = __builtin_fminf(a, b);
-    partner_pair<false>(mx, a, b); mx = __builtin_fmaxf(a, b);
+    partner_pair<false>(mn, a, b); mn = fmin2(a, b);
+    partner_pair<false>(mx, a, b); mx = fmax2(a, b);
   }
 }
 
@@ -149,16 +155,16 @@ struct Ext2 {
 };
 __device__ __forceinline__ Ext2 ext2_of(float x) { return {x, __builtin_inff(), x, -__builtin_inff()}; }
 __device__ __forceinline__ void ext2_add(Ext2& e, float x) {
-  e.hi2 = __builtin_fmaxf(e.hi2, __builtin_fminf(e.hi1, x));
-  e.hi1 = __builtin_fmaxf(e.hi1, x);
-  e.lo2 = __builtin_fminf(e.lo2, __builtin_fmaxf(e.lo1, x));
-  e.lo1 = __builtin_fminf(e.lo1, x);
+  e.hi2 = fmax2(e.hi2, fmin2(e.hi1, x));
+  e.hi1 = fmax2(e.hi1, x);
+  e.lo2 = fmin2(e.lo2, fmax2(e.lo1, x));
+  e.lo1 = fmin2(e.lo1, x);
 }
 __device__ __forceinline__ void ext2_merge(Ext2& e, const Ext2& o) {
-  e.hi2 = __builtin_fmaxf(__builtin_fminf(e.hi1, o.hi1), __builtin_fmaxf(e.hi2, o.hi2));
-  e.hi1 = __builtin_fmaxf(e.hi1, o.hi1);
-  e.lo2 = __builtin_fminf(__builtin_fmaxf(e.lo1, o.lo1), __builtin_fminf(e.lo2, o.lo2));
-  e.lo1 = __builtin_fminf(e.lo1, o.lo1);
+  e.hi2 = fmax2(fmin2(e.hi1, o.hi1), fmax2(e.hi2, o.hi2));
+  e.hi1 = fmax2(e.hi1, o.hi1);
+  e.lo2 = fmin2(fmax2(e.lo1, o.lo1), fmin2(e.lo2, o.lo2));
+  e.lo1 = fmin2(e.lo1, o.lo1);
 }
 template <int CTRL>
 __device__ __forceinline__ void ext2_dpp_merge(Ext2& e) {
@@ -320,8 +326,8 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
       mx[e] = x[0][e];
 #pragma unroll
       for (int i = 1; i < kRPT; ++i) {
-        mn[e] = __builtin_fminf(mn[e], x[i][e]);
-        mx[e] = __builtin_fmaxf(mx[e], x[i][e]);
+        mn[e] = fmin2(mn[e], x[i][e]);
+        mx[e] = fmax2(mx[e], x[i][e]);
       }
       minmax_across<kTPR>(mn[e], mx[e]);
     }
@@ -349,8 +355,8 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
       s_par[5][t] = kv;
       if (keep == 0) store_side<DT>(side.idx, side.val, t, 255, 0.0f);
     } else {
-      lo = __builtin_fminf(__builtin_fminf(s_red[0][t], s_red[1][t]), __builtin_fminf(s_red[2][t], s_red[3][t]));
-      hi = __builtin_fmaxf(__builtin_fmaxf(s_red[4][t], s_red[5][t]), __builtin_fmaxf(s_red[6][t], s_red[7][t]));
+      lo = fmin2(fmin2(s_red[0][t], s_red[1][t]), fmin2(s_red[2][t], s_red[3][t]));
+      hi = fmax2(fmax2(s_red[4][t], s_red[5][t]), fmax2(s_red[6][t], s_red[7][t]));
     }
     float dl, z;
     bool ex = false;
@@ -466,8 +472,8 @@ __device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0
       mx = x[0];
 #pragma unroll
       for (int e = 1; e < kVE; ++e) {
-        mn = __builtin_fminf(mn, x[e]);
-        mx = __builtin_fmaxf(mx, x[e]);
+        mn = fmin2(mn, x[e]);
+        mx = fmax2(mx, x[e]);
       }
       minmax_run<kTPR>(mn, mx);
     }

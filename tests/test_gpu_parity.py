@@ -131,8 +131,9 @@ def test_short_caches(T):
 
 @pytest.mark.parametrize("bits", list(range(1, 9)))
 def test_constructed_edge_values(bits):
-    """Ties at half steps, all-equal groups and tokens, -0.0, fp32 subnormal
-    ranges, large magnitudes: every code and parameter bit-exact."""
+    """Ties at half steps, all-equal groups and tokens, -0.0, groups of
+    zeros of both signs, fp32 subnormal ranges, large magnitudes: every code
+    and parameter bit-exact."""
     kvq = _kvq()
     log("bits", bits)
     rng = np.random.default_rng(bits)
@@ -165,6 +166,9 @@ def test_constructed_edge_values(bits):
             elif k == 4:  # large magnitudes
                 K[0, h, rows] = rng.standard_normal((G, D)).astype(np.float32) * np.float32(1e30)
                 V[0, h, rows] = rng.standard_normal((G, D)).astype(np.float32) * np.float32(1e30)
+            elif k == 5:  # zeros of both signs: every key channel and value token all zero
+                K[0, h, rows] = np.where(rng.random((G, D)) < 0.5, np.float32(-0.0), np.float32(0.0))
+                V[0, h, rows] = np.where(rng.random((G, D)) < 0.5, np.float32(-0.0), np.float32(0.0))
             else:
                 K[0, h, rows] = rng.standard_normal((G, D)).astype(np.float32) * np.float32(10.0 ** (k - 6))
                 V[0, h, rows] = rng.standard_normal((G, D)).astype(np.float32)

@@ -82,19 +82,22 @@ __device__ __forceinline__ void affine_codes(const float* x, const float* delta,
                                              const float* rcp, bool exact, uint32_t* code) {
   constexpr float levels = float((1 << BITS) - 1);
   constexpr float kBand = 0.5f - float(1 << BITS) * 0x1p-21f;
-  bool risky = exact;
+  // the largest distance of a quotient from its rounded value (fmaxf skips
+  // the NaN of an infinite quotient, whose code the clamp decides)
+  float dev = 0.0f;
   float c[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const float a = x[i] - zp[i];
     const float y = a * rcp[i];
     const float r = __builtin_rintf(y);
-    risky |= __builtin_fabsf(y - r) >= kBand;
-    // clamped: an entry kept exact in a side table lies outside the dense
-    // range (an infinite or NaN y, from x - zp overflowing, clamps too)
-    c[i] = fmin2(fmax2(r, 0.0f), levels);
+    dev = __builtin_fmaxf(dev, __builtin_fabsf(y - r));
+    // clamped (one median): an entry kept exact in a side table lies
+    // outside the dense range; y is never NaN (x - zp is finite for inputs
+    // below 2^127, and the reciprocal is finite), an infinite y clamps too
+    c[i] = __builtin_amdgcn_fmed3f(r, 0.0f, levels);
   }
-  if (__builtin_amdgcn_ballot_w64(risky) != 0) {
+  if (__builtin_amdgcn_ballot_w64(exact || dev >= kBand) != 0) {
 #pragma unroll
     for (int i = 0; i < N; ++i) code[i] = affine_code(x[i], delta[i], zp[i], levels);
   } else {

@@ -132,18 +132,21 @@ def prefill_bytes(w, T: int, qcap: int) -> int:
 
 def decode_splits(w, T: int, cus: int, ws_splits: int = 1024) -> int:
     """Split count of one decode call, by the launch rule of the library's
-    host code (matrix-core path: one round of two workgroups per CU over
-    64-token chunks; VALU path: see kvq_api.hip), for the split-partial
-    byte count."""
+    host code (matrix-core path: one round of one workgroup per CU over
+    64-token chunks, at most min(64, 8 * (4096 // (2 * D * element bytes)))
+    exact tokens per split; VALU path: see kvq_api.hip), for the
+    split-partial byte count."""
     ns, Q, nr = partition(T, w.sink, w.residual, w.group)
     n_fp = ns + nr
     if uses_mfma(w) and Q > 0:
         nblk = -(-Q // 64) - window_start(w, T) // 64
-        want = max(1, 2 * cus // (w.batch * w.n_kv_heads))
+        want = max(1, cus // (w.batch * w.n_kv_heads))
         want = min(want, nblk, ws_splits)
         bps = -(-nblk // want)
         n_split = -(-nblk // bps)
-        return max(n_split, min(-(-n_fp // 64), ws_splits), 1)
+        eb = 4 if w.dtype == "f32" else 2
+        xcap = min(64, 8 * (4096 // (2 * w.head_dim * eb)))
+        return max(n_split, min(-(-n_fp // xcap), ws_splits), 1)
     return None
 
 

@@ -325,9 +325,10 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
 
   // The matrix-core kernel covers GQA groups of 4 and 8 with 2- and 4-bit
   // codes, once at least one token is quantized (its chunk loads assume a
-  // chunk 0), for caches without side tables or pre-RoPE keys.  It works per KV head on 64-token chunks, with the grid sized
-  // to one round of two workgroups per CU, and spreads the full-precision
-  // tokens evenly over its splits.  Everything else runs a VALU kernel on
+  // chunk 0), for caches without side tables or pre-RoPE keys.  It works
+  // per KV head on 64-token chunks, with the grid sized to one round of
+  // one workgroup per CU, and spreads the full-precision tokens evenly over
+  // its splits.  Everything else runs a VALU kernel on
   // value-code blocks, again with the full-precision tokens spread evenly
   // over the splits: GQA groups of 2..8 heads the grouped one, MHA and
   // larger groups the per-head one.
@@ -351,16 +352,18 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, int64
   int64_t n_split = 0;
   bool direct = false;
   if (mfma) {
-    const int64_t slots = 2 * int64_t(device_cu_count());
+    // one round of workgroups, one per CU
+    const int64_t slots = int64_t(device_cu_count());
     const int64_t rows = int64_t(B) * H;
     int64_t want = slots / rows > 0 ? slots / rows : 1;
     if (want > nblk) want = nblk;
     if (want > cap_splits) want = cap_splits;
     bps = want > 0 ? (nblk + want - 1) / want : 1;
     n_split = nblk > 0 ? (nblk + bps - 1) / bps : 0;
-    // at most ~64 exact tokens per split: splits past the chunks, if any,
-    // take exact tokens only
-    int64_t want_fp = (n_fp + 63) / 64;
+    // at most mfma_exact_cap exact tokens per split (their rows are staged
+    // in LDS): splits past the chunks, if any, take exact tokens only
+    const int64_t xcap = kvq::mfma_exact_cap(int(kvq_dtype_bytes(cfg->dtype)), int(D));
+    int64_t want_fp = (n_fp + xcap - 1) / xcap;
     if (want_fp > cap_splits) want_fp = cap_splits;
     if (n_split < want_fp) n_split = want_fp;
     if (n_split < 1) n_split = 1;

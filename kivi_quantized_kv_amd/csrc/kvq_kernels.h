@@ -68,7 +68,7 @@ struct AttnArgs {
   int n_split;              // splits per (batch, q head)
   int direct;               // VALU kernel, one split per row: write out, no merge
   int blocks_per_split;     // value-code blocks per split (VALU kernel; the matrix-core
-                            // kernel deals chunks to its waves in turn instead)
+                            // kernel's waves take chunks from a counter instead)
   int fp_per_split;         // full-precision tokens per split
   int64_t ml_offset;        // floats before the (m, l) pairs in ws
   // Sliding window: quantized tokens before u_lo are outside it.  The
@@ -115,6 +115,13 @@ template <int DT, int D, int BITS, int MODE>
 hipError_t launch_attn_gqa(const AttnArgs& a, int B, hipStream_t s);
 template <int DT, int D, int BITS, int MODE>
 int attn_gqa_blocks_per_cu();
+// The matrix-core kernel: one workgroup of kMfmaWaves waves per CU.  Each
+// wave stages the rows of its exact (sink and residual) tokens in 4 KB of
+// LDS, so a split takes at most mfma_exact_cap(element bytes, D) of them.
+constexpr int kMfmaWaves = 8;
+constexpr int mfma_exact_cap(int esz, int D) {
+  return kMfmaWaves * (4096 / (2 * D * esz)) < 64 ? kMfmaWaves * (4096 / (2 * D * esz)) : 64;
+}
 template <int DT, int D, int BITS, int GQA>
 hipError_t launch_attn_mfma(const AttnArgs& a, int B, hipStream_t s);
 template <int DT, int D>

@@ -36,17 +36,19 @@
 // holds in the S^T accumulator for one channel in one 32-bit unit, so the
 // P' operand comes straight from the q.K^T output registers.
 //
-// Memory pipeline: the waves of one (batch, KV head) take its chunks in
-// turn (wave w of W gets chunks w, w + W, ...), so at any moment they
-// stream one contiguous stretch of the cache; while a wave computes one
-// of its chunks the codes of its next one are already in flight into
-// registers (non-temporal loads: read once, not kept in the caches), and so
-// are its key/value parameters, which are staged through wave-private LDS
-// (broadcast reads) when the chunk comes up.  The sink and residual tokens
-// of a split are spread over its waves; each wave loads its first one
-// before the chunk batches and folds it in, in a softmax state of its own,
-// while the batches are in flight.  The workgroup merge joins the four
-// waves' quantized states and their exact-token states.
+// Work split: one workgroup of kMfmaWaves waves per CU and split of a
+// (batch, KV head); split s owns chunks s, s + n_split, ..., so at any
+// moment the splits stream one contiguous stretch of the cache.  Its waves
+// take those chunks in order from a counter in LDS (the first two each
+// fixed), so a wave whose loads come back early takes more of them and the
+// waves of a CU finish together.  While a wave computes one chunk the codes
+// of its next one are already in flight into registers (non-temporal
+// loads: read once, not kept in the caches), and so are its key/value
+// parameters, which are staged through wave-private LDS (broadcast reads).
+// The sink and residual tokens of a split are spread over its waves: each
+// wave copies its tokens' rows into LDS before the chunk batches and folds
+// them in after its last chunk.  The workgroup merge joins the waves'
+// states.
 //
 // MFMA operand layout (16x16x32, 64 lanes): lane l holds A[row l%16][k in
 // group l/16] and B[k in group l/16][col l%16] (8 values each, the same
@@ -182,15 +184,18 @@ __device__ __forceinline__ void copy_to_lds(const void* src, const void* lds) {
 }
 
 // s_waitcnt for the vector-memory counter only (expcnt and lgkmcnt left
-// at their maxima), N < 16.
+// at their maxima), N < 64 (the count's low four bits sit in bits 3:0 of
+// the immediate, its high two in bits 15:14).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 template <int DT, int D, int BITS, int GQA, bool G32>
-__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
+__global__ __launch_bounds__(64 * kMfmaWaves, 1) void k_attn_mfma(AttnArgs a) {
+  constexpr int kW = kMfmaWaves;
+  constexpr int kT = 64 * kW;
   using VLy = VLayout<BITS>;
   using CR = ChunkRegs<D, BITS>;
   constexpr int kRB = D * BITS / 8;        // bytes per key row
@@ -239,25 +244,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 
   __shared__ float s_q[GQA][D + 4];    // scale*log2e * q; rows padded against bank conflicts
   __shared__ float s_qf[GQA][D + 4];   // the same times each channel's field scale
-  __shared__ float s_o[4][GQA][D];
-  __shared__ float s_m[4][GQA], s_l[4][GQA], s_z[4][GQA];
-  __shared__ float s_of[4][GQA][D];                  // each wave's exact-token partial
-  __shared__ float s_mf[4][GQA], s_lf[4][GQA];
-  // wave-private parameter buffers of the chunks at even / odd positions
-  // of the wave's run, filled by LDS copies.  Two separate arrays, so that
-  // the compiler, which orders reads of an array after the copies in flight
-  // into it, does not hold the reads of one buffer behind the other's copies.
-  __shared__ float4 s_kp0[4][2][2 * D / 4], s_kp1[4][2][2 * D / 4];   // [wave][group][delta | zero]
-  __shared__ float s_vp0[4][2][64], s_vp1[4][2][64];                  // [wave][delta | zero][token]
+  __shared__ float s_o[kW][D][16];     // each wave's accumulator rows, channel-major
+  __shared__ float s_m[kW][GQA], s_l[kW][GQA], s_z[kW][GQA];
+  // wave-private parameter buffers of the chunks in register sets a / b,
+  // filled by LDS copies.  Two separate arrays, so that the compiler, which
+  // orders reads of an array after the copies in flight into it, does not
+  // hold the reads of one buffer behind the other's copies.
+  __shared__ float4 s_kp0[kW][2][2 * D / 4], s_kp1[kW][2][2 * D / 4];   // [wave][group][delta | zero]
+  __shared__ float s_vp0[kW][2][64], s_vp1[kW][2][64];                  // [wave][delta | zero][token]
+  // wave-private rows of the wave's exact tokens (key row, value row each)
+  __shared__ uint32_t s_x[kW][1024];
+  __shared__ int s_next;                                               // the chunk counter
 
   // Chunks are numbered from the first one the query attends to (chunk c0,
-  // the first of the sliding window; 0 without one).  This wave's chunks:
-  // gw, gw + nw_row, ... (none for waves past the chunk count, whose splits
-  // only take exact tokens).
+  // the first of the sliding window; 0 without one).  This workgroup's
+  // chunks: j = 0, 1, ... is chunk split + j * n_split (none for splits past
+  // the chunk count, which only take exact tokens).  Only the last chunk of
+  // the quantized range can be a half chunk (32 tokens).
   const int64_t nch = ((a.Q + 63) >> 6) - a.c0;
-  const int64_t nw_row = int64_t(a.n_split) * 4;
-  const int64_t gw = int64_t(split) * 4 + wave;
-  const int64_t wn = gw < nch ? (nch - gw + nw_row - 1) / nw_row : 0;
+  const int64_t nsp = a.n_split;
+  const int nj = split < nch ? int((nch - split + nsp - 1) / nsp) : 0;
+  const bool wg_half = (a.Q & 63) != 0 && nj > 0 && split + int64_t(nj - 1) * nsp == nch - 1;
+  const int nfull = nj - (wg_half ? 1 : 0);
+  // 1: a full chunk, 2: the half chunk, 0: past the workgroup's chunks
+  auto state_of = [&](int j) { return j < nfull ? 1 : (j == nfull && wg_half ? 2 : 0); };
+  auto chunk_of = [&](int j) { return int64_t(split) + int64_t(j) * nsp; };
   // first storage row of chunk ch: the ring's chunk slot (c0 + ch) mod
   // (qcap / 64), by one conditional subtraction (the live chunks span at
   // most qcap / 64 + 1 slots)
@@ -316,20 +327,45 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // q first, then the first exact token, then the first two batches (q and
-  // that token complete before them), then q into LDS
-  constexpr int kQPer = GQA * D / 256;
+  // q (raw elements) is copied into LDS by the waves ahead of any chunk
+  // batch (requests issued after the first batches of all CUs would queue
+  // behind them, and every wave needs q for its first chunk), then each
+  // wave issues its first batch and waits for its q copies alone.  Its
+  // second batch and the copies of its exact-token rows (four, always;
+  // those past its rows copy 16 bytes of chunk 0) go out during its first
+  // chunk: a CU's memory pipeline takes requests in issue order and holds
+  // a wave's issue while it is full, so a wave that issued two batches up
+  // front could not start its first chunk, landed, before the second one
+  // had gone out.
   using QE = typename Elem<DT>::T;
-  QE qraw[kQPer];                                  // widened after the batches are issued
+  constexpr int kEsz = Elem<DT>::bytes;
+  constexpr int kQRowB = D * kEsz;                 // bytes per q row
+  constexpr int kQI = GQA * kQRowB / 256;          // 256-byte copies of q
+  __shared__ uint32_t s_qraw[GQA * kQRowB / 4];
 #pragma unroll
-  for (int j = 0; j < kQPer; ++j) {
-    const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
-    qraw[j] = reinterpret_cast<const QE*>(a.q)[b * a.q_sb + (h * GQA + qh) * a.q_sh + d];
+  for (int i0 = 0; i0 < (kQI + kW - 1) / kW; ++i0) {
+    const int i = i0 * kW + wave;
+    if (i < kQI) {
+      const int o = i * 256 + lane * 4, qh = o / kQRowB;
+      const char* src = reinterpret_cast<const char*>(a.q) +
+                        (b * a.q_sb + (h * GQA + qh) * a.q_sh) * kEsz + o % kQRowB;
+      copy_to_lds<4>(src, reinterpret_cast<const char*>(&s_qraw[0]) + i * 256);
+    }
   }
-  // This wave's exact tokens (sinks and the residual window): f0 + wave,
-  // f0 + wave + 4, ... below f1.  The first one's rows are loaded before
-  // the chunk batches, so that they land first and are folded in while the
-  // batches are in flight.
+  // This wave's first batch (a wave without chunks issues a batch that is
+  // not live, on chunk 0, which exists: the kernel runs only with Q > 0),
+  // behind q; then q alone is waited for.
+  CR ra, rb;
+  const int jA0 = wave, jB0 = wave + kW;
+  issue_batch(chunk_of(jA0), state_of(jA0) != 0, ra, std::integral_constant<int, 0>{});
+  wait_vmcnt<kBatch>();
+  __syncthreads();
+  // The split's exact tokens (sinks and the residual window) are [f0, f1);
+  // this wave's are f0 + wave, f0 + wave + kW, ...  The rows of the first
+  // kXPer of them (4 KB; the planner keeps a split's count within
+  // mfma_exact_cap, unless the workspace is too small for more splits) are
+  // copied into s_x[wave] (token i: key row, then value row); all are
+  // folded in after the wave's last chunk.
   const int64_t f0 = int64_t(split) * a.fp_per_split;
   const int64_t f1 = f0 + a.fp_per_split < a.n_fp ? f0 + a.fp_per_split : a.n_fp;
   auto fp_row = [&](int64_t i, const void*& kb, const void*& vb, int64_t& off) {
@@ -341,51 +377,57 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       kb = a.k_resid; vb = a.v_resid; off = (bh * a.ring + slot) * D;
     }
   };
-  // first exact token, raw bits (widened after the batches are issued):
-  // key quarter row, values
-  using KR = std::conditional_t<DT == DT_F32, float4, uint2>;
-  KR fkr[kQCH / 4];
-  uint32_t fvr[kNB];                                 // one 32-bit register per value (no packing)
-  const bool has_fp = f0 + wave < f1;
-  if (has_fp) {
-    const void* kb;
-    const void* vb;
-    int64_t off;
-    fp_row(f0 + wave, kb, vb, off);
-#pragma unroll
-    for (int c = 0; c < kQCH; c += 4)
-      fkr[c / 4] = *reinterpret_cast<const KR*>(reinterpret_cast<const QE*>(kb) + off + lg * kQCH + c);
-#pragma unroll
-    for (int n = 0; n < kNB; ++n) {
-      if constexpr (DT == DT_F32) fvr[n] = reinterpret_cast<const uint32_t*>(vb)[off + 16 * n + col];
-      else fvr[n] = reinterpret_cast<const QE*>(vb)[off + 16 * n + col];
-    }
-  }
-  // The first two batches, on every wave (a wave with fewer chunks issues
-  // batches that are not live, on chunk 0, which exists: the kernel runs
-  // only with Q > 0).  Under a branch they would make the compiler's wait
-  // for q below cover both batches.
-  CR ra, rb;
-  issue_batch(gw, wn > 0, ra, std::integral_constant<int, 0>{});
-  issue_batch(gw + nw_row, wn > 1, rb, std::integral_constant<int, 1>{});
-  __shared__ float s_qmx[4];
+  constexpr int kRowB = D * kEsz;                  // bytes per row
+  constexpr int kXPer = 4096 / (2 * kRowB);         // tokens staged per wave
+  const int nxw = f0 + wave < f1 ? int((f1 - f0 - wave + kW - 1) / kW) : 0;
+  __shared__ float s_qmx[kW];
   float qmx = 0.f;                                 // max |scale*log2e * q| of the workgroup
+  constexpr int kQPer = (GQA * D + kT - 1) / kT;
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
-    const int x = threadIdx.x + 256 * j, qh = x / D, d = x % D;
-    float qf;
-    if constexpr (DT == DT_F32) qf = qraw[j];
-    else if constexpr (DT == DT_F16) qf = f16_bits_to_f32(qraw[j]);
-    else qf = bf16_bits_to_f32(qraw[j]);
-    const float v = qf * a.sm_scale_log2;
-    s_q[qh][d] = v;
-    s_qf[qh][d] = v * field_scale<BITS>(d);
-    qmx = __builtin_fmaxf(qmx, __builtin_fabsf(v));
+    const int x = threadIdx.x + kT * j, qh = x / D, d = x % D;
+    if (x < GQA * D) {
+      float qf;
+      if constexpr (DT == DT_F32) qf = reinterpret_cast<const float*>(&s_qraw[0])[x];
+      else if constexpr (DT == DT_F16) qf = f16_bits_to_f32(reinterpret_cast<const QE*>(&s_qraw[0])[x]);
+      else qf = bf16_bits_to_f32(reinterpret_cast<const QE*>(&s_qraw[0])[x]);
+      const float v = qf * a.sm_scale_log2;
+      s_q[qh][d] = v;
+      s_qf[qh][d] = v * field_scale<BITS>(d);
+      qmx = __builtin_fmaxf(qmx, __builtin_fabsf(v));
+    }
   }
   qmx = wave_max(qmx);
   if (lane == 0) s_qmx[wave] = qmx;
+  if (threadIdx.x == 0) s_next = 2 * kW;
   __syncthreads();
-  const float qmax = __builtin_fmaxf(__builtin_fmaxf(s_qmx[0], s_qmx[1]), __builtin_fmaxf(s_qmx[2], s_qmx[3]));
+  float qmax = s_qmx[0];
+#pragma unroll
+  for (int w = 1; w < kW; ++w) qmax = __builtin_fmaxf(qmax, s_qmx[w]);
+  // issue_second starts this wave's second batch and its exact-token
+  // copies.
+  auto issue_second = [&]() {
+    {
+      const int bytes = (nxw < kXPer ? nxw : kXPer) * 2 * kRowB;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int o = k * 1024 + lane * 16;
+        const int r = o / kRowB, i = r >> 1;
+        const char* src = reinterpret_cast<const char*>(kc_head);
+        if (k * 1024 < bytes) {
+          const void* kb;
+          const void* vb;
+          int64_t off;
+          fp_row(f0 + wave + int64_t(i < nxw ? i : 0) * kW, kb, vb, off);
+          const char* row = reinterpret_cast<const char*>((r & 1) ? vb : kb) + off * kEsz;
+          // lanes past the wave's rows copy the start of its first row (in bounds)
+          src = i < nxw ? row + o % kRowB : row;
+        }
+        copy_to_lds<16>(src, reinterpret_cast<const char*>(&s_x[wave][0]) + k * 1024);
+      }
+    }
+    issue_batch(chunk_of(jB0), state_of(jB0) != 0, rb, std::integral_constant<int, 1>{});
+  };
   // Key weights w = x * delta with |x| <= qmax: every field weight is at
   // most 1.25 qmax delta_max, so the fp16 high parts stay finite while the
   // chunk's largest key delta is below 2^15 / qmax.  A chunk at or above
@@ -427,9 +469,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   };
 
   // Wave state into LDS: l and z reduced over the owner columns' lane
-  // groups, the high and low rows joined, o in real units (acc times
-  // 2^uexp).
-  auto stash = [&](float (*so)[D], float* sm, float* sl, float* sz, int uexp) {
+  // groups; the accumulator (in real units by then) written whole, rows
+  // channel-major, its high and low rows joined in the workgroup merge.
+  auto stash = [&]() {
     float lr = l + dpp_rot<kJoin>(l);     // owner (even tiles or exact tokens) + partner (odd tiles)
     float zr = z + dpp_rot<kJoin>(z);
     if constexpr (DUAL) {
@@ -443,107 +485,102 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     lr = sum_xor32(sum_xor16(lr));
     zr = sum_xor32(sum_xor16(zr));
     if (lane < GQA) {
-      sm[lane] = m;
-      sl[lane] = lr;
-      if (sz) sz[lane] = zr;
+      s_m[wave][lane] = m;
+      s_l[wave][lane] = lr;
+      s_z[wave][lane] = zr;
     }
 #pragma unroll
-    for (int n = 0; n < kNB; ++n) {
+    for (int n = 0; n < kNB; ++n) *reinterpret_cast<f32x4_t*>(&s_o[wave][n * 16 + col][4 * lg]) = acc[n];
+  };
+
+  // An exact token folded into the state, from its partial score over the
+  // lane's quarter row (an fp32 dot product) and its values vv, which are
+  // added to the high rows in the accumulator's units.
+  auto fold_score = [&](float part, const float* vv) {
+    part = sum_xor16(part);
+    const float sc = sum_xor32(part);             // score of head hh
+    raise_max(sc);
+    const float p = __builtin_amdgcn_exp2f(sc - m);
+    if (lg == 0 && owner) l += p;                 // one lane group of the owner columns
+    float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = acc[n][i];
-        if constexpr (DUAL) v = sum_xor32(sum_xor16(v));   // rows r, r + 4, r + 8, r + 12
-        else if constexpr (GQA == 8) v = sum_xor32(v);     // rows r and r + 8
-        else v = sum_xor16(v);                             // rows r and r + 4
-        const int row = 4 * lg + i;
-        if (row < GQA) so[row][n * 16 + col] = __builtin_amdgcn_ldexpf(v, uexp);
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                    ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, p)));
+      pr[i2] = (4 * lg + i2) < GQA ? v : 0.f;     // high rows only
+    }
+#pragma unroll
+    for (int n = 0; n < kNB; ++n)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] = __builtin_fmaf(pr[i2], vv[n], acc[n][i2]);
+  };
+
+  // The wave's exact token i: its partial score over the lane's quarter
+  // row and its values, from its rows in s_x (i < kXPer; the key row is
+  // read four channels at a time, so few registers stay live), or past
+  // the staged ones from the cache.
+  auto exact_part = [&](int i) -> float {
+    float part = 0.f;
+    if (i >= kXPer) {
+      const void* kb;
+      const void* vb;
+      int64_t off;
+      fp_row(f0 + wave + int64_t(i) * kW, kb, vb, off);
+#pragma unroll
+      for (int c = 0; c < kQCH; c += 4) {
+        float k4[4];
+        load4<DT>(kb, off + lg * kQCH + c, k4);
+        const float4 q4 = *reinterpret_cast<const float4*>(&s_q[hh][lg * kQCH + c]);
+        part = __builtin_fmaf(k4[0], q4.x, part);
+        part = __builtin_fmaf(k4[1], q4.y, part);
+        part = __builtin_fmaf(k4[2], q4.z, part);
+        part = __builtin_fmaf(k4[3], q4.w, part);
+      }
+      return part;
+    }
+    const char* xk = reinterpret_cast<const char*>(&s_x[wave][0]) + i * 2 * kRowB;
+#pragma unroll
+    for (int c = 0; c < kQCH; c += 4) {
+      float k4[4];
+      if constexpr (DT == DT_F32) {
+        const float4 v = *reinterpret_cast<const float4*>(xk + (lg * kQCH + c) * 4);
+        k4[0] = v.x; k4[1] = v.y; k4[2] = v.z; k4[3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(xk + (lg * kQCH + c) * 2);
+        const uint32_t e[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) k4[t] = DT == DT_F16 ? f16_bits_to_f32(e[t]) : bf16_bits_to_f32(e[t]);
+      }
+      const float4 q4 = *reinterpret_cast<const float4*>(&s_q[hh][lg * kQCH + c]);
+      part = __builtin_fmaf(k4[0], q4.x, part);
+      part = __builtin_fmaf(k4[1], q4.y, part);
+      part = __builtin_fmaf(k4[2], q4.z, part);
+      part = __builtin_fmaf(k4[3], q4.w, part);
+    }
+    return part;
+  };
+  auto exact_values = [&](int i, float* vv) {
+    if (i >= kXPer) {
+      const void* kb;
+      const void* vb;
+      int64_t off;
+      fp_row(f0 + wave + int64_t(i) * kW, kb, vb, off);
+#pragma unroll
+      for (int n = 0; n < kNB; ++n) vv[n] = load1<DT>(vb, off + 16 * n + col);
+      return;
+    }
+    const char* xv = reinterpret_cast<const char*>(&s_x[wave][0]) + i * 2 * kRowB + kRowB;
+#pragma unroll
+    for (int n = 0; n < kNB; ++n) {
+      if constexpr (DT == DT_F32) {
+        vv[n] = reinterpret_cast<const float*>(xv)[16 * n + col];
+      } else {
+        const uint32_t e = reinterpret_cast<const uint16_t*>(xv)[16 * n + col];
+        vv[n] = DT == DT_F16 ? f16_bits_to_f32(e) : bf16_bits_to_f32(e);
       }
     }
   };
-
-  // ---- exact tokens first, in a softmax state of their own (scores as
-  // fp32 dot products, values added to the high rows in real units); it
-  // goes to LDS and meets the quantized state in the workgroup merge.
-  {
-    auto fold_fp = [&](const float* kq, const float* vv) {
-      float part = 0.f;
-#pragma unroll
-      for (int c = 0; c < kQCH; c += 4) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&s_q[hh][lg * kQCH + c]);
-        part = __builtin_fmaf(kq[c], q4.x, part);
-        part = __builtin_fmaf(kq[c + 1], q4.y, part);
-        part = __builtin_fmaf(kq[c + 2], q4.z, part);
-        part = __builtin_fmaf(kq[c + 3], q4.w, part);
-      }
-      part = sum_xor16(part);
-      const float sc = sum_xor32(part);             // score of head hh
-      raise_max(sc);
-      const float p = __builtin_amdgcn_exp2f(sc - m);
-      if (lg == 0 && owner) l += p;                 // one lane group of the owner columns
-      float pr[4];
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                      ((4 * lg + i2) % GQA) << 2, __builtin_bit_cast(int, p)));
-        pr[i2] = (4 * lg + i2) < GQA ? v : 0.f;     // high rows only
-      }
-#pragma unroll
-      for (int n = 0; n < kNB; ++n)
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] = __builtin_fmaf(pr[i2], vv[n], acc[n][i2]);
-    };
-    if (has_fp) {
-      // keep the widening here, after the batches were issued
-#pragma unroll
-      for (int n = 0; n < kNB; ++n) asm volatile("" : "+v"(fvr[n]));
-#pragma unroll
-      for (int c = 0; c < kQCH / 4; ++c) {
-        if constexpr (DT == DT_F32) {
-          asm volatile("" : "+v"(fkr[c].x), "+v"(fkr[c].y), "+v"(fkr[c].z), "+v"(fkr[c].w));
-        } else {
-          asm volatile("" : "+v"(fkr[c].x), "+v"(fkr[c].y));
-        }
-      }
-      float fk[kQCH], fv[kNB];
-      auto widen1 = [](uint32_t r) -> float {
-        if constexpr (DT == DT_F16) return f16_bits_to_f32(r);
-        else return bf16_bits_to_f32(r);
-      };
-#pragma unroll
-      for (int c = 0; c < kQCH; c += 4) {
-        if constexpr (DT == DT_F32) {
-          fk[c] = fkr[c / 4].x; fk[c + 1] = fkr[c / 4].y; fk[c + 2] = fkr[c / 4].z; fk[c + 3] = fkr[c / 4].w;
-        } else {
-          fk[c] = widen1(fkr[c / 4].x & 0xFFFFu); fk[c + 1] = widen1(fkr[c / 4].x >> 16);
-          fk[c + 2] = widen1(fkr[c / 4].y & 0xFFFFu); fk[c + 3] = widen1(fkr[c / 4].y >> 16);
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < kNB; ++n) {
-        if constexpr (DT == DT_F32) fv[n] = __builtin_bit_cast(float, fvr[n]);
-        else fv[n] = widen1(fvr[n]);
-      }
-      fold_fp(fk, fv);
-      for (int64_t i = f0 + wave + 4; i < f1; i += 4) {
-        const void* kb;
-        const void* vb;
-        int64_t off;
-        fp_row(i, kb, vb, off);
-        float kq[kQCH], vv[kNB];
-#pragma unroll
-        for (int c = 0; c < kQCH; c += 4) load4<DT>(kb, off + lg * kQCH + c, &kq[c]);
-#pragma unroll
-        for (int n = 0; n < kNB; ++n) vv[n] = load1<DT>(vb, off + 16 * n + col);
-        fold_fp(kq, vv);
-      }
-    }
-    stash(s_of[wave], s_mf[wave], s_lf[wave], nullptr, 0);
-#pragma unroll
-    for (int n = 0; n < kNB; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m = -__builtin_inff();
-    l = 0.f;
-    z = 0.f;
-  }
+  int x_done = 0;                                  // exact tokens folded in so far
 
   {
     // ------------------------------------------------------------ quantized
@@ -622,8 +659,39 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 
     // A half chunk (only ever the last of the quantized range) holds 32
     // tokens: tiles 0 and 1, the first 32-token step of P.V.
-    auto process_chunk = [&](const CR& r, int64_t ch, auto half_tag, auto buf_tag) {
+    // The wave's staged exact tokens, folded into the state in the units of
+    // the accumulator (values times 2^(kexp - 24)); kexp is lowered first
+    // where the largest value needs it, so that p * v stays below 2^108.
+    auto fold_exact_scaled = [&]() {
+      const int nst = nxw < kXPer ? nxw : kXPer;   // the staged ones
+      for (int i = 0; i < nst; ++i) {
+        const float part = exact_part(i);
+        float vv[kNB];
+        exact_values(i, vv);
+        float vm = 0.f;
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) vm = __builtin_fmaxf(vm, __builtin_fabsf(vv[n]));
+        const int ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(wave_max(vm)));
+        if (kexp - 24 + ev > 100) {
+          const int knew = 124 - ev;
+#pragma unroll
+          for (int n = 0; n < kNB; ++n)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) acc[n][i2] = __builtin_amdgcn_ldexpf(acc[n][i2], knew - kexp);
+          kexp = knew;
+          set_vke();
+        }
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) vv[n] = __builtin_amdgcn_ldexpf(vv[n], kexp - 24);
+        fold_score(part, vv);
+      }
+      x_done = nst;
+    };
+    // ORD 1: the wave's first chunk, whose batch is the only one issued: it
+    // waits for all of it and starts the second batch after its q.K^T.
+    auto process_chunk = [&](const CR& r, int64_t ch, auto half_tag, auto buf_tag, auto ord_tag) {
       constexpr bool HALF = decltype(half_tag)::value;
+      constexpr bool FIRST = decltype(ord_tag)::value == 1;
       constexpr int kTiles = HALF ? 2 : 4;
       constexpr int BUF = decltype(buf_tag)::value;
       const auto& kpb = BUF == 0 ? s_kp0 : s_kp1;
@@ -635,7 +703,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       // with 32-token groups has one)
       constexpr int kLiveGroups = (G32 && !HALF) ? 2 : 1;
       // this chunk's batch is complete once at most the next one is in flight
-      wait_vmcnt<kBatch>();
+      if constexpr (FIRST) wait_vmcnt<0>();
+      else wait_vmcnt<kBatch>();
       // ---- value scale: a delta at or above 2^(7-kexp) lowers kexp so
       // that the largest delta seen sits in [2^6, 2^7); with p <= 2^8 the
       // value weights stay below 2^15.  Checked here, acted on (rarely)
@@ -711,6 +780,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         }
         tile_products(r, sc, t_begin, t_end);
       }
+      if constexpr (FIRST) issue_second();
       // join the high and low columns of each head (scores - kappa, times
       // 2^-24)
       auto join_tiles = [&]() {
@@ -948,84 +1018,143 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       }
     };
 
-    // only the last chunk of the quantized range can be a half chunk, and
-    // only the wave whose run ends on it has one
-    const bool last_half = (a.Q & 63) != 0 && gw + (wn - 1) * nw_row == nch - 1;
-    const int64_t n_full = wn - (last_half ? 1 : 0);
-    // After a chunk, its registers and parameter buffer are free: start
-    // the batch of the wave's chunk after next.  Past the wave's last chunk
-    // that batch is not live (one cache line of chunk 0 per instruction), so
-    // that a batch always follows each chunk, as the counter waits assume.
-    // The copies into the buffer are ordered after this wave's reads of it
-    // by the wait on the LDS counter.
-    auto run_chunk = [&](int64_t k, CR& r, auto half_tag, auto buf_tag) {
-      __builtin_amdgcn_s_setprio(1);
-      process_chunk(r, gw + k * nw_row, half_tag, buf_tag);
+    // The wave's first two chunks are fixed (j = wave and wave + kW); every
+    // later index comes from the workgroup's counter, fetched one chunk
+    // ahead so that its LDS round trip is hidden.  After a chunk, its
+    // registers and parameter buffer are free: the batch of the next index
+    // starts there.  Past the workgroup's chunks that batch is not live (one
+    // cache line of chunk 0 per instruction), so that a batch always
+    // follows each chunk, as the counter waits assume.  The copies into the
+    // buffer are ordered after this wave's reads of it by the wait on the
+    // LDS counter.
+    int jA = jA0, jB = jB0;
+    int stA = state_of(jA), stB = state_of(jB);
+    auto fetch = [&]() {
+      int v = 0;
+      if (lane == 0) v = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return v;                                      // in lane 0
+    };
+    int jn = fetch();
+    auto next_batch = [&](CR& r, int& j, int& st, auto buf_tag) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      issue_batch(gw + (k + 2) * nw_row, k + 2 < wn, r, buf_tag);
+      j = __builtin_amdgcn_readfirstlane(jn);
+      st = state_of(j);
+      issue_batch(chunk_of(j), st != 0, r, buf_tag);
+      jn = fetch();
+    };
+    auto run_chunk = [&](CR& r, int& j, int& st, auto buf_tag) {
+      __builtin_amdgcn_s_setprio(1);
+      process_chunk(r, chunk_of(j), std::false_type{}, buf_tag, std::integral_constant<int, 0>{});
+      next_batch(r, j, st, buf_tag);
       __builtin_amdgcn_s_setprio(0);
     };
-    using Full = std::false_type;
-    using Half = std::true_type;
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    // ra holds the wave's chunk k, rb its chunk k + 1 (in flight or
-    // landed).  The loop is entered only with rb's batch the newest, so the
-    // compiler's own waits for ra's registers never reach far into rb's;
-    // an odd last full chunk and the half chunk are peeled.
-    int64_t k = 0;
-    for (; k + 1 < n_full; k += 2) {
-      run_chunk(k, ra, Full{}, B0{});
-      run_chunk(k + 1, rb, Full{}, B1{});
+    // The first chunk (set a) issues set b's batch, and after it the
+    // staged exact tokens are folded in (their copies went out ahead of set
+    // b's batch, so waiting for them leaves both batches in flight); then
+    // the sets alternate, b first, and the set checked is always the one
+    // with the older (smaller) index, whose batch is not the newest, so the
+    // compiler's own waits for its registers never reach far into the other
+    // set's.  A set whose chunk is not a full one ends the loop; it may hold
+    // the half chunk (the other set's index is larger, so it holds nothing).
+    bool at_a = true;
+    if (stA == 1) {
+      __builtin_amdgcn_s_setprio(1);
+      process_chunk(ra, chunk_of(jA), std::false_type{}, B0{}, std::integral_constant<int, 1>{});
+      next_batch(ra, jA, stA, B0{});
+      __builtin_amdgcn_s_setprio(0);
+      if (nxw > 0) {
+        wait_vmcnt<2 * kBatch>();
+        fold_exact_scaled();
+      }
+      for (;;) {
+        if (stB != 1) {
+          at_a = false;
+          break;
+        }
+        run_chunk(rb, jB, stB, B1{});
+        if (stA != 1) break;
+        run_chunk(ra, jA, stA, B0{});
+      }
+    } else {
+      issue_second();
     }
-    if (k < n_full) {
-      run_chunk(k, ra, Full{}, B0{});
-      if (last_half) run_chunk(k + 1, rb, Half{}, B1{});
-    } else if (last_half) {
-      run_chunk(k, ra, Half{}, B0{});
+    __builtin_amdgcn_s_setprio(1);
+    if (at_a) {
+      if (stA == 2) process_chunk(ra, chunk_of(jA), std::true_type{}, B0{}, std::integral_constant<int, 0>{});
+    } else if (stB == 2) {
+      process_chunk(rb, chunk_of(jB), std::true_type{}, B1{}, std::integral_constant<int, 0>{});
     }
-    // let every copy land before the buffers are left behind
+    __builtin_amdgcn_s_setprio(0);
+    // let every copy land before the buffers are left behind (and the
+    // exact-token rows are read)
     wait_vmcnt<0>();
   }
+  // ---- the accumulator in real units, then this wave's exact tokens
+  {
+    const int uexp = 24 - kexp;
+#pragma unroll
+    for (int n = 0; n < kNB; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[n][i] = __builtin_amdgcn_ldexpf(acc[n][i], uexp);
+    for (int i = x_done; i < nxw; ++i) {
+      const float part = exact_part(i);
+      float vv[kNB];
+      exact_values(i, vv);
+      fold_score(part, vv);
+    }
+  }
   // ---- wave result
-  stash(s_o[wave], s_m[wave], s_l[wave], s_z[wave], 24 - kexp);
+  stash();
   __syncthreads();
-  // ---- merge the four waves' quantized and exact-token states: the
-  // weights 2^(m_j - M) of the eight states of each head once, then the
-  // rows; write this split's partial for each head
-  __shared__ float s_fac[GQA][8], s_M[GQA];
-  if (threadIdx.x < 8 * GQA) {
-    const int qh = threadIdx.x / 8, j = threadIdx.x % 8;
+  // ---- merge the waves' states: the weights 2^(m_j - M) once per (head,
+  // wave), then the rows (the high and low rows of each head joined);
+  // write this split's partial for each head
+  __shared__ float s_fac[GQA][kW], s_M[GQA];
+  if (threadIdx.x < kW * GQA) {
+    const int qh = threadIdx.x / kW, j = threadIdx.x % kW;
     float M = s_m[0][qh];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, s_m[w][qh]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, s_mf[w][qh]);
+    for (int w = 1; w < kW; ++w) M = __builtin_fmaxf(M, s_m[w][qh]);
     // a split with no tokens at all leaves m = -inf, l = 0, o = 0
     const float Mref = M == -__builtin_inff() ? 0.f : M;
-    const float mj = j < 4 ? s_m[j][qh] : s_mf[j - 4][qh];
-    s_fac[qh][j] = __builtin_amdgcn_exp2f(mj - Mref);
+    s_fac[qh][j] = __builtin_amdgcn_exp2f(s_m[j][qh] - Mref);
     if (j == 0) s_M[qh] = M;
   }
   __syncthreads();
-  for (int x = threadIdx.x; x < GQA * D; x += 256) {
-    const int qh = x / D, d = x % D;
-    float o = 0.f;
+  constexpr int kHG = GQA / 4;                     // groups of four heads
+  for (int x = threadIdx.x; x < kHG * D; x += kT) {
+    const int hg = x / D, d = x % D;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      o = __builtin_fmaf(s_fac[qh][w], s_o[w][qh][d] + s_z[w][qh], o);
-      o = __builtin_fmaf(s_fac[qh][4 + w], s_of[w][qh][d], o);
-    }
-    const int64_t row = int64_t(b) * a.Hq + h * GQA + qh;
-    partial_o(a, row, split, D)[d] = o;
-    if (d == 0) {
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        L = __builtin_fmaf(s_fac[qh][w], s_l[w][qh], L);
-        L = __builtin_fmaf(s_fac[qh][4 + w], s_lf[w][qh], L);
+    for (int w = 0; w < kW; ++w) {
+      f32x4_t r = *reinterpret_cast<const f32x4_t*>(&s_o[w][d][4 * hg]);
+      if constexpr (DUAL) {
+        // rows r, r + 4, r + 8, r + 12: both key groups' high and low rows
+        r += *reinterpret_cast<const f32x4_t*>(&s_o[w][d][4]);
+        r += *reinterpret_cast<const f32x4_t*>(&s_o[w][d][8]);
+        r += *reinterpret_cast<const f32x4_t*>(&s_o[w][d][12]);
+      } else {
+        r += *reinterpret_cast<const f32x4_t*>(&s_o[w][d][4 * hg + GQA]);   // the low rows
       }
-      *reinterpret_cast<float2*>(partial_ml(a, row, split)) = float2{s_M[qh], L};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qh = 4 * hg + i;
+        o[i] = __builtin_fmaf(s_fac[qh][w], r[i] + s_z[w][qh], o[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qh = 4 * hg + i;
+      const int64_t row = int64_t(b) * a.Hq + h * GQA + qh;
+      partial_o(a, row, split, D)[d] = o[i];
+      if (d == 0) {
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) L = __builtin_fmaf(s_fac[qh][w], s_l[w][qh], L);
+        *reinterpret_cast<float2*>(partial_ml(a, row, split)) = float2{s_M[qh], L};
+      }
     }
   }
 }
@@ -1033,9 +1162,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 template <int DT, int D, int BITS, int GQA>
 hipError_t launch_attn_mfma(const AttnArgs& a, int B, hipStream_t s) {
   if (a.G == 32)
-    hipLaunchKernelGGL((k_attn_mfma<DT, D, BITS, GQA, true>), dim3(a.n_split, a.H, B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_attn_mfma<DT, D, BITS, GQA, true>), dim3(a.n_split, a.H, B), dim3(64 * kMfmaWaves), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((k_attn_mfma<DT, D, BITS, GQA, false>), dim3(a.n_split, a.H, B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_attn_mfma<DT, D, BITS, GQA, false>), dim3(a.n_split, a.H, B), dim3(64 * kMfmaWaves), 0,
+                       s, a);
   return hipGetLastError();
 }
 

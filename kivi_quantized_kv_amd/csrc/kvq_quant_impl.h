@@ -14,9 +14,15 @@
 // |y| 2^-21 of a half integer (r, the product and the division's own
 // rounding move the quotient by less than |y| 1.5 2^-22).  Since 0 <= y <=
 // (2^b - 1)(1 + 2^-21), one band (2^b) 2^-21 wide around the half integers
-// covers every element; waves holding an element in it, or a delta below
-// 2^-125 (kept off the reciprocal), take the exact division instead.  The prefill and the freeze run the same group and step
-// routines; only the row source differs (input tensor or residual ring).
+// covers every element.  Inputs of few significant bits (bf16) put many
+// quotients exactly on a half integer h; such an exact tie is recognised
+// by the residual fma(-h, delta, x - zp), which is zero exactly when x - zp
+// = h delta (delta >= 2^-125 keeps every nonzero residual representable),
+// and takes rint(h).  Any other element in the band, or an element whose
+// delta is below 2^-125 (kept off the reciprocal), takes the exact
+// division; it runs once per element index of a wave that holds one.  The
+// prefill and the freeze run the same group and step routines; only the
+// row source differs (input tensor or residual ring).
 #pragma once
 
 #include "kvq_kernels.h"
@@ -75,34 +81,41 @@ __device__ __forceinline__ float code_rcp(float delta, bool& exact) {
 }
 
 // Codes of n elements x[i] against per-element (delta, zero, 1/delta):
-// guarded reciprocal first, the exact division for the whole wave when any
-// lane holds an element near a rounding boundary or flagged `exact`.
+// guarded reciprocal first.  An element index for which some lane is in the
+// band (or flagged `exact`) checks those lanes for exact ties, and the
+// lanes holding any other such element run the exact division (the other
+// lanes keep their codes; with none, the division is skipped).
 template <int N, int BITS>
 __device__ __forceinline__ void affine_codes(const float* x, const float* delta, const float* zp,
                                              const float* rcp, bool exact, uint32_t* code) {
   constexpr float levels = float((1 << BITS) - 1);
   constexpr float kBand = 0.5f - float(1 << BITS) * 0x1p-21f;
-  // the largest distance of a quotient from its rounded value (fmaxf skips
-  // the NaN of an infinite quotient, whose code the clamp decides)
-  float dev = 0.0f;
-  float c[N];
+  const uint64_t ex = __builtin_amdgcn_ballot_w64(exact);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const float a = x[i] - zp[i];
     const float y = a * rcp[i];
     const float r = __builtin_rintf(y);
-    dev = __builtin_fmaxf(dev, __builtin_fabsf(y - r));
+    const float d = y - r;   // NaN for an infinite quotient: never in the band
     // clamped (one median): an entry kept exact in a side table lies
     // outside the dense range; y is never NaN (x - zp is finite for inputs
     // below 2^127, and the reciprocal is finite), an infinite y clamps too
-    c[i] = __builtin_amdgcn_fmed3f(r, 0.0f, levels);
-  }
-  if (__builtin_amdgcn_ballot_w64(exact || dev >= kBand) != 0) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) code[i] = affine_code(x[i], delta[i], zp[i], levels);
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) code[i] = uint32_t(c[i]);
+    float ci = __builtin_amdgcn_fmed3f(r, 0.0f, levels);
+    if ((__builtin_amdgcn_ballot_w64(__builtin_fabsf(d) >= kBand) | ex) != 0) {
+      const bool near = exact || __builtin_fabsf(d) >= kBand;
+      const float h = r + __builtin_copysignf(0.5f, d);   // the half integer next to y
+      const bool tie = !exact && __builtin_fmaf(-h, delta[i], a) == 0.0f;
+      if (near) {
+        if (tie) {
+          ci = __builtin_amdgcn_fmed3f(__builtin_rintf(h), 0.0f, levels);
+        } else if (delta[i] != 0.0f) {
+          ci = __builtin_amdgcn_fmed3f(__builtin_rintf(__fdiv_rn(a, delta[i])), 0.0f, levels);
+        } else {
+          ci = 0.0f;
+        }
+      }
+    }
+    code[i] = uint32_t(ci);
   }
 }
 

@@ -119,26 +119,8 @@ __device__ __forceinline__ void affine_codes(const float* x, const float* delta,
   }
 }
 
-// All-reduce of min and max over the lanes l, l ^ S, l ^ 2S, ... (S = step,
-// a power of two; lanes sharing l mod S).
-template <int S>
-__device__ __forceinline__ void minmax_across(float& mn, float& mx) {
-  if constexpr (S <= 8) {
-    mn = fmin2(mn, dpp_mov<kRowRor8>(mn));
-    mx = fmax2(mx, dpp_mov<kRowRor8>(mx));
-  }
-  if constexpr (S <= 16) {
-    float a, b;
-    partner_pair<false>(mn, a, b); mn = fmin2(a, b);
-    partner_pair<false>(mx, a, b); mx = fmax2(a, b);
-  }
-  float a, b;
-  partner_pair<true>(mn, a, b); mn = fmin2(a, b);
-  partner_pair<true>(mx, a, b); mx = fmax2(a, b);
-}
-
 // All-reduce of min and max over aligned runs of N consecutive lanes (N =
-// 8, 16 or 32).
+// 4, 8, 16 or 32).
 template <int N>
 __device__ __forceinline__ void minmax_run(float& mn, float& mx) {
   mn = fmin2(mn, dpp_mov<kQuadXor1>(mn));
@@ -146,8 +128,10 @@ __device__ __forceinline__ void minmax_run(float& mn, float& mx) {
   mn = fmin2(mn, dpp_mov<kQuadXor2>(mn));
   mx = fmax2(mx, dpp_mov<kQuadXor2>(mx));
   constexpr int kHalfMirror = 0x141, kMirror = 0x140;
-  mn = fmin2(mn, dpp_mov<kHalfMirror>(mn));   // quads of a half row meet
-  mx = fmax2(mx, dpp_mov<kHalfMirror>(mx));
+  if constexpr (N >= 8) {
+    mn = fmin2(mn, dpp_mov<kHalfMirror>(mn));   // quads of a half row meet
+    mx = fmax2(mx, dpp_mov<kHalfMirror>(mx));
+  }
   if constexpr (N >= 16) {
     mn = fmin2(mn, dpp_mov<kMirror>(mn));     // halves of a row meet
     mx = fmax2(mx, dpp_mov<kMirror>(mx));
@@ -187,29 +171,12 @@ __device__ __forceinline__ void ext2_dpp_merge(Ext2& e) {
   const Ext2 o{dpp_mov<CTRL>(e.lo1), dpp_mov<CTRL>(e.lo2), dpp_mov<CTRL>(e.hi1), dpp_mov<CTRL>(e.hi2)};
   ext2_merge(e, o);
 }
-template <bool X32>
-__device__ __forceinline__ void ext2_swap_merge(Ext2& e) {
-  Ext2 a, b;
-  partner_pair<X32>(e.lo1, a.lo1, b.lo1);
-  partner_pair<X32>(e.lo2, a.lo2, b.lo2);
-  partner_pair<X32>(e.hi1, a.hi1, b.hi1);
-  partner_pair<X32>(e.hi2, a.hi2, b.hi2);
-  ext2_merge(a, b);
-  e = a;
-}
-// ext2 all-reduce over the lanes l, l ^ S, l ^ 2S, ... (as minmax_across)
-template <int S>
-__device__ __forceinline__ void ext2_across(Ext2& e) {
-  if constexpr (S <= 8) ext2_dpp_merge<kRowRor8>(e);
-  if constexpr (S <= 16) ext2_swap_merge<false>(e);
-  ext2_swap_merge<true>(e);
-}
-// ext2 all-reduce over aligned runs of N = 8 or 16 lanes (as minmax_run)
+// ext2 all-reduce over aligned runs of N = 4, 8 or 16 lanes (as minmax_run)
 template <int N>
 __device__ __forceinline__ void ext2_run(Ext2& e) {
   ext2_dpp_merge<kQuadXor1>(e);
   ext2_dpp_merge<kQuadXor2>(e);
-  ext2_dpp_merge<0x141>(e);   // half-row mirror
+  if constexpr (N >= 8) ext2_dpp_merge<0x141>(e);   // half-row mirror
   if constexpr (N >= 16) ext2_dpp_merge<0x140>(e);   // row mirror
 }
 // The dense range [lo, hi] and the kept entry's value kv; returns 1 (the
@@ -283,8 +250,10 @@ __device__ __forceinline__ void widen_piece(const Piece<DT>& pc, float* out) {
 
 // ----------------------------------------------------------------------------
 // One key group of G rows, 256 threads: per-channel min / max over the rows,
-// delta and zero point, the packed code rows.  Thread t holds piece t % kTPR
-// (channels kVE * (t % kTPR) ..) of rows t / kTPR + kRPP * i.
+// delta and zero point, the packed code rows.  The kRW = 64 / kTPR rows a
+// wave holds per pass sit in consecutive lanes, so the reduction over them
+// runs within DPP rows: lane l of wave w holds piece l / kRW (channels kVE *
+// (l / kRW) ..) of rows kRW w + l % kRW + kRPP * i.
 // ----------------------------------------------------------------------------
 template <int DT, int D, int G>
 struct KeyRows {
@@ -292,12 +261,23 @@ struct KeyRows {
   static_assert(kRPT >= 1 && G % RowSplit<DT, D>::kRPP == 0, "group rows per thread");
   Piece<DT> raw[kRPT];
 };
+template <int DT, int D>
+struct KeyLane {
+  static constexpr int kRW = 64 / RowSplit<DT, D>::kTPR;   // rows per wave and pass
+  int cs, r0;
+  __device__ KeyLane() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    cs = lane / kRW;
+    r0 = wave * kRW + lane % kRW;
+  }
+};
 
 // This thread's pieces of a key group's rows.
 template <int DT, int D, int G, class Rows>
 __device__ __forceinline__ void load_key_rows(const Rows& rows, KeyRows<DT, D, G>& kr) {
   using RS = RowSplit<DT, D>;
-  const int t = threadIdx.x, cs = t % RS::kTPR, r0 = t / RS::kTPR;
+  const KeyLane<DT, D> kl;
+  const int cs = kl.cs, r0 = kl.r0;
 #pragma unroll
   for (int i = 0; i < KeyRows<DT, D, G>::kRPT; ++i)
     load_piece<DT>(rows.row(r0 + i * RS::kRPP) + cs * RS::kVE * Elem<DT>::bytes, kr.raw[i]);
@@ -311,7 +291,9 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
   constexpr int kVE = RS::kVE, kTPR = RS::kTPR, kRPP = RS::kRPP;
   constexpr int kRPT = KeyRows<DT, D, G>::kRPT;
   constexpr float kLevels = float((1 << BITS) - 1);
-  const int t = threadIdx.x, cs = t % kTPR, r0 = t / kTPR;
+  constexpr int kRW = KeyLane<DT, D>::kRW;
+  const KeyLane<DT, D> kl;
+  const int t = threadIdx.x, cs = kl.cs, r0 = kl.r0;
   const int lane = t & 63, wave = t >> 6;
   const Piece<DT>* raw = kr.raw;
   float x[kRPT][kVE];
@@ -326,8 +308,8 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
       Ext2 ex2 = ext2_of(x[0][e]);
 #pragma unroll
       for (int i = 1; i < kRPT; ++i) ext2_add(ex2, x[i][e]);
-      ext2_across<kTPR>(ex2);
-      if (lane < kTPR) {
+      ext2_run<kRW>(ex2);
+      if (lane % kRW == 0) {
         s_red[wave][cs * kVE + e] = ex2.lo1;
         s_red[4 + wave][cs * kVE + e] = ex2.hi1;
         s_red[8 + wave][cs * kVE + e] = ex2.lo2;
@@ -345,9 +327,9 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
         mn[e] = fmin2(mn[e], x[i][e]);
         mx[e] = fmax2(mx[e], x[i][e]);
       }
-      minmax_across<kTPR>(mn[e], mx[e]);
+      minmax_run<kRW>(mn[e], mx[e]);
     }
-    if (lane < kTPR) {
+    if (lane % kRW == 0) {
 #pragma unroll
       for (int e = 0; e < kVE; ++e) {
         s_red[wave][cs * kVE + e] = mn[e];

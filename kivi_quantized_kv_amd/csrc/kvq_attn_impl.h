@@ -802,8 +802,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 16 ? 4 : valu_waves<DT, D, BITS, MO
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the split partials: M = max_j m_j,
 // L = sum_j 2^(m_j - M) l_j, out = sum_j 2^(m_j - M) o_j / L.
-// One workgroup per (32-channel block, q head, batch), one round of loads
-// up to 64 splits: thread (slot, c4) folds channels [4 c4, 4 c4 + 4) of the
+// Above 64 splits: one workgroup per (32-channel block, q head, batch), one
+// round of loads up to 64 splits: thread (slot, c4) folds channels [4 c4, 4 c4 + 4) of the
 // block for splits slot, slot + 32, ... (float4 loads) into a running
 // state of its own (local max, sums); the 32 slot states then meet through
 // LDS by the same rule, with each slot's weight 2^(M_slot - M) computed once.
@@ -917,9 +917,81 @@ hipError_t launch_attn_valu(const AttnArgs& a, int B, hipStream_t s) {
   hipLaunchKernelGGL((k_attn_valu<DT, D, BITS, 4, MODE>), dim3(a.n_split, a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+// Merge for up to 64 splits: one wave per (batch, q head) row.  Lane l
+// folds float4 column l % kQ (kQ = D / 4) over splits l / kQ, l / kQ + kS,
+// ... (kS = 64 / kQ slices), 16 per slice per round of loads, in
+// registers; the slices then meet across lanes.
+template <int DT, int D>
+__global__ __launch_bounds__(64) void k_merge_row(AttnArgs a) {
+  constexpr int kQ = D / 4;
+  constexpr int kS = 64 / kQ;
+  constexpr int kU = 16;
+  const int lane = threadIdx.x, c4 = lane % kQ, ss = lane / kQ;
+  const int64_t row = blockIdx.x;
+  const int ns = a.n_split;
+  const float2* ml = reinterpret_cast<const float2*>(partial_ml(a, row, 0));
+  const float* ob = partial_o(a, row, 0, D) + 4 * c4;
+  float M = -__builtin_inff(), L = 0.f;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = ss; j0 < ns; j0 += kS * kU) {
+    float2 p[kU];
+    float4 o[kU];
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int j = j0 + kS * i;
+      const int jj = j < ns ? j : ns - 1;   // in bounds; weight 0 below
+      p[i] = ml[jj];
+      o[i] = *reinterpret_cast<const float4*>(ob + int64_t(jj) * D);
+      if (j >= ns) p[i].x = -__builtin_inff();
+    }
+    float cm = p[0].x;
+#pragma unroll
+    for (int i = 1; i < kU; ++i) cm = __builtin_fmaxf(cm, p[i].x);
+    if (cm > M) {
+      const float f = __builtin_amdgcn_exp2f(M - cm);   // 0 while M = -inf
+      acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+      L *= f;
+      M = cm;
+    }
+    const float Mref = M == -__builtin_inff() ? 0.f : M;
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const float w = __builtin_amdgcn_exp2f(p[i].x - Mref);   // 0 for empty splits
+      acc.x = __builtin_fmaf(w, o[i].x, acc.x);
+      acc.y = __builtin_fmaf(w, o[i].y, acc.y);
+      acc.z = __builtin_fmaf(w, o[i].z, acc.z);
+      acc.w = __builtin_fmaf(w, o[i].w, acc.w);
+      L = __builtin_fmaf(w, p[i].y, L);
+    }
+  }
+  // the slices meet: lanes kQ, 2 kQ apart hold the same column
+#pragma unroll
+  for (int x = kQ; x < 64; x <<= 1) {
+    const float M2 = __shfl_xor(M, x, 64), L2 = __shfl_xor(L, x, 64);
+    const float4 a2 = {__shfl_xor(acc.x, x, 64), __shfl_xor(acc.y, x, 64), __shfl_xor(acc.z, x, 64),
+                       __shfl_xor(acc.w, x, 64)};
+    const float Mn = __builtin_fmaxf(M, M2);
+    const float Mr = Mn == -__builtin_inff() ? 0.f : Mn;
+    const float f1 = __builtin_amdgcn_exp2f(M - Mr), f2 = __builtin_amdgcn_exp2f(M2 - Mr);
+    acc.x = __builtin_fmaf(acc.x, f1, a2.x * f2);
+    acc.y = __builtin_fmaf(acc.y, f1, a2.y * f2);
+    acc.z = __builtin_fmaf(acc.z, f1, a2.z * f2);
+    acc.w = __builtin_fmaf(acc.w, f1, a2.w * f2);
+    L = __builtin_fmaf(L, f1, L2 * f2);
+    M = Mn;
+  }
+  if (ss == 0) {
+    float4 r = {acc.x / L, acc.y / L, acc.z / L, acc.w / L};
+    *reinterpret_cast<float4*>(a.out + row * D + 4 * c4) = r;
+  }
+}
+
 template <int DT, int D>
 hipError_t launch_merge(const AttnArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((k_merge<DT, D>), dim3(D / 32, a.Hq, B), dim3(256), 0, s, a);
+  if (a.n_split <= 64)
+    hipLaunchKernelGGL((k_merge_row<DT, D>), dim3(unsigned(int64_t(B) * a.Hq)), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_merge<DT, D>), dim3(D / 32, a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -117,11 +117,6 @@ template <int DT, int D, int BITS> struct QuantValuesFn {
     return launch_quant_values<DT, D, BITS>(a, n, B, H, s);
   }
 };
-template <int DT, int D, int BITS> struct CopyFpFn {
-  static hipError_t run(const FpCopyArgs& a, int64_t n, int B, int H, hipStream_t s) {
-    return launch_copy_fp<DT, D>(a, n, B, H, s);
-  }
-};
 template <int DT, int D, int BITS> struct AppendFn {
   static hipError_t run(const AppendArgs& a, int B, int H, hipStream_t s) {
     return launch_append<DT, D, BITS>(a, B, H, s);
@@ -184,8 +179,9 @@ template <int DT, int D, int BITS> struct AttnValuDirectOkFn {
   static bool run() { return attn_valu_direct_ok<DT, D, BITS>(); }
 };
 
-// Prefill of one half: fp copies of sinks and residual tokens, then the
-// quantized range (keys per group or values per 32-token step).
+// Prefill of one half in one launch: the quantized range (keys per group or
+// values per 32-token step) and, in the workgroups past it, the fp copies
+// of the sinks and residual tokens.
 kvq_status prefill_half(const kvq_config* c, const kvq_cache* k, const kvq_tensor& x,
                         int64_t n_tokens, void* stream, bool keys) {
   kvq_status st = check_config(c);
@@ -195,36 +191,37 @@ kvq_status prefill_half(const kvq_config* c, const kvq_cache* k, const kvq_tenso
   if (n_tokens < 0) return KVQ_EINVAL;
   if (n_tokens > c->capacity) return KVQ_ECAPACITY;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t S = c->sink, R = c->residual, G = c->group;
+  const int64_t S = c->sink, R = c->residual, G = c->group, D = c->head_dim;
   const int64_t Q = quantized_count(n_tokens, S, R, G);
   const int64_t n_sink = n_tokens < S ? n_tokens : S;
   const int64_t n_res = n_tokens > S ? n_tokens - S - Q : 0;
   const int B = c->batch, H = c->n_kv_heads;
-  if (n_sink + n_res > 0) {
-    FpCopyArgs f{};
-    f.src = x.ptr; f.sb = x.stride_b; f.sh = x.stride_h; f.st = x.stride_t;
-    f.sink = keys ? k->k_sink : k->v_sink;
-    f.resid = keys ? k->k_resid : k->v_resid;
-    f.n_sink = n_sink; f.first_resid = S + Q; f.S = S; f.ring = R + G; f.H = H;
-    if (dispatch3<CopyFpFn>(c, f, n_sink + n_res, B, H, s) != hipSuccess) return KVQ_EHIP;
-  }
-  if (Q > 0) {
-    QuantArgs q{};
-    q.src = x.ptr; q.sb = x.stride_b; q.sh = x.stride_h; q.st = x.stride_t;
-    q.codes = keys ? k->k_codes : k->v_codes;
-    q.scale = keys ? k->k_scale : k->v_scale;
-    q.zero = keys ? k->k_zero : k->v_zero;
-    q.S = S; q.qcap = kvq_qcap(c); q.H = H; q.G = int(G);
-    q.outliers = c->outliers;
-    q.oidx = keys ? k->k_oidx : k->v_oidx;
-    q.oval = static_cast<uint8_t*>(keys ? k->k_oval : k->v_oval);
-    // with a window only the groups of the last qcap quantized tokens are
-    // kept (older ones would be evicted by them), each storage slot once
-    const int64_t k_first = Q > q.qcap ? (Q - q.qcap) / G : 0;
-    q.k0 = keys ? k_first : k_first * G / 32;
-    const int64_t n_units = keys ? Q / G - k_first : (Q - k_first * G) / 32;
-    hipError_t e = keys ? dispatch3<QuantKeysFn>(c, q, n_units, B, H, s)
-                        : dispatch3<QuantValuesFn>(c, q, n_units, B, H, s);
+  QuantArgs q{};
+  q.src = x.ptr; q.sb = x.stride_b; q.sh = x.stride_h; q.st = x.stride_t;
+  q.codes = keys ? k->k_codes : k->v_codes;
+  q.scale = keys ? k->k_scale : k->v_scale;
+  q.zero = keys ? k->k_zero : k->v_zero;
+  q.S = S; q.qcap = kvq_qcap(c); q.H = H; q.G = int(G);
+  q.outliers = c->outliers;
+  q.oidx = keys ? k->k_oidx : k->v_oidx;
+  q.oval = static_cast<uint8_t*>(keys ? k->k_oval : k->v_oval);
+  // with a window only the groups of the last qcap quantized tokens are
+  // kept (older ones would be evicted by them), each storage slot once
+  const int64_t k_first = Q > q.qcap ? (Q - q.qcap) / G : 0;
+  q.k0 = keys ? k_first : k_first * G / 32;
+  q.n_units = Q > 0 ? (keys ? Q / G - k_first : (Q - k_first * G) / 32) : 0;
+  FpCopyArgs& f = q.fp;
+  f.src = x.ptr; f.sb = x.stride_b; f.sh = x.stride_h; f.st = x.stride_t;
+  f.sink = keys ? k->k_sink : k->v_sink;
+  f.resid = keys ? k->k_resid : k->v_resid;
+  f.n_sink = n_sink; f.first_resid = S + Q; f.S = S; f.ring = R + G; f.H = H;
+  q.n_fp_rows = n_sink + n_res;
+  const int64_t vec_per_row = D * int64_t(kvq_dtype_bytes(c->dtype)) / 16;
+  const int64_t n_copy = (q.n_fp_rows * vec_per_row + 255) / 256;
+  const int64_t n_blocks = q.n_units + n_copy;
+  if (n_blocks > 0) {
+    hipError_t e = keys ? dispatch3<QuantKeysFn>(c, q, n_blocks, B, H, s)
+                        : dispatch3<QuantValuesFn>(c, q, n_blocks, B, H, s);
     if (e != hipSuccess) return KVQ_EHIP;
   }
   return KVQ_OK;

@@ -31,6 +31,11 @@ struct QuantArgs {
   uint8_t* oidx;            // side table (outliers != 0): positions, laid out as scale
   uint8_t* oval;            // and the kept values in the input dtype
   int H, G, outliers;
+  // Workgroups x >= n_units copy the full-precision rows instead (sinks,
+  // then the residual tokens: n_fp_rows per head, 256 16-byte vectors per
+  // workgroup).
+  FpCopyArgs fp;
+  int64_t n_units, n_fp_rows;
 };
 
 struct AppendArgs {
@@ -96,11 +101,9 @@ __device__ __forceinline__ float* partial_ml(const AttnArgs& a, int64_t row, int
 }
 
 template <int DT, int D, int BITS>
-hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_groups, int B, int H, hipStream_t s);
+hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_blocks, int B, int H, hipStream_t s);
 template <int DT, int D, int BITS>
-hipError_t launch_quant_values(const QuantArgs& a, int64_t n_steps, int B, int H, hipStream_t s);
-template <int DT, int D>
-hipError_t launch_copy_fp(const FpCopyArgs& a, int64_t n_rows, int B, int H, hipStream_t s);
+hipError_t launch_quant_values(const QuantArgs& a, int64_t n_blocks, int B, int H, hipStream_t s);
 template <int DT, int D, int BITS>
 hipError_t launch_append(const AppendArgs& a, int B, int H, hipStream_t s);
 // MODE bit 0: side tables; bit 1: pre-RoPE keys.

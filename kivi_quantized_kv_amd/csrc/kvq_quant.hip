@@ -1,5 +1,6 @@
 // Explicit instantiations of the quantize kernels (templates in
-// kvq_quant_impl.h) for the widths whose codes fill whole bytes (2, 4 and 8 bits) and the full-precision row copy.
+// kvq_quant_impl.h) for the widths whose codes fill whole bytes (2, 4 and 8
+// bits).
 #include "kvq_quant_impl.h"
 
 namespace kvq {
@@ -16,12 +17,5 @@ namespace kvq {
 KVQ_QUANT_INST_W(2)
 KVQ_QUANT_INST_W(4)
 KVQ_QUANT_INST_W(8)
-
-template hipError_t launch_copy_fp<DT_F32, 64>(const FpCopyArgs&, int64_t, int, int, hipStream_t);
-template hipError_t launch_copy_fp<DT_F32, 128>(const FpCopyArgs&, int64_t, int, int, hipStream_t);
-template hipError_t launch_copy_fp<DT_F16, 64>(const FpCopyArgs&, int64_t, int, int, hipStream_t);
-template hipError_t launch_copy_fp<DT_F16, 128>(const FpCopyArgs&, int64_t, int, int, hipStream_t);
-template hipError_t launch_copy_fp<DT_BF16, 64>(const FpCopyArgs&, int64_t, int, int, hipStream_t);
-template hipError_t launch_copy_fp<DT_BF16, 128>(const FpCopyArgs&, int64_t, int, int, hipStream_t);
 
 }  // namespace kvq

@@ -536,15 +536,18 @@ __device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0
 // ----------------------------------------------------------------------------
 // Prefill kernels
 // ----------------------------------------------------------------------------
+// One workgroup's share of the full-precision rows of head (b, h): 16-byte
+// vectors blk * 256 .. blk * 256 + 255 of the n_rows rows (sinks first,
+// then the residual tokens, each to its sink or ring slot).
 template <int DT, int D>
-__global__ __launch_bounds__(64) void k_copy_fp_rows(FpCopyArgs a) {
-  // grid: x = fp row (sinks first, then residual tokens), y = head, z = batch
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t row = blockIdx.x;
-  const int64_t tok = row < a.n_sink ? row : a.first_resid + (row - a.n_sink);
+__device__ __forceinline__ void copy_fp_block(const FpCopyArgs& a, int64_t n_rows, int64_t blk, int h, int b) {
   constexpr int EB = Elem<DT>::bytes;
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.src) +
-                       (b * a.sb + h * a.sh + tok * a.st) * EB;
+  constexpr int kVec = D * EB / 16;  // 16-byte vectors per row
+  const int64_t v = blk * 256 + threadIdx.x;
+  const int64_t row = v / kVec;
+  if (row >= n_rows) return;
+  const int64_t tok = row < a.n_sink ? row : a.first_resid + (row - a.n_sink);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.src) + (b * a.sb + h * a.sh + tok * a.st) * EB;
   uint8_t* dst;
   if (tok < a.S) {
     dst = reinterpret_cast<uint8_t*>(a.sink) + ((int64_t(b) * a.H + h) * a.S + tok) * D * EB;
@@ -552,20 +555,24 @@ __global__ __launch_bounds__(64) void k_copy_fp_rows(FpCopyArgs a) {
     const int64_t slot = (tok - a.S) % a.ring;
     dst = reinterpret_cast<uint8_t*>(a.resid) + ((int64_t(b) * a.H + h) * a.ring + slot) * D * EB;
   }
-  constexpr int kVec = D * EB / 16;  // 16-byte vectors per row
-  for (int v = threadIdx.x; v < kVec; v += 64)
-    reinterpret_cast<uint4*>(dst)[v] = reinterpret_cast<const uint4*>(src)[v];
+  reinterpret_cast<uint4*>(dst)[v % kVec] = reinterpret_cast<const uint4*>(src)[v % kVec];
 }
 
 // grid: x = unit (key group, or 32-token value step) of the quantized range
 // from unit a.k0 on, y = head, z = batch; unit k is stored at storage row
 // (k * unit tokens) mod qcap.  One unit per workgroup: many small resident
 // workgroups at different phases overlap loads with arithmetic better than
-// fewer workgroups streaming several units each (measured).
+// fewer workgroups streaming several units each (measured).  Workgroups
+// x >= n_units copy the full-precision rows, so a prefill half is one
+// launch.
 template <int DT, int D, int BITS, int G>
 __global__ __launch_bounds__(256) void k_quant_keys(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) float s_red[16][D];
   __shared__ __attribute__((aligned(16))) float s_par[6][D];
+  if (blockIdx.x >= a.n_units) {
+    copy_fp_block<DT, D>(a.fp, a.n_fp_rows, blockIdx.x - a.n_units, blockIdx.y, blockIdx.z);
+    return;
+  }
   const int64_t k = a.k0 + blockIdx.x;
   const int64_t ks = k % (a.qcap / G);              // storage slot of group k
   const int h = blockIdx.y, b = blockIdx.z;
@@ -584,6 +591,10 @@ __global__ __launch_bounds__(256) void k_quant_keys(QuantArgs a) {
 template <int DT, int D, int BITS>
 __global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[D * kStepPitch];
+  if (blockIdx.x >= a.n_units) {
+    copy_fp_block<DT, D>(a.fp, a.n_fp_rows, blockIdx.x - a.n_units, blockIdx.y, blockIdx.z);
+    return;
+  }
   const int64_t st = a.k0 + blockIdx.x;
   const int64_t r0 = (32 * st) % a.qcap;            // storage row of the step's first token
   const int h = blockIdx.y, b = blockIdx.z;
@@ -669,22 +680,17 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 // launchers
 // ----------------------------------------------------------------------------
 template <int DT, int D, int BITS>
-hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_units, int B, int H, hipStream_t s) {
-  const dim3 grid(unsigned(n_units), H, B);
+hipError_t launch_quant_keys(const QuantArgs& a, int64_t n_blocks, int B, int H, hipStream_t s) {
+  const dim3 grid(unsigned(n_blocks), H, B);
   if (a.G == 32) hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 32>), grid, dim3(256), 0, s, a);
   else if (a.G == 64) hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 64>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_quant_keys<DT, D, BITS, 128>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <int DT, int D, int BITS>
-hipError_t launch_quant_values(const QuantArgs& a, int64_t n_units, int B, int H, hipStream_t s) {
-  hipLaunchKernelGGL((k_quant_values<DT, D, BITS>), dim3(unsigned(n_units), H, B), dim3(256), 0,
+hipError_t launch_quant_values(const QuantArgs& a, int64_t n_blocks, int B, int H, hipStream_t s) {
+  hipLaunchKernelGGL((k_quant_values<DT, D, BITS>), dim3(unsigned(n_blocks), H, B), dim3(256), 0,
                      s, a);
-  return hipGetLastError();
-}
-template <int DT, int D>
-hipError_t launch_copy_fp(const FpCopyArgs& a, int64_t n_rows, int B, int H, hipStream_t s) {
-  hipLaunchKernelGGL((k_copy_fp_rows<DT, D>), dim3(unsigned(n_rows), H, B), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 template <int DT, int D, int BITS>

@@ -415,39 +415,50 @@ __device__ __forceinline__ void key_group(const KeyRows<DT, D, G>& kr, float* k_
 // ----------------------------------------------------------------------------
 constexpr int kStepPitch = 36;   // bytes per channel row of the LDS code tile
 
+// Value rows of a step: thread t holds kVE channels of token t / 8 (8
+// threads per row, one token each), as kNV 16-byte vectors kSeg channels
+// apart, so that each load instruction reads whole 128-byte spans of rows.
 template <int DT, int D>
-struct StepRows {
-  static constexpr int kTPT = 32 / RowSplit<DT, D>::kRPP;   // tokens per thread
-  static_assert(kTPT >= 1 && 32 % RowSplit<DT, D>::kRPP == 0, "tokens per pass");
-  Piece<DT> raw[kTPT];
+struct VSplit {
+  static constexpr int kVE = D == 128 ? 16 : 8;    // channels per thread
+  static constexpr int kTPR = D / kVE;             // threads per row: 8
+  static constexpr int kEPV = 16 / Elem<DT>::bytes;  // channels per vector
+  static constexpr int kNV = kVE / kEPV;           // vectors per thread
+  static constexpr int kSeg = D / kNV;             // channels between a thread's vectors
+  static_assert(kTPR * 32 == 256, "one token per thread");
+  // channel of element e of thread column cs
+  static __device__ __forceinline__ int chan(int cs, int e) { return (e / kEPV) * kSeg + cs * kEPV + e % kEPV; }
 };
 
-// This thread's pieces of the 32 value rows of a step.
+template <int DT, int D>
+struct StepRows {
+  uint4 raw[VSplit<DT, D>::kNV];
+};
+
+// This thread's vectors of its value row of a step.
 template <int DT, int D, class Rows>
 __device__ __forceinline__ void load_step_rows(const Rows& rows, StepRows<DT, D>& sr) {
-  using RS = RowSplit<DT, D>;
-  const int t = threadIdx.x, cs = t % RS::kTPR, r0 = t / RS::kTPR;
+  using VS = VSplit<DT, D>;
+  const int t = threadIdx.x, cs = t % VS::kTPR;
+  const uint8_t* row = rows.row(t / VS::kTPR);
 #pragma unroll
-  for (int j = 0; j < StepRows<DT, D>::kTPT; ++j)
-    load_piece<DT>(rows.row(r0 + j * RS::kRPP) + cs * RS::kVE * Elem<DT>::bytes, sr.raw[j]);
+  for (int i = 0; i < VS::kNV; ++i)
+    sr.raw[i] = *reinterpret_cast<const uint4*>(row + (i * VS::kSeg + cs * VS::kEPV) * Elem<DT>::bytes);
 }
 
 template <int DT, int D, int BITS>
 __device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0, float* v_scale,
                                            float* v_zero, uint8_t* v_codes_head, Side side,
                                            uint8_t* s_codes) {
-  using RS = RowSplit<DT, D>;
+  using VS = VSplit<DT, D>;
   using VL = VLayout<BITS>;
-  constexpr int kVE = RS::kVE, kTPR = RS::kTPR, kRPP = RS::kRPP;
-  constexpr int kTPT = StepRows<DT, D>::kTPT;
+  constexpr int kVE = VS::kVE, kTPR = VS::kTPR;
   constexpr float kLevels = float((1 << BITS) - 1);
-  const int t = threadIdx.x, cs = t % kTPR, r0 = t / kTPR;
-  const Piece<DT>* raw = sr.raw;
-#pragma unroll
-  for (int j = 0; j < kTPT; ++j) {
-    const int tok = r0 + j * kRPP;
+  const int t = threadIdx.x, cs = t % kTPR, tok = t / kTPR;
+  {
     float x[kVE];
-    widen_piece<DT>(raw[j], x);
+#pragma unroll
+    for (int i = 0; i < VS::kNV; ++i) widen16<DT>(sr.raw[i], x + i * VS::kEPV);
     float mn, mx;
     if (side.on) {
       Ext2 ex2 = ext2_of(x[0]);
@@ -463,7 +474,7 @@ __device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0
       } else {
 #pragma unroll
         for (int e = 0; e < kVE; ++e)
-          if (x[e] == kv) store_side<DT>(side.idx, side.val, u0 + tok, cs * kVE + e, x[e]);
+          if (x[e] == kv) store_side<DT>(side.idx, side.val, u0 + tok, VS::chan(cs, e), x[e]);
       }
     } else {
       mn = x[0];
@@ -492,7 +503,7 @@ __device__ __forceinline__ void value_step(const StepRows<DT, D>& sr, int64_t u0
     uint32_t code[kVE];
     affine_codes<kVE, BITS>(x, delta, zp, rcp, exact, code);
 #pragma unroll
-    for (int e = 0; e < kVE; ++e) s_codes[(cs * kVE + e) * kStepPitch + tok] = uint8_t(code[e]);
+    for (int e = 0; e < kVE; ++e) s_codes[VS::chan(cs, e) * kStepPitch + tok] = uint8_t(code[e]);
   }
   __syncthreads();
   // units of this step: unit x of the block holds channel d = 16 n + jj for

@@ -225,6 +225,54 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+
+def stream_read_ceiling(layers, n_calls: int):
+    """A measured read ceiling for the decode call's bytes: the plain
+    streaming-read kernel of libkvq_probe.so over each layer cache's own
+    buffers (every byte of each, layer caches rotated as in the attention
+    timing, so that each pass reads from HBM), for a few launch shapes; the
+    fastest is reported.  None when the probe library is not built."""
+    path = os.path.join(ROOT, "kivi_quantized_kv_amd", "libkvq_probe.so")
+    if not os.path.exists(path):
+        return None
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(path)
+    lib.kvqprobe_stream_read.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    sets = []
+    for c in layers:
+        bufs = [getattr(c, n) for n in type(c).BUFFERS if getattr(c, n).numel() > 0]
+        ptrs = (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+        sizes = (ctypes.c_int64 * len(bufs))(*[b.numel() * b.element_size() for b in bufs])
+        sets.append((ptrs, sizes, len(bufs), sum(sizes)))
+    grids = (256, 512, 1024)
+    out = torch.empty(max(grids) * 512, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for grid, u in ((256, 8), (256, 4), (512, 4), (1024, 4)):
+        def run(count):
+            for i in range(count):
+                ptrs, sizes, n, _ = sets[i % len(sets)]
+                rc = lib.kvqprobe_stream_read(ptrs, sizes, n, ctypes.c_void_p(out.data_ptr()), grid, u,
+                                              ctypes.c_void_p(stream))
+                if rc != 0:
+                    raise RuntimeError(f"kvqprobe_stream_read failed: {rc}")
+        run(20)
+        e0, e1 = _events()
+        torch.cuda.synchronize()
+        e0.record()
+        run(n_calls)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n_calls * 1e3
+        if best is None or us < best[0]:
+            best = (us, grid, u)
+    nbytes = sum(s[3] for s in sets) / len(sets)
+    return {"us": round(best[0], 3), "bytes": int(nbytes), "GBps": round(nbytes / (best[0] * 1e3), 1),
+            "launch": f"{best[1]} workgroups x 512 threads, {best[2]} 16-byte loads in flight per thread"}
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,6 +442,7 @@ def main():
         groups.append(g0.elapsed_time(g1) / 20 * 1e3)
     bytes_per_call = sum(algorithmic_bytes(w, T) for T in attn_T) / n_calls
     achieved = bytes_per_call / (mean_attn_ms / 1e3) / 1e9
+    read_ceiling = stream_read_ceiling(layers, n_calls)
     splits = decode_splits(w, n_tok[0], cus)
     pbytes = prefill_bytes(w, T0, cfg.qcap)
     detail = {
@@ -402,6 +451,11 @@ def main():
                                  "p10": round(float(np.percentile(groups, 10)), 3),
                                  "p90": round(float(np.percentile(groups, 90)), 3)},
         "attn_calls_timed": n_calls,
+        # the same cache buffers read by a plain streaming kernel, and the
+        # decode call's rate as a fraction of that measured ceiling
+        "stream_read": read_ceiling,
+        "attn_over_stream_read": (None if read_ceiling is None else
+                                  round(achieved / read_ceiling["GBps"], 4)),
         "step_us_minus_attn_us": round(ms_per_step * 1e3 - mean_attn_ms * 1e3, 3),
         "append_plain_us": None if append_plain_us is None else round(append_plain_us, 3),
         "append_freeze_us": round(append_freeze_us, 3),
@@ -447,7 +501,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"kvq_decode_attention: {attn_kernel_name(w)} (split-K attention) + k_merge; "
+            "kernel": (f"kvq_decode_attention: {attn_kernel_name(w)} (split-K attention) + the split merge; "
                        f"mean over {n_calls} back-to-back calls, HIP events on the launch stream"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -1,7 +1,9 @@
 """Build libkvq.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
 Every source is compiled on each call; objects are compiled in parallel and
-linked into kivi_quantized_kv_amd/libkvq.so.
+linked into kivi_quantized_kv_amd/libkvq.so.  The streaming-read probe that
+the benchmark uses as a measured read ceiling is linked on its own into
+kivi_quantized_kv_amd/libkvq_probe.so.
 """
 from __future__ import annotations
 
@@ -14,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
+PROBE_OUT = os.path.join(HERE, "libkvq_probe.so")
+PROBE_SOURCES = ["probe_read.hip"]
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["kvq_quant.hip", "kvq_quant_any.hip", "kvq_attn.hip", "kvq_attn_any.hip",
            "kvq_attn_rope.hip", "kvq_attn_rope_any.hip", "kvq_gqa.hip", "kvq_gqa_outl.hip",
@@ -39,19 +43,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, OUT)
+    shutil.move(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [s for s in SOURCES + PROBE_SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES if s in objs], OUT)
+    _link([objs[s] for s in PROBE_SOURCES if s in objs], PROBE_OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", PROBE_OUT)
     return OUT
 
 

@@ -35,6 +35,22 @@ def test_library_exports_every_declared_entry_point():
         assert hasattr(lib, name)
 
 
+def test_probe_library_is_separate_from_the_abi():
+    """The streaming-read probe the benchmark times lives in its own library:
+    libkvq.so exports only kvq_* entry points, libkvq_probe.so its one call."""
+    kvq, _ = _lib()
+    probe = os.path.join(os.path.dirname(kvq.LIB_PATH), "libkvq_probe.so")
+    if not os.path.exists(probe):
+        pytest.skip("libkvq_probe.so not built")
+    main = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    assert "kvqprobe_" not in main
+    out = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True,
+                         check=True).stdout
+    assert re.search(r"\bT kvqprobe_stream_read$", out, re.M)
+    assert "kvq_decode_attention" not in out
+
+
 def _header_sizes(cfg):
     """Compile a tiny C program against kvq.h and print its closed forms."""
     src = r"""

@@ -60,7 +60,7 @@ __device__ __forceinline__ float load1(const void* base, int64_t i) {
 // code section).
 __device__ __forceinline__ void affine_params(float mn, float mx, float levels, float& delta,
                                               float& zp) {
-  delta = __fdiv_rn(mx - mn, levels);
+  delta = __fdiv_rn((mx - mn) + 0.0f, levels);   // a range of zeros of either signs: +0
   zp = mn + 0.0f;
 }
 

@@ -119,22 +119,44 @@ __device__ __forceinline__ void affine_codes(const float* x, const float* delta,
   }
 }
 
+// min / max of v and the v of the lane a DPP pattern selects, in one
+// instruction (the move fused into the operation; inline assembly, as the
+// compiler's min / max carry an operand canonicalization that blocks the
+// fusion; the s_nop gives the two wait states a DPP read needs after the
+// VALU write of its source, which the compiler does not see in the asm).  For finite inputs the result equals the IEEE minimum / maximum
+// except that a +0 / -0 pair may give either zero: the reductions' callers
+// take zp = mn + 0 and delta from (mx - mn) + 0, which are then the same.
+#define KVQ_DPP_MINMAX(NAME, OP, CTRL)                                                             \
+  __device__ __forceinline__ float NAME(float v) {                                                \
+    float d;                                                                                       \
+    asm volatile("s_nop 1\n\t" OP " %0, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf" : "=v"(d) : "v"(v)); \
+    return d;                                                                                      \
+  }
+KVQ_DPP_MINMAX(min_qx1, "v_min_f32_dpp", "quad_perm:[1,0,3,2]")
+KVQ_DPP_MINMAX(max_qx1, "v_max_f32_dpp", "quad_perm:[1,0,3,2]")
+KVQ_DPP_MINMAX(min_qx2, "v_min_f32_dpp", "quad_perm:[2,3,0,1]")
+KVQ_DPP_MINMAX(max_qx2, "v_max_f32_dpp", "quad_perm:[2,3,0,1]")
+KVQ_DPP_MINMAX(min_hmir, "v_min_f32_dpp", "row_half_mirror")
+KVQ_DPP_MINMAX(max_hmir, "v_max_f32_dpp", "row_half_mirror")
+KVQ_DPP_MINMAX(min_mir, "v_min_f32_dpp", "row_mirror")
+KVQ_DPP_MINMAX(max_mir, "v_max_f32_dpp", "row_mirror")
+#undef KVQ_DPP_MINMAX
+
 // All-reduce of min and max over aligned runs of N consecutive lanes (N =
 // 4, 8, 16 or 32).
 template <int N>
 __device__ __forceinline__ void minmax_run(float& mn, float& mx) {
-  mn = fmin2(mn, dpp_mov<kQuadXor1>(mn));
-  mx = fmax2(mx, dpp_mov<kQuadXor1>(mx));
-  mn = fmin2(mn, dpp_mov<kQuadXor2>(mn));
-  mx = fmax2(mx, dpp_mov<kQuadXor2>(mx));
-  constexpr int kHalfMirror = 0x141, kMirror = 0x140;
+  mn = min_qx1(mn);
+  mx = max_qx1(mx);
+  mn = min_qx2(mn);
+  mx = max_qx2(mx);
   if constexpr (N >= 8) {
-    mn = fmin2(mn, dpp_mov<kHalfMirror>(mn));   // quads of a half row meet
-    mx = fmax2(mx, dpp_mov<kHalfMirror>(mx));
+    mn = min_hmir(mn);   // quads of a half row meet
+    mx = max_hmir(mx);
   }
   if constexpr (N >= 16) {
-    mn = fmin2(mn, dpp_mov<kMirror>(mn));     // halves of a row meet
-    mx = fmax2(mx, dpp_mov<kMirror>(mx));
+    mn = min_mir(mn);    // halves of a row meet
+    mx = max_mir(mx);
   }
   if constexpr (N >= 32) {
     float a, b;
